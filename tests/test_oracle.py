@@ -1,0 +1,515 @@
+"""Pins for the fp64 oracle, against things other than the oracle itself.
+
+Every check here is one of: an exact closed form (uniform logits, a
+hand-worked example in tests/golden/), a torch library routine that computes
+the same named quantity (cross_entropy, Categorical.entropy, kl_div,
+log_softmax), central finite differences of the total loss, an independent
+torch autograd of the total loss, or an invariant the mathematics fixes
+(shift invariance, identity teacher, ratio one, clipped tokens,
+superposition, accumulation). The last section plants mistakes in the oracle
+and checks that these pins catch them.
+
+KL_OLD_NEW and ADV_MEAN have no definition on the pages; they are checked
+against the closed forms of the readings taken (k3 estimator, mean
+advantage) only: parity unpinned by the pages.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import headloss_oracle as ho
+from oracle import SLOT, Spec
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ALL_LOSSES = oracle.CE | oracle.ZLOSS | oracle.GRPO | oracle.ENTROPY
+
+
+def _eval(expr):
+    return float(eval(expr, {"__builtins__": {}}, {"log": math.log}))
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _grpo_inputs(rng, x, labels, spec, spread=0.05):
+    """old_logprobs near the current label log-prob, advantages ~ N(0,1)."""
+    vals = ho.row_values(spec, x, labels)
+    old = vals["logp"] + rng.normal(0.0, spread, size=x.shape[0])
+    adv = rng.normal(0.0, 1.0, size=x.shape[0])
+    return old, adv
+
+
+# ---------------------------------------------------------------------------
+# Hand-worked example (tests/golden/hand_example_v4.json)
+# ---------------------------------------------------------------------------
+def test_golden_hand_example():
+    with open(os.path.join(HERE, "golden", "hand_example_v4.json")) as f:
+        g = json.load(f)
+    sp = g["spec"]
+    flags = 0
+    for name in sp["flags"]:
+        flags |= getattr(oracle, name)
+    spec = Spec(V=sp["V"], flags=flags, w_ce=sp["w_ce"], w_z=sp["w_z"],
+                w_distill=sp["w_distill"], w_grpo=sp["w_grpo"],
+                grad_scale=sp["grad_scale"], temperature=sp["temperature"],
+                eps=sp["eps"], logit_scale=sp["logit_scale"], softcap=sp["softcap"])
+    inp = g["inputs"]
+    x = np.array([[_eval(e) for e in row] for row in inp["logits"]])
+    t = np.array([[_eval(e) for e in row] for row in inp["teacher"]])
+    y = np.array(inp["labels"], dtype=np.int64)
+    old = np.array([_eval(e) for e in inp["old_logprobs"]])
+    adv = np.array([_eval(e) for e in inp["advantages"]])
+    scalars, grad = oracle.forward_backward(spec, x, y, None, t, old, adv)
+    for name, expr in g["expected_scalars"].items():
+        assert scalars[SLOT[name]] == pytest.approx(_eval(expr), abs=1e-12), name
+    exp_grad = np.array([[_eval(e) for e in row] for row in g["expected_grad"]])
+    np.testing.assert_allclose(grad, exp_grad, atol=1e-14, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("V", [1024, 151936])
+def test_uniform_logits_closed_forms(V):
+    spec = Spec(V=V, flags=oracle.CE | oracle.ZLOSS | oracle.ENTROPY, w_z=1.0)
+    x = np.zeros((2, V))
+    y = np.array([0, V - 1])
+    sc, grad = oracle.forward_backward(spec, x, y)
+    logV = math.log(V)
+    assert sc[SLOT["CE"]] == pytest.approx(logV, rel=1e-14)
+    assert sc[SLOT["Z"]] == pytest.approx(logV ** 2, rel=1e-14)
+    assert sc[SLOT["ENTROPY"]] == pytest.approx(logV, rel=1e-13)
+    # CE grad: (1/V - delta)/n ; z grad: 2 log V / V / n
+    expect = np.full((2, V), (1.0 / V + 2 * logV / V) / 2)
+    expect[0, 0] -= 0.5
+    expect[1, V - 1] -= 0.5
+    np.testing.assert_allclose(grad, expect, atol=1e-15, rtol=1e-12)
+
+
+def test_uniform_values_from_the_survey_table():
+    # all-zero logits: CE = log V (1024 -> 6.9315, 151936 -> 11.9312), z = (log V)^2
+    assert math.log(1024) == pytest.approx(6.9315, abs=1e-4)
+    assert math.log(151936) == pytest.approx(11.9312, abs=1e-4)
+    assert math.log(1024) ** 2 == pytest.approx(48.045, abs=1e-3)
+
+
+def test_entropy_extremes():
+    V = 300
+    spec = Spec(V=V, flags=oracle.ENTROPY)
+    x = np.zeros((1, V))
+    x[0, 17] = 50.0  # one dominant logit: entropy ~ 0
+    sc, _ = oracle.forward_backward(spec, x, want_grad=False)
+    assert 0.0 <= sc[SLOT["ENTROPY"]] < 1e-17 * V * 60
+
+
+# ---------------------------------------------------------------------------
+# torch library routines computing the same named quantity
+# ---------------------------------------------------------------------------
+def test_ce_value_and_grad_vs_torch_cross_entropy():
+    rng = _rng(1)
+    N, V = 23, 41
+    x = rng.normal(0, 2.0, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    y[[3, 7, 11]] = -100
+    w, G = 0.7, 0.37
+    spec = Spec(V=V, flags=oracle.CE, w_ce=w, grad_scale=G)
+    sc, grad = oracle.forward_backward(spec, x, y)
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    ce = F.cross_entropy(xt, torch.tensor(y), ignore_index=-100, reduction="mean")
+    (G * w * ce).backward()
+    assert sc[SLOT["CE"]] == pytest.approx(ce.item(), rel=1e-13)
+    np.testing.assert_allclose(grad, xt.grad.numpy(), atol=1e-15, rtol=1e-11)
+    assert sc[SLOT["N_VALID"]] == N - 3
+
+
+def test_entropy_vs_torch_categorical():
+    rng = _rng(2)
+    x = rng.normal(0, 3.0, size=(9, 77))
+    spec = Spec(V=77, flags=oracle.ENTROPY)
+    vals = ho.row_values(spec, x)
+    ref = torch.distributions.Categorical(logits=torch.tensor(x)).entropy().numpy()
+    np.testing.assert_allclose(vals["entropy"], ref, rtol=1e-12)
+
+
+@pytest.mark.parametrize("tau", [1.0, 2.0, 0.5])
+def test_kl_vs_torch_kl_div(tau):
+    rng = _rng(3)
+    N, V = 7, 53
+    t = rng.normal(0, 3.0, size=(N, V))
+    x = 0.8 * t + rng.normal(0, 1.0, size=(N, V))
+    spec = Spec(V=V, flags=oracle.FKL, temperature=tau)
+    vals = ho.row_values(spec, x, teacher=t)
+    logq = torch.log_softmax(torch.tensor(x), -1)
+    logp = torch.log_softmax(torch.tensor(t) / tau, -1)
+    fkl = F.kl_div(logq, logp, log_target=True, reduction="none").sum(-1).numpy()
+    rkl = F.kl_div(logp, logq, log_target=True, reduction="none").sum(-1).numpy()
+    np.testing.assert_allclose(vals["fkl"], fkl, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(vals["rkl"], rkl, rtol=1e-11, atol=1e-14)
+
+
+def test_newlogp_vs_torch_log_softmax():
+    rng = _rng(4)
+    N, V = 11, 29
+    x = rng.normal(0, 2.0, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    spec = Spec(V=V, flags=oracle.GRPO, w_ce=0.0, w_grpo=1.0, logit_scale=0.5, softcap=3.0)
+    old, adv = _grpo_inputs(rng, x, y, spec)
+    sc, _ = oracle.forward_backward(spec, x, y, None, None, old, adv, want_grad=False)
+    s = spec.softcap * torch.tanh(torch.tensor(x) * spec.logit_scale / spec.softcap)
+    ref = torch.log_softmax(s, -1)[torch.arange(N), torch.tensor(y)].mean().item()
+    assert sc[SLOT["NEWLOGP"]] == pytest.approx(ref, rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Independent torch autograd of the total loss (pins every hand gradient)
+# ---------------------------------------------------------------------------
+def _torch_total(spec, x, y, mask, t, old, adv):
+    """The weighted total, built from torch library pieces, differentiated by autograd."""
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    k, c = spec.logit_scale, spec.softcap
+    s = c * torch.tanh(k * xt / c) if c > 0 else k * xt
+    yv = torch.tensor(y) if y is not None else None
+    valid = torch.ones(x.shape[0], dtype=torch.bool)
+    if mask is not None:
+        valid &= torch.tensor(mask) != 0
+    if yv is not None:
+        valid &= (yv != -100) & (yv >= 0) & (yv < spec.V)
+    n = spec.divisor if spec.divisor > 0 else float(valid.sum())
+    sv = s[valid]
+    total = torch.zeros((), dtype=torch.float64)
+    logq = torch.log_softmax(sv, -1)
+    if spec.flags & oracle.CE:
+        total = total + spec.w_ce * F.cross_entropy(sv, yv[valid], reduction="sum") / n
+    if spec.flags & oracle.ZLOSS:
+        total = total + spec.w_z * (torch.logsumexp(sv, -1) ** 2).sum() / n
+    if spec.flags & (oracle.FKL | oracle.RKL):
+        logp = torch.log_softmax(torch.tensor(t)[valid] / spec.temperature, -1)
+        if spec.flags & oracle.FKL:
+            kl = F.kl_div(logq, logp, log_target=True, reduction="sum")
+        else:
+            kl = F.kl_div(logp, logq, log_target=True, reduction="sum")
+        total = total + spec.w_distill * kl / n
+    if spec.flags & oracle.GRPO:
+        lp = logq.gather(-1, yv[valid][:, None])[:, 0]
+        r = torch.exp(lp - torch.tensor(old)[valid])
+        A = torch.tensor(adv)[valid]
+        obj = torch.minimum(r * A, torch.clamp(r, 1 - spec.eps, 1 + spec.eps) * A)
+        total = total + spec.w_grpo * (-obj).sum() / n
+    (spec.grad_scale * total).backward()
+    return xt.grad.numpy()
+
+
+@pytest.mark.parametrize("mode", ["fkl", "rkl"])
+@pytest.mark.parametrize("softcap", [0.0, 4.0])
+def test_total_gradient_vs_torch_autograd(mode, softcap):
+    rng = _rng(5)
+    N, V = 13, 37
+    t = rng.normal(0, 3.0, size=(N, V))
+    x = 0.7 * t + rng.normal(0, 1.5, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    y[2] = -100
+    mask = np.ones(N, dtype=np.uint8)
+    mask[5] = 0
+    flags = oracle.CE | oracle.ZLOSS | oracle.GRPO | oracle.ENTROPY
+    flags |= oracle.FKL if mode == "fkl" else oracle.RKL
+    spec = Spec(V=V, flags=flags, w_ce=1.0, w_z=0.3, w_distill=0.5, w_grpo=0.8,
+                grad_scale=0.25, temperature=1.5, eps=0.2, logit_scale=0.5,
+                softcap=softcap)
+    old, adv = _grpo_inputs(rng, x, y, spec, spread=0.3)
+    _, grad = oracle.forward_backward(spec, x, y, mask, t, old, adv)
+    ref = _torch_total(spec, x, y, mask, t, old, adv)
+    np.testing.assert_allclose(grad, ref, atol=1e-15, rtol=1e-10)
+
+
+# ---------------------------------------------------------------------------
+# Central finite differences of the oracle's own total
+# ---------------------------------------------------------------------------
+def _fd_check(spec, x, y, mask, t, old, adv, h=1e-6, tol=2e-8):
+    _, grad = oracle.forward_backward(spec, x, y, mask, t, old, adv)
+    fd = np.zeros_like(x)
+    for i in range(x.shape[0]):
+        for j in range(x.shape[1]):
+            xp = x.copy(); xp[i, j] += h
+            xm = x.copy(); xm[i, j] -= h
+            fp = oracle.total_loss(spec, xp, y, mask, t, old, adv)
+            fm = oracle.total_loss(spec, xm, y, mask, t, old, adv)
+            fd[i, j] = (fp - fm) / (2 * h)
+    np.testing.assert_allclose(grad, fd, atol=tol, rtol=0)
+
+
+@pytest.mark.parametrize("mode", ["fkl", "rkl"])
+@pytest.mark.parametrize("softcap,scale", [(0.0, 1.0), (2.5, 0.7)])
+def test_finite_differences_all_losses(mode, softcap, scale):
+    rng = _rng(6)
+    N, V = 4, 9
+    t = rng.normal(0, 2.0, size=(N, V))
+    x = rng.normal(0, 2.0, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    flags = ALL_LOSSES | (oracle.FKL if mode == "fkl" else oracle.RKL)
+    spec = Spec(V=V, flags=flags, w_ce=0.9, w_z=0.2, w_distill=0.6, w_grpo=1.1,
+                grad_scale=0.5, temperature=1.7, eps=0.2, logit_scale=scale,
+                softcap=softcap)
+    old, adv = _grpo_inputs(rng, x, y, spec, spread=0.05)
+    _fd_check(spec, x, y, None, t, old, adv)
+
+
+def test_finite_differences_clipped_grpo_tokens():
+    rng = _rng(7)
+    N, V = 3, 8
+    x = rng.normal(0, 2.0, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    spec = Spec(V=V, flags=oracle.GRPO, w_ce=0.0, w_grpo=1.0, eps=0.2)
+    vals = ho.row_values(spec, x, y)
+    # ratio 1.5 with A>0 (clipped, flat), ratio 0.5 with A<0 (clipped, flat),
+    # ratio 1.5 with A<0 (unclipped, flows)
+    old = vals["logp"] - np.log(np.array([1.5, 0.5, 1.5]))
+    adv = np.array([1.0, -1.0, -1.0])
+    _, grad = oracle.forward_backward(spec, x, y, None, None, old, adv)
+    assert np.all(grad[0] == 0) and np.all(grad[1] == 0)
+    assert np.abs(grad[2]).max() > 0.1
+    _fd_check(spec, x, y, None, None, old, adv)
+
+
+# ---------------------------------------------------------------------------
+# Invariants and special cases
+# ---------------------------------------------------------------------------
+def test_shift_invariance():
+    rng = _rng(8)
+    N, V = 6, 31
+    t = rng.normal(0, 3, size=(N, V))
+    x = rng.normal(0, 3, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    flags = oracle.CE | oracle.RKL | oracle.GRPO | oracle.ENTROPY
+    spec = Spec(V=V, flags=flags, w_distill=0.5, w_grpo=1.0, temperature=2.0)
+    old, adv = _grpo_inputs(rng, x, y, spec)
+    sc0, g0 = oracle.forward_backward(spec, x, y, None, t, old, adv)
+    shift = rng.normal(0, 10, size=(N, 1))
+    sc1, g1 = oracle.forward_backward(spec, x + shift, y, None, t + 3 * shift, old, adv)
+    for name in ("CE", "DISTILL", "GRPO", "ENTROPY", "NEWLOGP", "RATIO", "TOTAL"):
+        assert sc1[SLOT[name]] == pytest.approx(sc0[SLOT[name]], rel=1e-11, abs=1e-12), name
+    np.testing.assert_allclose(g1, g0, atol=1e-13)
+
+
+def test_z_loss_is_not_shift_invariant():
+    rng = _rng(9)
+    x = rng.normal(0, 1, size=(3, 20))
+    spec = Spec(V=20, flags=oracle.ZLOSS, w_ce=0.0, w_z=1.0)
+    v0 = ho.row_values(spec, x)
+    v1 = ho.row_values(spec, x + 2.5)
+    np.testing.assert_allclose(v1["z"], (v0["lse"] + 2.5) ** 2, rtol=1e-13)
+
+
+def test_identity_teacher_gives_zero_kl_and_zero_distill_grad():
+    rng = _rng(10)
+    N, V = 5, 64
+    x = rng.normal(0, 3, size=(N, V))
+    for flag in (oracle.FKL, oracle.RKL):
+        spec = Spec(V=V, flags=flag, w_ce=0.0, w_distill=1.0, temperature=1.0)
+        sc, grad = oracle.forward_backward(spec, x, teacher=x)
+        assert abs(sc[SLOT["DISTILL"]]) < 1e-14
+        assert np.abs(grad).max() < 1e-16
+
+
+def test_kl_nonnegative_and_uniform_teacher_limit():
+    rng = _rng(11)
+    N, V = 8, 40
+    t = rng.normal(0, 3, size=(N, V))
+    x = rng.normal(0, 3, size=(N, V))
+    spec = Spec(V=V, flags=oracle.FKL, temperature=1.0)
+    v = ho.row_values(spec, x, teacher=t)
+    assert np.all(v["fkl"] >= 0) and np.all(v["rkl"] >= 0)
+    # tau -> infinity: the teacher is uniform, FKL = -log V - mean_j log q_j
+    spec_inf = Spec(V=V, flags=oracle.FKL, temperature=1e12)
+    vi = ho.row_values(spec_inf, x, teacher=t)
+    expect = -math.log(V) - v["logq"].mean(axis=1)
+    np.testing.assert_allclose(vi["fkl"], expect, rtol=1e-9)
+
+
+def test_grpo_ratio_one_reduces_to_policy_gradient():
+    rng = _rng(12)
+    N, V = 10, 25
+    x = rng.normal(0, 2, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    spec = Spec(V=V, flags=oracle.GRPO, w_ce=0.0, w_grpo=1.0)
+    vals = ho.row_values(spec, x, y)
+    old = vals["logp"].copy()
+    adv = rng.normal(0, 1, size=N)
+    sc, grad = oracle.forward_backward(spec, x, y, None, None, old, adv)
+    assert sc[SLOT["GRPO"]] == pytest.approx(-adv.mean(), rel=1e-12)
+    assert sc[SLOT["RATIO"]] == pytest.approx(1.0, rel=1e-14)
+    assert sc[SLOT["CLIPFRAC"]] == 0.0
+    assert abs(sc[SLOT["KL_OLD_NEW"]]) < 1e-15
+    assert sc[SLOT["ADV_MEAN"]] == pytest.approx(adv.mean(), rel=1e-14)
+    # gradient = -A * d logp / dx / n, with d logp/dx from torch autograd
+    xt = torch.tensor(x, requires_grad=True)
+    lp = torch.log_softmax(xt, -1)[torch.arange(N), torch.tensor(y)]
+    (-(torch.tensor(adv) * lp).sum() / N).backward()
+    np.testing.assert_allclose(grad, xt.grad.numpy(), atol=1e-15, rtol=1e-11)
+
+
+def test_grpo_zero_advantage_and_clipped_closed_forms():
+    rng = _rng(13)
+    N, V = 4, 12
+    x = rng.normal(0, 2, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    spec = Spec(V=V, flags=oracle.GRPO, w_ce=0.0, w_grpo=1.0, eps=0.2)
+    vals = ho.row_values(spec, x, y)
+    old = vals["logp"] - np.log(1.5)             # ratio 1.5 everywhere
+    sc, grad = oracle.forward_backward(spec, x, y, None, None, old, np.zeros(N))
+    assert sc[SLOT["GRPO"]] == 0.0 and np.all(grad == 0)
+    A = np.array([0.5, 1.0, 2.0, 3.0])           # all positive: clipped at 1+eps
+    sc, grad = oracle.forward_backward(spec, x, y, None, None, old, A)
+    assert sc[SLOT["GRPO"]] == pytest.approx(-(1.2 * A).mean(), rel=1e-14)
+    assert np.all(grad == 0)
+    assert sc[SLOT["CLIPFRAC"]] == 1.0
+    assert sc[SLOT["KL_OLD_NEW"]] == pytest.approx(0.5 - math.log(1.5), rel=1e-12)
+
+
+def test_softcap_and_scale_limits():
+    rng = _rng(14)
+    N, V = 5, 33
+    x = rng.normal(0, 2, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    base = dict(V=V, flags=oracle.CE | oracle.ZLOSS | oracle.ENTROPY, w_z=0.1)
+    sc0, g0 = oracle.forward_backward(Spec(**base), x, y)
+    sc1, g1 = oracle.forward_backward(Spec(**base, softcap=1e7), x, y)
+    np.testing.assert_allclose(sc1, sc0, rtol=1e-10)
+    np.testing.assert_allclose(g1, g0, atol=1e-12)
+    # logit_scale k on raw logits equals scale 1 on k*x, with the chain factor k
+    k = 0.37
+    sc2, g2 = oracle.forward_backward(Spec(**base, logit_scale=k), x, y)
+    sc3, g3 = oracle.forward_backward(Spec(**base), k * x, y)
+    np.testing.assert_allclose(sc2, sc3, rtol=1e-13)
+    np.testing.assert_allclose(g2, k * g3, atol=1e-15)
+
+
+def test_superposition_of_single_loss_runs():
+    rng = _rng(15)
+    N, V = 9, 45
+    t = rng.normal(0, 3, size=(N, V))
+    x = 0.8 * t + rng.normal(0, 1, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    y[0] = -100
+    w = dict(w_ce=0.5, w_z=0.01, w_distill=1.0, w_grpo=0.7)
+    full = Spec(V=V, flags=ALL_LOSSES | oracle.RKL, temperature=2.0, **w)
+    old, adv = _grpo_inputs(rng, x, y, full)
+    sc, g = oracle.forward_backward(full, x, y, None, t, old, adv)
+    acc = np.zeros_like(x)
+    for flag, key in ((oracle.CE, "w_ce"), (oracle.ZLOSS, "w_z"),
+                      (oracle.RKL, "w_distill"), (oracle.GRPO, "w_grpo")):
+        single = Spec(V=V, flags=flag, temperature=2.0,
+                      **{k: (v if k == key else 0.0) for k, v in w.items()})
+        _, gk = oracle.forward_backward(single, x, y, None, t, old, adv)
+        acc += gk
+    np.testing.assert_allclose(g, acc, atol=1e-15, rtol=1e-12)
+    # a zero-weight loss still reports its scalar and adds nothing to the gradient
+    zero = Spec(V=V, flags=ALL_LOSSES | oracle.RKL, temperature=2.0,
+                **{**w, "w_grpo": 0.0})
+    sc0, g0 = oracle.forward_backward(zero, x, y, None, t, old, adv)
+    assert sc0[SLOT["GRPO"]] == sc[SLOT["GRPO"]] and sc0[SLOT["RATIO"]] == sc[SLOT["RATIO"]]
+    nog = Spec(V=V, flags=ALL_LOSSES | oracle.RKL, temperature=2.0, **{**w, "w_grpo": 0.0})
+    _, g_no_grpo = oracle.forward_backward(nog, x, y, None, t, old, adv)
+    np.testing.assert_allclose(g0, g_no_grpo, atol=0)
+
+
+def test_masking_accumulate_divisor_and_bad_labels():
+    rng = _rng(16)
+    N, V = 12, 20
+    x = rng.normal(0, 2, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    y[1] = -100
+    y[2] = V + 5       # out of range: masked and counted
+    y[3] = -7          # out of range: masked and counted
+    mask = np.ones(N, dtype=np.uint8)
+    mask[4] = 0
+    y[4] = V + 1       # masked by the mask byte: not counted as bad
+    existing = rng.normal(0, 1, size=(N, V))
+    spec = Spec(V=V, flags=oracle.CE | oracle.ZLOSS | oracle.ACCUMULATE, w_z=0.1)
+    sc, g_acc = oracle.forward_backward(spec, x, y, mask, grad_in=existing)
+    spec_over = Spec(V=V, flags=oracle.CE | oracle.ZLOSS, w_z=0.1)
+    sc2, g = oracle.forward_backward(spec_over, x, y, mask)
+    assert sc[SLOT["N_VALID"]] == N - 4 and sc[SLOT["N_BADLABEL"]] == 2
+    for r in (1, 2, 3, 4):
+        assert np.all(g[r] == 0.0)
+        assert np.array_equal(g_acc[r], existing[r])
+    np.testing.assert_allclose(g_acc - existing, g, atol=1e-15)
+    # divisor: scalars and gradient both use it
+    spec_div = Spec(V=V, flags=oracle.CE | oracle.ZLOSS, w_z=0.1, divisor=100.0)
+    sc3, g3 = oracle.forward_backward(spec_div, x, y, mask)
+    np.testing.assert_allclose(sc3[SLOT["CE"]], sc2[SLOT["CE"]] * (N - 4) / 100.0, rtol=1e-14)
+    np.testing.assert_allclose(g3, g * (N - 4) / 100.0, atol=1e-16)
+
+
+def test_all_rows_masked_gives_zeros():
+    x = np.random.default_rng(17).normal(size=(4, 10))
+    y = np.full(4, -100)
+    spec = Spec(V=10, flags=ALL_LOSSES, w_grpo=1.0)
+    sc, g = oracle.forward_backward(spec, x, y, None, None, np.zeros(4), np.ones(4))
+    assert np.all(sc == 0.0) and np.all(g == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each mutation of the oracle must be caught by a pin above
+# ---------------------------------------------------------------------------
+def _mutant_total_grad_fails(monkeypatch, target, replacement):
+    monkeypatch.setattr(ho, target, replacement)
+    try:
+        for mode in ("fkl", "rkl"):
+            for sc in (0.0, 4.0):
+                test_total_gradient_vs_torch_autograd(mode, sc)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    orig_grads = ho.loss_gradients_wrt_s
+    orig_deriv = ho.transform_derivative
+    orig_values = ho.row_values
+
+    def wrong_rkl_sign(spec, vals):
+        g = orig_grads(spec, vals)
+        if "distill" in g and spec.has(oracle.RKL):
+            g["distill"] = vals["q"] * (vals["logq"] - vals["logp_t"] + vals["rkl"][:, None])
+        return g
+
+    def dropped_z_factor(spec, vals):
+        g = orig_grads(spec, vals)
+        if "z" in g:
+            g["z"] = vals["lse"][:, None] * vals["q"]
+        return g
+
+    def wrong_label_index(spec, vals):
+        vals = dict(vals)
+        vals["y"] = (vals["y"] + 1) % vals["q"].shape[1]
+        return orig_grads(spec, vals)
+
+    def chain_without_tanh(x, spec):
+        return np.full_like(np.asarray(x, dtype=np.float64), spec.logit_scale)
+
+    def grpo_always_active(spec, *a, **k):
+        v = orig_values(spec, *a, **k)
+        if "grpo_active" in v:
+            v["grpo_active"] = np.ones_like(v["grpo_active"])
+        return v
+
+    for target, repl in (("loss_gradients_wrt_s", wrong_rkl_sign),
+                         ("loss_gradients_wrt_s", dropped_z_factor),
+                         ("loss_gradients_wrt_s", wrong_label_index),
+                         ("transform_derivative", chain_without_tanh)):
+        assert _mutant_total_grad_fails(monkeypatch, target, repl), target
+        monkeypatch.setattr(ho, "loss_gradients_wrt_s", orig_grads)
+        monkeypatch.setattr(ho, "transform_derivative", orig_deriv)
+
+    monkeypatch.setattr(ho, "row_values", grpo_always_active)
+    with pytest.raises(AssertionError):
+        test_finite_differences_clipped_grpo_tokens()
+    monkeypatch.setattr(ho, "row_values", orig_values)
