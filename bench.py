@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Throughput of the fused LM-head loss on one MI355X.
+
+A step is one hl_forward_backward call (valid-row count, fused softmax +
+losses + gradient kernel, batch reduction) over one batch of synthetic
+inputs already resident in HBM. Prints one JSON line on stdout; progress
+goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "tokens/s + achieved HBM GB/s (% peak), CE+z+GRPO+entropy, V=151936 bf16, 1 GPU"
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, vendor figure
+FUSED_KERNEL = "fused_kernel"
+LOSS_NAMES = {1: "CE", 2: "z", 4: "FKL", 8: "RKL", 16: "GRPO", 32: "entropy"}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources (tells whether stored counters still apply)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lm_head_vocab_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cuh", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def plan_kwargs(w):
+    wt = w.weights
+    return dict(ce=wt.get("ce", 1.0), z=wt.get("z", 0.0), distill=wt.get("distill", 0.0),
+                grpo=wt.get("grpo", 0.0), grad_scale=wt.get("grad_scale", 1.0),
+                divisor=wt.get("divisor", 0.0), temperature=w.temperature, eps=w.eps,
+                logit_scale=w.logit_scale, softcap=w.softcap)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle, as it stands, on a bounded sample of rows
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, budget_s: float, threads: int):
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    spec = oracle.Spec(V=w.V, flags=w.flags, w_ce=w.weights.get("ce", 1.0), w_z=w.weights.get("z", 0.0),
+                       w_distill=w.weights.get("distill", 0.0), w_grpo=w.weights.get("grpo", 0.0),
+                       grad_scale=w.weights.get("grad_scale", 1.0), temperature=w.temperature,
+                       eps=w.eps, logit_scale=w.logit_scale, softcap=w.softcap)
+    rows_per_task = 2
+
+    def sample(n_rows, seed):
+        inp = workloads.generate(w, "cpu", seed=seed, n_rows=n_rows)
+        x = inp["logits"].double().numpy()
+        y = inp["labels"].numpy() if inp["labels"] is not None else None
+        d = dict(labels=y, mask=inp["mask"].numpy() if inp["mask"] is not None else None,
+                 teacher=inp["teacher"].double().numpy() if inp["teacher"] is not None else None,
+                 advantages=inp["advantages"].double().numpy() if inp["advantages"] is not None else None,
+                 grad_in=inp["grad_init"].double().numpy() if inp["grad_init"] is not None else None)
+        if w.flags & oracle.GRPO:
+            d["old_logprobs"] = oracle.row_values(spec, x, y)["logp"] + inp["old_noise"].double().numpy()
+        return x, d
+
+    def task(args):
+        x, d = args
+        oracle.rows_forward_backward(spec, x, float(w.N), **d)
+
+    def split(x, d, k):
+        out = []
+        for r0 in range(0, x.shape[0], k):
+            sl = slice(r0, r0 + k)
+            out.append((x[sl], {key: (v[sl] if v is not None else None) for key, v in d.items()}))
+        return out
+
+    # a fixed sample of rows, processed in rounds until the time budget is spent
+    n_rows = 4 * threads * rows_per_task
+    x, d = sample(n_rows, seed=workloads.seed_for(w.name, 8))
+    tasks = split(x, d, rows_per_task)
+    log(f"cpu baseline: oracle on {n_rows}-row sample x V={w.V}, {threads} threads, ~{budget_s:.0f} s")
+    done = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            list(ex.map(task, tasks))
+            done += n_rows
+            dt = time.perf_counter() - t0
+            if dt >= budget_s:
+                break
+    n_rows = done
+    return {"value": n_rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_rows} row evaluations of a {4 * threads * rows_per_task}-row host-drawn sample of "
+                      f"{w.name} (V={w.V}, same recipe), full forward+backward in numpy fp64, "
+                      f"{threads} threads, {dt:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+# GPU measurement
+# ---------------------------------------------------------------------------
+def stored_traffic(w, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{FUSED_KERNEL}_{w.name}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("src_hash") != src_hash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-separate", action="store_true")
+    ap.add_argument("--chunks", type=int, default=0, help="force the split-vocab chunk count")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    w = workloads.WORKLOADS[args.workload]
+
+    # The host baseline runs before anything touches the GPU.
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        cpu = cpu_baseline(w, args.cpu_seconds, threads)
+        log(f"cpu baseline {cpu['value']:.1f} tokens/s")
+
+    import torch
+
+    import lm_head_vocab_amd as hl
+
+    dev = torch.device("cuda:0")
+    log(f"generating {w.name}: N={w.N} V={w.V} {w.dtype}")
+    inp = workloads.generate(w, dev)
+    if w.flags & workloads.GRPO:
+        # old = label log-prob of the stored logits (fp32, torch) + noise: input synthesis
+        N = w.N
+        old = torch.empty(N, dtype=torch.float32, device=dev)
+        y = inp["labels"].clamp(min=0)
+        for r0 in range(0, N, 512):
+            r1 = min(N, r0 + 512)
+            xs = inp["logits"][r0:r1].float()
+            s = w.softcap * torch.tanh(xs * (w.logit_scale / w.softcap)) if w.softcap > 0 else xs * w.logit_scale
+            old[r0:r1] = torch.log_softmax(s, 1).gather(1, y[r0:r1, None])[:, 0]
+        inp["old_logprobs"] = old + inp["old_noise"]
+    labels = inp["labels"]
+    valid = (labels >= 0) & (labels < w.V)
+    if inp["mask"] is not None:
+        valid &= inp["mask"] != 0
+    n_valid = int(valid.sum().item())
+    acc = bool(w.flags & workloads.ACCUMULATE)
+    grad = inp["grad_init"].clone() if acc else torch.empty_like(inp["logits"])
+    plan = hl.Plan(w.V, w.torch_dtype, w.flags, chunks=args.chunks, **plan_kwargs(w))
+    geo = plan.describe()
+    log(f"plan {geo}")
+
+    def step(p=plan, g=grad):
+        return p(inp["logits"], labels=labels, mask=inp["mask"], teacher=inp["teacher"],
+                 old_logprobs=inp.get("old_logprobs"), advantages=inp["advantages"], grad=g)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    K = args.steps
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in kev:          # materialise the events before handing them to the library
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        plan.set_timing_events(*kev[i])
+        step()
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    plan.set_timing_events(None, None)
+    ms_total = t_start.elapsed_time(t_stop)
+    ms_step = ms_total / K
+    kernel_ms = sorted(a.elapsed_time(b) for a, b in kev)
+    kernel_avg = sum(kernel_ms) / K
+    log(f"timed {K} steps: {ms_step:.4f} ms/step, fused kernel {kernel_avg:.4f} ms avg")
+
+    algo_bytes = workloads.algorithmic_bytes(w, n_valid)
+    achieved = algo_bytes / (kernel_avg * 1e-3) / 1e9
+    src_hash = source_hash()
+    traffic = stored_traffic(w, src_hash)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                "kernel": FUSED_KERNEL, "kernel_ms_avg": round(kernel_avg, 5),
+                "algorithmic_bytes_per_launch": algo_bytes}
+
+    # plain device-to-device copy bandwidth, for context
+    nb = 4 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nb * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    separate = None
+    if not args.no_separate:
+        plans = []
+        first = True
+        for bit, lname in LOSS_NAMES.items():
+            if not (w.flags & bit):
+                continue
+            kw = plan_kwargs(w)
+            keep = {1: "ce", 2: "z", 4: "distill", 8: "distill", 16: "grpo"}.get(bit)
+            for key in ("ce", "z", "distill", "grpo"):
+                if key != keep:
+                    kw[key] = 0.0
+            flags = bit
+            if bit != 32 and not first:
+                flags |= hl.ACCUMULATE
+            if bit == 32:
+                plans.append((hl.Plan(w.V, w.torch_dtype, flags, **kw), None))
+            else:
+                if first and acc:
+                    flags |= hl.ACCUMULATE
+                plans.append((hl.Plan(w.V, w.torch_dtype, flags, **kw), grad))
+                first = False
+
+        def sep_step():
+            for p, g in plans:
+                step(p, g)
+        for _ in range(max(1, args.warmup)):
+            sep_step()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(K):
+            sep_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sep_ms = e0.elapsed_time(e1) / K
+        separate = {"ms_per_step": round(sep_ms, 5), "passes": [LOSS_NAMES[b] for b in LOSS_NAMES if w.flags & b],
+                    "fused_speedup": round(sep_ms / ms_step, 3)}
+        log(f"separate passes: {sep_ms:.4f} ms/step ({separate['fused_speedup']}x)")
+
+    tokens_s = w.N / (ms_step * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "N": w.N, "V": w.V, "dtype": w.dtype,
+                   "losses": "+".join(LOSS_NAMES[b] for b in LOSS_NAMES if w.flags & b),
+                   "accumulate": acc, "n_valid": n_valid, "variant": geo},
+        "hbm_GBps_step": round(algo_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "frac_peak_step": round(algo_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "copy_GBps": round(copy_gbps, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "separate_pass": separate,
+        "src_hash": src_hash,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

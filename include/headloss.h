@@ -1,0 +1,213 @@
+/*
+ * headloss.h - C ABI of the MI355X fused language-model head loss.
+ *
+ * One call takes one row of logits per token over the whole vocabulary,
+ * computes the student softmax once in fp32, and from that one shared softmax
+ * emits every requested loss / metric scalar and the single combined logits
+ * gradient. This is the "monolithic" head loss of Fast-LLM issue #507
+ * ("Monolithic fused head-loss kernel for combinable losses + metrics",
+ * section Proposed direction: run the softmax once, emit all requested
+ * scalars and the combined gradient in one pass), with the loss set of
+ * Fast-LLM PR #549 ("Monolithic fused head-loss kernel (torch.compile)",
+ * section Loss coverage) and the gradient split of Fast-LLM PR #558 (the
+ * Triton kernel for the monolithic loss, section Design):
+ *
+ *     grad_j = prob_coeff * softmax_j - label_coeff * delta(j, label)
+ *              + distillation term
+ *
+ * Conventions for every entry point:
+ *  - Pointers named dev_* or documented as "device" point to GPU memory
+ *    allocated by the caller (e.g. by PyTorch); the library never frees them
+ *    and keeps no reference to them after the call returns.
+ *  - Every check is made on the host, before anything is enqueued; a call
+ *    that returns an error has enqueued nothing. No kernel traps.
+ *  - Calls that enqueue work are asynchronous on the given HIP stream
+ *    (NULL = the default stream); results are valid after the stream is
+ *    synchronised.
+ */
+#ifndef HEADLOSS_H
+#define HEADLOSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+typedef enum {
+    HL_OK = 0,
+    HL_ERR_INVALID_ARG = 1,   /* a value or pointer is out of its documented range */
+    HL_ERR_MISSING_INPUT = 2, /* an enabled loss lacks one of its inputs */
+    HL_ERR_UNSUPPORTED = 3,   /* a valid request this build does not implement */
+    HL_ERR_WORKSPACE = 4,     /* no workspace, or one too small for n_rows */
+    HL_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
+} hl_status;
+
+/* Element type of logits, teacher logits and gradient (all three share it). */
+typedef enum { HL_F32 = 0, HL_BF16 = 1 } hl_dtype;
+
+/* Loss and metric flags (#507 Proposed direction: "a config / flag-set
+ * describing which losses and metrics to emit"). At most one distillation
+ * direction per plan (#558 What it does: at most one of each kind). */
+enum {
+    HL_CE = 1u << 0,       /* label cross-entropy  -log softmax_y            */
+    HL_ZLOSS = 1u << 1,    /* z-loss  (log sum_j exp s_j)^2                  */
+    HL_FKL = 1u << 2,      /* distillation, KL(teacher || student)           */
+    HL_RKL = 1u << 3,      /* distillation, KL(student || teacher)           */
+    HL_GRPO = 1u << 4,     /* GRPO clipped objective + new-logprob/ratio/
+                              clamp/KL/advantage statistics                  */
+    HL_ENTROPY = 1u << 5,  /* entropy metric (no gradient)                   */
+    HL_ACCUMULATE = 1u << 16 /* mode bit: add into grad_out instead of
+                                overwriting it (#558 Validation: gradient
+                                accumulation)                                */
+};
+
+/* Loss weights and gradient scaling. Each scalar slot reports its loss
+ * unweighted (#558 Design: every loss stores its own forward scalar); the
+ * weights enter TOTAL and the gradient only. A zero weight keeps the loss's
+ * scalars and removes its gradient term (#558 Validation: a zero-weight loss
+ * still logs its diagnostics). */
+typedef struct {
+    float ce;         /* weight of HL_CE                                    */
+    float z;          /* weight of HL_ZLOSS                                 */
+    float distill;    /* weight of HL_FKL / HL_RKL                          */
+    float grpo;       /* weight of HL_GRPO                                  */
+    float grad_scale; /* extra factor on the gradient only (G)              */
+    float divisor;    /* > 0: divide sums by this; <= 0: by the number of
+                         valid rows of the call                             */
+} hl_weights;
+
+/* Output slots of scalars_out (device float[HL_NUM_SCALARS]). Slots of
+ * losses that are not enabled are written as 0. */
+enum {
+    HL_S_CE = 0, HL_S_Z, HL_S_DISTILL, HL_S_GRPO, HL_S_NEWLOGP, HL_S_RATIO,
+    HL_S_CLIPFRAC, HL_S_KL_OLD_NEW, HL_S_ADV_MEAN, HL_S_ENTROPY, HL_S_TOTAL,
+    HL_S_N_VALID, HL_S_N_BADLABEL,
+    HL_NUM_SCALARS
+};
+
+/* Per-row value columns (see hl_row_values). */
+enum {
+    HL_R_CE = 0, HL_R_Z, HL_R_DISTILL, HL_R_GRPO, HL_R_NEWLOGP, HL_R_RATIO,
+    HL_R_CLIPPED, HL_R_K3, HL_R_ADV, HL_R_ENTROPY, HL_R_VALID, HL_R_PAD,
+    HL_NUM_ROW_COLS
+};
+
+typedef struct hl_plan_s* hl_plan_t;
+
+/*
+ * hl_plan - validate a loss set and choose the kernel variant for it.
+ *
+ * Defines the operation of #507 Proposed direction (one softmax, every
+ * requested scalar, one combined gradient) for rows of length V.
+ *   out          receives the plan handle (host pointer, must not be NULL).
+ *   V            vocabulary size, >= 1.
+ *   dtype        element type of logits / teacher / gradient.
+ *   loss_flags   OR of HL_* loss flags (at least one loss or metric) and
+ *                optionally HL_ACCUMULATE.
+ *   weights      host pointer; all fields finite.
+ *   temperature  divides the teacher logits (distillation only), > 0
+ *                (#549 Bundled fix: the temperature is honoured).
+ *   eps          GRPO clip range, 0 < eps < 1 (GRPO only).
+ *   logit_scale  student logits are multiplied by it, finite and > 0; one
+ *                plan = one scale (#549 Approach: one softmax = one scale).
+ *   softcap      0 = off; > 0: s = softcap * tanh(logit_scale * x / softcap).
+ * Makes no HIP call. Errors: HL_ERR_INVALID_ARG (V < 1, unknown flag bits,
+ * no loss flag, both HL_FKL and HL_RKL, temperature <= 0 with distillation,
+ * eps outside (0,1) with GRPO, bad scale or softcap, non-finite weight),
+ * HL_ERR_UNSUPPORTED (V too long for any kernel variant).
+ */
+hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags,
+                  const hl_weights* weights, float temperature, float eps,
+                  float logit_scale, float softcap);
+
+/* Release a plan and any workspace the library allocated for it. NULL is a
+ * no-op. The caller must have synchronised work that uses the plan. */
+void hl_plan_destroy(hl_plan_t plan);
+
+/* Bytes of device workspace a call with n_rows rows needs (0 on a NULL plan
+ * or negative n_rows). Independent of the data. */
+size_t hl_workspace_bytes(hl_plan_t plan, int64_t n_rows);
+
+/* Give the plan caller-owned device workspace (256-byte aligned, at least
+ * hl_workspace_bytes(plan, n_rows) for every later call). Replaces any
+ * workspace the library allocated. Errors: HL_ERR_INVALID_ARG (NULL plan or
+ * pointer, misaligned pointer). */
+hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t bytes);
+
+/*
+ * hl_forward_backward - the fused pass (#507 Proposed direction; #549
+ * Approach; #558 Design).
+ *   n_rows          number of tokens N >= 0 (0: scalars are all written 0).
+ *   logits          device [N, V] row-major contiguous, plan dtype, base
+ *                   16-byte aligned. Raw student logits.
+ *   labels          device int64[N] or NULL; -100 = ignored token. Needed by
+ *                   HL_CE and HL_GRPO. An unmasked label outside [0, V) that
+ *                   is not -100 masks the row and counts in N_BADLABEL.
+ *   mask            device uint8[N] or NULL; 0 = masked token. Masking
+ *                   applies to every loss and metric.
+ *   teacher_logits  device [N, V], plan dtype, 16-byte aligned base, or
+ *                   NULL; needed by HL_FKL / HL_RKL.
+ *   old_logprobs    device float[N] or NULL; needed by HL_GRPO.
+ *   advantages      device float[N] (per token) or NULL; needed by HL_GRPO.
+ *   grad_out        device [N, V], plan dtype, 16-byte aligned base, or NULL
+ *                   (NULL: metrics only, no gradient written). Overwrite
+ *                   mode writes every element (masked rows +0.0);
+ *                   HL_ACCUMULATE adds in fp32 and rounds once, and leaves
+ *                   masked rows untouched.
+ *   scalars_out     device float[HL_NUM_SCALARS], must not be NULL.
+ *   stream          HIP stream for all work of the call.
+ * Gradient with respect to the raw logits of a valid row:
+ *   grad_scale / n * ds/dx * sum_k weight_k * dloss_k/ds
+ * with n the number of valid rows (or weights.divisor when > 0).
+ * Errors: HL_ERR_INVALID_ARG (NULL plan, n_rows < 0, NULL logits or
+ * scalars_out, misaligned base pointer), HL_ERR_MISSING_INPUT (see above),
+ * HL_ERR_WORKSPACE (a workspace that is too small was set by the caller),
+ * HL_ERR_HIP. Allocates device memory only when no workspace was set (first
+ * call, or a larger n_rows than before); the allocation is kept by the plan.
+ * Concurrent calls with one plan race on its workspace: use one plan per
+ * stream.
+ */
+hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits,
+                              const int64_t* labels, const uint8_t* mask,
+                              const void* teacher_logits, const float* old_logprobs,
+                              const float* advantages, void* grad_out,
+                              float* scalars_out, hipStream_t stream);
+
+/* Device pointer to the per-row values of the plan's last call: float
+ * [n_rows, HL_NUM_ROW_COLS] inside the workspace (masked rows are all 0,
+ * HL_R_VALID is 1 for counted rows). Valid until the next call with the plan
+ * or a workspace change. These are the per-token values the batch means of
+ * #549 Loss coverage are taken over (new_logprobs, entropy, ratio, ...).
+ * Returns NULL when the plan has no workspace yet. */
+const float* hl_row_values(hl_plan_t plan);
+
+/* Override the number of vocabulary chunks per row (0 = automatic). More than
+ * one chunk selects the split-vocab variant: each row is spread over several
+ * workgroups whose softmax statistics are combined before the gradient pass
+ * (the looped multi-block path of #558 Validation). Errors:
+ * HL_ERR_INVALID_ARG (chunks < 0 or > 64), HL_ERR_UNSUPPORTED (no variant
+ * fits V with that many chunks). */
+hl_status hl_plan_set_chunks(hl_plan_t plan, int chunks);
+
+/* Describe the chosen variant: chunks per row, threads per workgroup, 16-byte
+ * vectors held per thread per tensor. Any pointer may be NULL. */
+hl_status hl_plan_describe(hl_plan_t plan, int* chunks, int* block, int* vec_per_thread);
+
+/* Record the two events (hipEvent_t, may be NULL to stop) immediately before
+ * and after the fused kernel of every later call, on the call's stream, so a
+ * profiler can time the dominant kernel alone. */
+hl_status hl_plan_set_timing_events(hl_plan_t plan, hipEvent_t before, hipEvent_t after);
+
+/* Static text for a status code. */
+const char* hl_status_str(hl_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HEADLOSS_H */

@@ -1,0 +1,157 @@
+// Launchers of the valid-row count and the batch reduction kernels.
+#include "hl_device.cuh"
+
+namespace hl {
+
+// ---------------------------------------------------------------------------
+// count_kernel: one workgroup of 1024 threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
+    __shared__ uint32_t s_v[16], s_b[16];
+    uint32_t nv = 0, nb = 0;
+    for (int64_t r = threadIdx.x; r < p.n_rows; r += 1024) {
+        bool valid, bad;
+        int64_t y;
+        row_status(p.labels, p.mask, r, p.V, valid, bad, y);
+        nv += valid;
+        nb += bad;
+        if (p.row_counters) p.row_counters[r] = 0u;
+    }
+    for (int m = 32; m >= 1; m >>= 1) {
+        nv += __shfl_xor(nv, m, 64);
+        nb += __shfl_xor(nb, m, 64);
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) { s_v[wave] = nv; s_b[wave] = nb; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t tv = 0, tb = 0;
+        for (int w = 0; w < 16; ++w) { tv += s_v[w]; tb += s_b[w]; }
+        p.ctrl[CTRL_NVALID] = tv;
+        p.ctrl[CTRL_NBAD] = tb;
+        p.ctrl[CTRL_CLAIM] = 0u;
+        p.ctrl[CTRL_ERROR] = 0u;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// reduce_kernel: one workgroup of 1024 threads. Turns each row's softmax
+// record into the reported per-row values in fp64 (lse = M + log2 Z in the
+// log2 domain, entropy, KL, CE, new log-prob, GRPO objective and statistics),
+// stores them for hl_row_values, and sums them in a fixed order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void reduce_kernel(const ReduceParams p) {
+    constexpr double LN2 = 0.69314718055994530942;
+    __shared__ double s_acc[16][NSUM];
+    double acc[NSUM];
+#pragma unroll
+    for (int c = 0; c < NSUM; ++c) acc[c] = 0.0;
+    const uint32_t f = p.flags;
+    for (int64_t r = threadIdx.x; r < p.n_rows; r += 1024) {
+        const float* rec = p.row_rec + r * REC;
+        double v[NCOL];
+#pragma unroll
+        for (int c = 0; c < NCOL; ++c) v[c] = 0.0;
+        if (rec[R_VALID] != 0.f) {
+            const double Z = rec[R_Z];
+            const double l2Z = log2(Z);
+            const double lse = ((double)rec[R_M] + l2Z) * LN2;
+            v[RC_Z] = lse * lse;
+            v[RC_ENT] = LN2 * (l2Z - (double)rec[R_S] / Z);
+            if (f & (F_FKL | F_RKL)) {
+                const double Zt = rec[R_ZT];
+                const double l2Zt = log2(Zt);
+                v[RC_KL] = (f & F_FKL) ? LN2 * ((double)rec[R_SX] / Zt - l2Zt + l2Z)
+                                       : LN2 * ((double)rec[R_SX] / Z - l2Z + l2Zt);
+            }
+            if (p.labels != nullptr) {
+                const double xy = rec[R_XY];
+                const double sy = p.cap > 0.f ? (double)p.cap * tanh((double)p.k * xy / (double)p.cap)
+                                              : (double)p.k * xy;
+                v[RC_CE] = lse - sy;
+                v[RC_LOGP] = sy - lse;
+                if (f & F_GRPO) {
+                    const double adv = p.advantages[r];
+                    const double d = v[RC_LOGP] - (double)p.old_logprobs[r];
+                    const double ratio = exp(d);
+                    const double eps = p.eps;
+                    const double rc = ratio < 1.0 - eps ? 1.0 - eps : (ratio > 1.0 + eps ? 1.0 + eps : ratio);
+                    const double un = ratio * adv, cl = rc * adv;
+                    v[RC_GRPO] = -(un < cl ? un : cl);
+                    v[RC_RATIO] = ratio;
+                    v[RC_CLIP] = fabs(ratio - 1.0) > eps ? 1.0 : 0.0;
+                    v[RC_K3] = expm1(d) - d;
+                    v[RC_ADV] = adv;
+                }
+            }
+            v[RC_VALID] = 1.0;
+        }
+        float* out = p.rows + r * NCOL;
+#pragma unroll
+        for (int c = 0; c < NCOL; ++c) out[c] = (float)v[c];
+#pragma unroll
+        for (int c = 0; c < NSUM; ++c) acc[c] += v[c];
+    }
+    // fixed butterfly within the wave, then waves in order
+#pragma unroll
+    for (int c = 0; c < NSUM; ++c) {
+        double x = acc[c];
+        for (int m = 1; m < 64; m <<= 1) x = __dadd_rn(x, __shfl_xor(x, m, 64));
+        acc[c] = x;
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) {
+#pragma unroll
+        for (int c = 0; c < NSUM; ++c) s_acc[wave][c] = acc[c];
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    double sum[NSUM];
+    for (int c = 0; c < NSUM; ++c) {
+        double x = 0.0;
+        for (int w = 0; w < 16; ++w) x += s_acc[w][c];
+        sum[c] = x;
+    }
+    const uint32_t n_valid = p.ctrl[CTRL_NVALID];
+    const double n = p.divisor > 0.f ? (double)p.divisor : (double)n_valid;
+    float out[NSCALARS];
+    for (int i = 0; i < NSCALARS; ++i) out[i] = 0.f;
+    if (n_valid > 0 && n > 0.0) {
+        const double inv = 1.0 / n;
+        double ce = 0, z = 0, kl = 0, grpo = 0;
+        if (f & F_CE) { ce = sum[RC_CE] * inv; out[0] = (float)ce; }
+        if (f & F_Z) { z = sum[RC_Z] * inv; out[1] = (float)z; }
+        if (f & (F_FKL | F_RKL)) { kl = sum[RC_KL] * inv; out[2] = (float)kl; }
+        if (f & F_GRPO) {
+            grpo = sum[RC_GRPO] * inv;
+            out[3] = (float)grpo;
+            out[4] = (float)(sum[RC_LOGP] * inv);
+            out[5] = (float)(sum[RC_RATIO] * inv);
+            out[6] = (float)(sum[RC_CLIP] * inv);
+            out[7] = (float)(sum[RC_K3] * inv);
+            out[8] = (float)(sum[RC_ADV] * inv);
+        }
+        if (f & F_ENT) out[9] = (float)(sum[RC_ENT] * inv);
+        out[10] = (float)((double)p.w_ce * ce + (double)p.w_z * z + (double)p.w_d * kl +
+                          (double)p.w_g * grpo);
+    }
+    out[11] = (float)n_valid;
+    out[12] = (float)p.ctrl[CTRL_NBAD];
+    if (p.ctrl[CTRL_ERROR] != 0u) {
+        // a split-vocab row never saw all of its chunks: nothing is trustworthy
+        for (int i = 0; i < 11; ++i) out[i] = __builtin_nanf("");
+    }
+    for (int i = 0; i < NSCALARS; ++i) p.scalars[i] = out[i];
+}
+
+hipError_t launch_count(const CountParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(count_kernel, dim3(1), dim3(1024), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(reduce_kernel, dim3(1), dim3(1024), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace hl

@@ -1,0 +1,588 @@
+// Device code of the fused LM-head loss for gfx950 (CDNA4).
+//
+// Three kernels per call, all on the caller's stream:
+//   count_kernel   valid-row count and bad-label count (the batch divisor
+//                  must be known before any gradient is written);
+//   fused_kernel   one workgroup per (row, vocabulary chunk): loads its slice
+//                  of the row into registers once, computes the softmax
+//                  statistics (max, sum-exp, entropy sum, teacher sums) with
+//                  wave64 DPP reductions, combines them across waves (and,
+//                  in the split-vocab variant, across the row's chunks), forms
+//                  the per-row coefficients and writes the gradient from the
+//                  registers it already holds;
+//   reduce_kernel  fixed-order fp64 sum of the per-row values into the batch
+//                  scalars.
+//
+// The gradient is written in the two-coefficient form of Fast-LLM PR #558
+// (Triton kernel for the monolithic loss, section Design): prob_coeff times
+// the softmax minus label_coeff at the label column, plus the distillation
+// term, formed in fp32 and rounded once (Fast-LLM PR #549, "Monolithic fused
+// head-loss kernel (torch.compile)", section Approach).
+#pragma once
+
+#include "hl_internal.h"
+
+namespace hl {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2f = 0.69314718055994530942f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------------------
+// Element formats. A 16-byte vector holds VEC elements.
+// ---------------------------------------------------------------------------
+struct F32T {
+    static constexpr int VEC = 4;
+    static constexpr int ESIZE = 4;
+    __device__ static __forceinline__ float get(const u32x4& w, int e) {
+        return __uint_as_float(w[e]);
+    }
+    __device__ static __forceinline__ float load1(const char* rowbase, int64_t i) {
+        return reinterpret_cast<const float*>(rowbase)[i];
+    }
+    __device__ static __forceinline__ void store1(char* rowbase, int64_t i, float g) {
+        reinterpret_cast<float*>(rowbase)[i] = g;
+    }
+    __device__ static __forceinline__ u32x4 pack(const float* g) {
+        u32x4 r;
+        r[0] = __float_as_uint(g[0]);
+        r[1] = __float_as_uint(g[1]);
+        r[2] = __float_as_uint(g[2]);
+        r[3] = __float_as_uint(g[3]);
+        return r;
+    }
+};
+
+struct BF16T {
+    static constexpr int VEC = 8;
+    static constexpr int ESIZE = 2;
+    // bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32.
+    __device__ static __forceinline__ float get(const u32x4& w, int e) {
+        const uint32_t word = w[e >> 1];
+        return (e & 1) ? __uint_as_float(word & 0xffff0000u) : __uint_as_float(word << 16);
+    }
+    __device__ static __forceinline__ float load1(const char* rowbase, int64_t i) {
+        const uint32_t h = reinterpret_cast<const uint16_t*>(rowbase)[i];
+        return __uint_as_float(h << 16);
+    }
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+        f32x2 v = {lo, hi};
+        bf16x2 b = __builtin_convertvector(v, bf16x2);   // v_cvt_pk_bf16_f32, RNE
+        return __builtin_bit_cast(uint32_t, b);
+    }
+    __device__ static __forceinline__ void store1(char* rowbase, int64_t i, float g) {
+        reinterpret_cast<uint16_t*>(rowbase)[i] = static_cast<uint16_t>(pack2(g, 0.0f) & 0xffffu);
+    }
+    __device__ static __forceinline__ u32x4 pack(const float* g) {
+        u32x4 r;
+        r[0] = pack2(g[0], g[1]);
+        r[1] = pack2(g[2], g[3]);
+        r[2] = pack2(g[4], g[5]);
+        r[3] = pack2(g[6], g[7]);
+        return r;
+    }
+};
+
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
+__device__ __forceinline__ float fast_exp2(float a) { return __builtin_amdgcn_exp2f(a); }
+
+// tanh from its definition: an odd Taylor polynomial (coefficients
+// 2^(2n) (2^(2n)-1) B_2n / (2n)!) for |z| < 0.55, where nine terms leave a
+// truncation error below 3e-9, and 1 - 2 / (exp(2|z|) + 1) above, where that
+// form has no cancellation.
+__device__ __forceinline__ float hl_tanh(float z) {
+    const float az = fabsf(z);
+    float r;
+    if (az < 0.55f) {
+        const float z2 = z * z;
+        float p = 0.000590027440945586f;
+        p = fmaf(p, z2, -0.0014558343870513183f);
+        p = fmaf(p, z2, 0.003592128036572481f);
+        p = fmaf(p, z2, -0.008863235529902197f);
+        p = fmaf(p, z2, 0.021869488536155203f);
+        p = fmaf(p, z2, -0.05396825396825397f);
+        p = fmaf(p, z2, 0.13333333333333333f);
+        p = fmaf(p, z2, -0.3333333333333333f);
+        r = fmaf(z * z2, p, z);
+    } else {
+        const float e = fast_exp2(az * (2.0f * kLog2e));
+        r = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+        r = copysignf(r, z);
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions. Within a row of 16 lanes: DPP quad_perm (xor 1, xor 2),
+// row_half_mirror, row_mirror; across rows: lane permutes. Every lane ends
+// with the same value, combined in the same pairing order.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // row_half_mirror
+constexpr int DPP_MIRROR = 0x140;       // row_mirror
+
+__device__ __forceinline__ float xor_lanes(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<DPP_XOR1>(v));
+    v = fmaxf(v, dpp<DPP_XOR2>(v));
+    v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+    v = fmaxf(v, dpp<DPP_MIRROR>(v));
+    v = fmaxf(v, xor_lanes(v, 16));
+    v = fmaxf(v, xor_lanes(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = __fadd_rn(v, dpp<DPP_XOR1>(v));
+    v = __fadd_rn(v, dpp<DPP_XOR2>(v));
+    v = __fadd_rn(v, dpp<DPP_HALF_MIRROR>(v));
+    v = __fadd_rn(v, dpp<DPP_MIRROR>(v));
+    v = __fadd_rn(v, xor_lanes(v, 16));
+    v = __fadd_rn(v, xor_lanes(v, 32));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Softmax-statistics record and its merge (the max-rescaling combine of an
+// online softmax). Written with non-contracted operations so that
+// merge(a, b) == merge(b, a) bit for bit; an empty slice has Z == 0.
+// ---------------------------------------------------------------------------
+struct Rec {
+    float M, Z, S, Mt, Zt, SX;
+};
+
+__device__ __forceinline__ Rec rec_empty() { return Rec{kNegInf, 0.f, 0.f, kNegInf, 0.f, 0.f}; }
+
+template <int TMODE>
+__device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b) {
+    const bool ea = (a.Z == 0.f), eb = (b.Z == 0.f);
+    Rec r;
+    const float M = fmaxf(a.M, b.M);
+    const float da = __fsub_rn(a.M, M), db = __fsub_rn(b.M, M);
+    const float fa = fast_exp2(da), fb = fast_exp2(db);
+    r.M = M;
+    r.Z = __fadd_rn(__fmul_rn(a.Z, fa), __fmul_rn(b.Z, fb));
+    r.S = __fadd_rn(__fmul_rn(fa, __fadd_rn(a.S, __fmul_rn(da, a.Z))),
+                    __fmul_rn(fb, __fadd_rn(b.S, __fmul_rn(db, b.Z))));
+    if (TMODE != TM_NONE) {
+        const float Mt = fmaxf(a.Mt, b.Mt);
+        const float dta = __fsub_rn(a.Mt, Mt), dtb = __fsub_rn(b.Mt, Mt);
+        const float fta = fast_exp2(dta), ftb = fast_exp2(dtb);
+        r.Mt = Mt;
+        r.Zt = __fadd_rn(__fmul_rn(a.Zt, fta), __fmul_rn(b.Zt, ftb));
+        if (TMODE == TM_FKL) {
+            // SX = sum_j 2^u_j (u_j - a_j): both offsets move
+            r.SX = __fadd_rn(__fmul_rn(fta, __fadd_rn(a.SX, __fmul_rn(__fsub_rn(dta, da), a.Zt))),
+                             __fmul_rn(ftb, __fadd_rn(b.SX, __fmul_rn(__fsub_rn(dtb, db), b.Zt))));
+        } else {
+            // SX = sum_j 2^a_j (a_j - u_j)
+            r.SX = __fadd_rn(__fmul_rn(fa, __fadd_rn(a.SX, __fmul_rn(__fsub_rn(da, dta), a.Z))),
+                             __fmul_rn(fb, __fadd_rn(b.SX, __fmul_rn(__fsub_rn(db, dtb), b.Z))));
+        }
+    } else {
+        r.Mt = 0.f; r.Zt = 0.f; r.SX = 0.f;
+    }
+    if (ea) r = b;
+    if (eb) r = a;
+    return r;
+}
+
+template <int CTRL, int TMODE>
+__device__ __forceinline__ Rec rec_dpp_step(const Rec& a) {
+    Rec b;
+    b.M = dpp<CTRL>(a.M);
+    b.Z = dpp<CTRL>(a.Z);
+    b.S = dpp<CTRL>(a.S);
+    if (TMODE != TM_NONE) {
+        b.Mt = dpp<CTRL>(a.Mt);
+        b.Zt = dpp<CTRL>(a.Zt);
+        b.SX = dpp<CTRL>(a.SX);
+    } else {
+        b.Mt = 0.f; b.Zt = 0.f; b.SX = 0.f;
+    }
+    return rec_merge<TMODE>(a, b);
+}
+
+// Merge the records held by lanes 0..15 of every 16-lane row; all lanes end
+// with the same result.
+template <int TMODE>
+__device__ __forceinline__ Rec rec_reduce16(Rec r) {
+    r = rec_dpp_step<DPP_XOR1, TMODE>(r);
+    r = rec_dpp_step<DPP_XOR2, TMODE>(r);
+    r = rec_dpp_step<DPP_HALF_MIRROR, TMODE>(r);
+    r = rec_dpp_step<DPP_MIRROR, TMODE>(r);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Row validity (shared by the count and fused kernels): masked when the mask
+// byte is 0, the label is -100, or the label is outside [0, V).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void row_status(const int64_t* labels, const uint8_t* mask, int64_t row,
+                                           int64_t V, bool& valid, bool& bad, int64_t& y) {
+    const bool unmasked = (mask == nullptr) || (mask[row] != 0);
+    valid = unmasked;
+    bad = false;
+    y = -1;
+    if (labels != nullptr) {
+        y = labels[row];
+        const bool in_range = (y >= 0) && (y < V);
+        valid = unmasked && in_range;
+        bad = unmasked && !in_range && (y != -100);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fused_kernel
+// ---------------------------------------------------------------------------
+// Bounded wait for the sibling chunks of a row (split-vocab variant only).
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+template <typename T, int BLOCK, int NVEC, int TMODE, bool SOFTCAP>
+__global__ __launch_bounds__(BLOCK) void fused_kernel(const FusedParams p) {
+    constexpr int VEC = T::VEC;
+    constexpr int ES = T::ESIZE;
+    constexpr int NW = BLOCK / 64;
+    static_assert(NW <= 16, "at most 16 waves per workgroup");
+
+    __shared__ float s_rec[16][REC];
+    __shared__ float s_fin[REC];
+    __shared__ float s_row[8];
+    __shared__ uint32_t s_item;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    // Which (row, chunk) this workgroup owns. With several chunks per row the
+    // items are claimed in order from a counter, so every chunk a workgroup
+    // waits for has already been claimed by a running workgroup.
+    uint32_t item;
+    if (p.chunks > 1) {
+        if (tid == 0) s_item = atomicAdd(&p.ctrl[CTRL_CLAIM], 1u);
+        __syncthreads();
+        item = s_item;
+    } else {
+        item = blockIdx.x;
+    }
+    const int64_t row = item / (uint32_t)p.chunks;
+    const int c = (int)(item % (uint32_t)p.chunks);
+
+    bool valid, bad;
+    int64_t y;
+    row_status(p.labels, p.mask, row, p.V, valid, bad, y);
+
+    // Row geometry: an unaligned head (< VEC elements), full 16-byte body
+    // vectors, a tail (< VEC elements). Head and tail belong to chunk 0.
+    const int64_t V = p.V;
+    const int64_t rowoff = row * V;
+    const int mis = (int)((rowoff * ES) & 15);
+    int head = mis ? (16 - mis) / ES : 0;
+    if (head > V) head = (int)V;
+    const int64_t nbv = (V - head) / VEC;
+    const int tail = (int)(V - head - nbv * VEC);
+    const int64_t cv = (nbv + p.chunks - 1) / p.chunks;
+    const int64_t vb = (int64_t)c * cv;
+    int64_t ve = vb + cv;
+    if (ve > nbv) ve = nbv;
+    const int nv = ve > vb ? (int)(ve - vb) : 0;
+    const int n_extra = (c == 0) ? head + tail : 0;
+    const bool has_e = tid < n_extra;
+    const int64_t eidx = (tid < head) ? (int64_t)tid : (int64_t)head + nbv * VEC + (tid - head);
+
+    const char* xrow = static_cast<const char*>(p.logits) + rowoff * ES;
+    const char* trow = static_cast<const char*>(p.teacher) + rowoff * ES;
+    char* grow = static_cast<char*>(p.grad) + rowoff * ES;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(xrow + (int64_t)head * ES) + vb;
+    const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)head * ES) + vb;
+    u32x4* gv = reinterpret_cast<u32x4*>(grow + (int64_t)head * ES) + vb;
+
+    if (!valid) {
+        if (p.grad != nullptr && !p.accumulate) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            for (int i = tid; i < nv; i += BLOCK) st_stream(gv + i, z);
+            if (has_e) T::store1(grow, eidx, 0.0f);
+        }
+        if (c == 0 && tid < REC) p.row_rec[row * REC + tid] = 0.0f;
+        return;
+    }
+
+    // Per-row scalars, fetched early by one thread.
+    if (tid == 0) {
+        s_row[0] = (y >= 0) ? T::load1(xrow, y) : 0.0f;
+        s_row[1] = p.old_logprobs ? p.old_logprobs[row] : 0.0f;
+        s_row[2] = p.advantages ? p.advantages[row] : 0.0f;
+    }
+
+    // ---- load the slice into registers (read once) ----
+    // Per-vector bounds and addresses are uniform (vector v of thread tid is
+    // element v * BLOCK + tid of the slice), so each test is tid < uniform and
+    // every address is a uniform base plus the one per-thread offset.
+    u32x4 xs[NVEC];
+    u32x4 ts[TMODE != TM_NONE ? NVEC : 1];
+#pragma unroll
+    for (int v = 0; v < NVEC; ++v) {
+        if (tid < nv - v * BLOCK) {
+            xs[v] = ld_stream(xv + v * BLOCK + tid);
+            if (TMODE != TM_NONE) ts[v] = ld_stream(tv + v * BLOCK + tid);
+        }
+    }
+    float xe = 0.f, te = 0.f;
+    if (has_e) {
+        xe = T::load1(xrow, eidx);
+        if (TMODE != TM_NONE) te = T::load1(trow, eidx);
+    }
+
+    // ---- pass 1a: max of the raw logits (the transform is increasing) ----
+    float mx = kNegInf, mt = kNegInf;
+#pragma unroll
+    for (int v = 0; v < NVEC; ++v) {
+        if (tid < nv - v * BLOCK) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                mx = fmaxf(mx, T::get(xs[v], e));
+                if (TMODE != TM_NONE) mt = fmaxf(mt, T::get(ts[v], e));
+            }
+        }
+    }
+    if (has_e) {
+        mx = fmaxf(mx, xe);
+        if (TMODE != TM_NONE) mt = fmaxf(mt, te);
+    }
+    mx = wave_max(mx);
+    const float M = SOFTCAP ? (p.cap * hl_tanh(mx * p.kc)) * kLog2e : mx * p.K1;
+    float Mt = 0.f;
+    if (TMODE != TM_NONE) Mt = wave_max(mt) * p.K2;
+
+    // ---- pass 1b: sums relative to the wave shift, in the log2 domain ----
+    float Z = 0.f, S = 0.f, Zt = 0.f, SX = 0.f;
+    auto accumulate = [&](float x, float t, float& z, float& s, float& zt, float& sx) {
+        const float a = SOFTCAP ? fmaf(p.cap * hl_tanh(x * p.kc), kLog2e, -M) : fmaf(x, p.K1, -M);
+        const float ex = fast_exp2(a);
+        z += ex;
+        s = fmaf(ex, a, s);
+        if (TMODE != TM_NONE) {
+            const float u = fmaf(t, p.K2, -Mt);
+            const float et = fast_exp2(u);
+            zt += et;
+            if (TMODE == TM_FKL) sx = fmaf(et, u - a, sx);
+            else sx = fmaf(ex, a - u, sx);
+        }
+    };
+#pragma unroll
+    for (int v = 0; v < NVEC; ++v) {
+        if (tid < nv - v * BLOCK) {
+            float z = 0.f, s = 0.f, zt = 0.f, sx = 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                accumulate(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z, s, zt, sx);
+            Z += z; S += s; Zt += zt; SX += sx;
+        }
+    }
+    if (has_e) accumulate(xe, te, Z, S, Zt, SX);
+
+    Z = wave_sum(Z);
+    S = wave_sum(S);
+    if (TMODE != TM_NONE) {
+        Zt = wave_sum(Zt);
+        SX = wave_sum(SX);
+    }
+    if (lane == 0) {
+        s_rec[wave][0] = M;
+        s_rec[wave][1] = Z;
+        s_rec[wave][2] = S;
+        s_rec[wave][3] = Mt;
+        s_rec[wave][4] = Zt;
+        s_rec[wave][5] = SX;
+    }
+    __syncthreads();
+
+    // ---- combine the waves' records (every wave, DPP tree over 16 lanes) ----
+    Rec r = rec_empty();
+    {
+        const int w = lane & 15;
+        if (w < NW) {
+            r.M = s_rec[w][0];
+            r.Z = s_rec[w][1];
+            r.S = s_rec[w][2];
+            r.Mt = s_rec[w][3];
+            r.Zt = s_rec[w][4];
+            r.SX = s_rec[w][5];
+            if (r.Z == 0.f) r = rec_empty();
+        }
+        r = rec_reduce16<TMODE>(r);
+    }
+
+    // ---- split-vocab: publish this chunk's record, wait for the others ----
+    if (p.chunks > 1) {
+        if (tid == 0) {
+            float* mine = p.chunk_rec + ((int64_t)row * p.chunks + c) * REC;
+            mine[0] = r.M; mine[1] = r.Z; mine[2] = r.S;
+            mine[3] = r.Mt; mine[4] = r.Zt; mine[5] = r.SX;
+            uint32_t* cnt = p.row_counters + row;
+            __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t spins = 0;
+            while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.chunks) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++spins > kSpinLimit) {
+                    __hip_atomic_store(&p.ctrl[CTRL_ERROR], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+            const float* all = p.chunk_rec + (int64_t)row * p.chunks * REC;
+            Rec acc = rec_empty();
+            for (int cc = 0; cc < p.chunks; ++cc) {
+                const float* q = all + cc * REC;
+                Rec b;
+                b.M = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                b.Z = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                b.S = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                b.Mt = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                b.Zt = __hip_atomic_load(q + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                b.SX = __hip_atomic_load(q + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                acc = rec_merge<TMODE>(acc, b);
+            }
+            s_fin[0] = acc.M; s_fin[1] = acc.Z; s_fin[2] = acc.S;
+            s_fin[3] = acc.Mt; s_fin[4] = acc.Zt; s_fin[5] = acc.SX;
+        }
+        __syncthreads();
+        r.M = s_fin[0]; r.Z = s_fin[1]; r.S = s_fin[2];
+        r.Mt = s_fin[3]; r.Zt = s_fin[4]; r.SX = s_fin[5];
+    }
+
+    // ---- per-row record for the batch reduction ----
+    if (c == 0 && tid == 0) {
+        float* out = p.row_rec + row * REC;
+        out[R_M] = r.M; out[R_Z] = r.Z; out[R_S] = r.S;
+        out[R_MT] = r.Mt; out[R_ZT] = r.Zt; out[R_SX] = r.SX;
+        out[R_XY] = s_row[0];
+        out[R_VALID] = 1.0f;
+    }
+    if (p.grad == nullptr) return;
+
+    // ---- gradient coefficients (fp32, every thread) ----
+    // All data registers are live here, so only single-instruction hardware
+    // log2 / exp2 / rcp are used; the reported per-row values are recomputed
+    // in fp64 by the reduction kernel from the same record.
+    const uint32_t f = p.flags;
+    const float l2Z = __builtin_amdgcn_logf(r.Z);
+    const float B2 = r.M + l2Z;                        // log2-domain lse
+    const float lse = B2 * kLn2f;
+    float Bt2 = 0.f, kl = 0.f;
+    if (TMODE != TM_NONE) {
+        const float l2Zt = __builtin_amdgcn_logf(r.Zt);
+        Bt2 = r.Mt + l2Zt;
+        if (TMODE == TM_RKL) kl = kLn2f * (r.SX * __builtin_amdgcn_rcpf(r.Z) - l2Z + l2Zt);
+    }
+    float a_g = 0.f;
+    if ((f & F_GRPO) && y >= 0) {
+        const float xy = s_row[0];
+        const float sy = SOFTCAP ? p.cap * hl_tanh(xy * p.kc) : p.k * xy;
+        const float d = (sy - lse) - s_row[1];
+        const float ratio = fast_exp2(d * kLog2e);
+        const float adv = s_row[2];
+        const bool active = !((adv > 0.f && ratio > 1.f + p.eps) || (adv < 0.f && ratio < 1.f - p.eps));
+        a_g = active ? adv * ratio : 0.f;
+    }
+    const uint32_t n_valid = p.ctrl[CTRL_NVALID];
+    const float n = p.divisor > 0.f ? p.divisor : (float)n_valid;
+    const float scale = p.grad_scale * p.k / n;
+    float P = 0.f, L = 0.f, wd = 0.f;
+    if ((f & F_CE) && p.w_ce != 0.f) { P += p.w_ce; L += p.w_ce; }
+    if ((f & F_Z) && p.w_z != 0.f) P += 2.f * p.w_z * lse;
+    if ((f & F_GRPO) && p.w_g != 0.f) { P += p.w_g * a_g; L += p.w_g * a_g; }
+    if ((f & (F_FKL | F_RKL)) && p.w_d != 0.f) wd = p.w_d;
+    if (TMODE == TM_FKL) P += wd;
+    const float alpha = scale * P;             // prob_coeff (times G k / n)
+    const float beta = scale * L;              // label_coeff
+    const float gam = scale * wd;              // forward-KL teacher coefficient
+    const float rho2 = scale * wd * kLn2f;
+    const float c0 = scale * (P - wd * kl);
+
+    // grad for one element; lab = label_coeff at the label column, else 0
+    auto grad_elem = [&](float x, float t, float lab) -> float {
+        float aq, cf = 1.0f;
+        if (SOFTCAP) {
+            const float th = hl_tanh(x * p.kc);
+            aq = fmaf(p.cap * th, kLog2e, -B2);
+            cf = fmaf(-th, th, 1.0f);
+        } else {
+            aq = fmaf(x, p.K1, -B2);
+        }
+        const float q = fast_exp2(aq);
+        float g;
+        if (TMODE == TM_NONE) {
+            g = fmaf(alpha, q, -lab);
+        } else if (TMODE == TM_FKL) {
+            const float pt = fast_exp2(fmaf(t, p.K2, -Bt2));
+            g = fmaf(alpha, q, fmaf(-gam, pt, -lab));
+        } else {
+            const float up = fmaf(t, p.K2, -Bt2);
+            g = fmaf(q, fmaf(rho2, aq - up, c0), -lab);
+        }
+        return SOFTCAP ? cf * g : g;
+    };
+
+    // label position relative to this chunk's body vectors (-1: not here)
+    int yv = -1;
+    int ly = 0;
+    if (y >= head + vb * VEC && y < head + ve * VEC) {
+        yv = (int)((y - head) / VEC - vb);
+        ly = (int)((y - head) % VEC);
+    }
+
+#pragma unroll
+    for (int v = 0; v < NVEC; ++v) {
+        if (tid < nv - v * BLOCK) {
+            float g[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                g[e] = grad_elem(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, 0.f);
+            if (tid == yv - v * BLOCK) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    if (e == ly)
+                        g[e] = grad_elem(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, beta);
+            }
+            if (p.accumulate) {
+                const u32x4 old = ld_stream(gv + v * BLOCK + tid);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) g[e] = T::get(old, e) + g[e];
+            }
+            st_stream(gv + v * BLOCK + tid, T::pack(g));
+        }
+    }
+    if (has_e) {
+        float g = grad_elem(xe, te, eidx == y ? beta : 0.f);
+        if (p.accumulate) g = T::load1(grow, eidx) + g;
+        T::store1(grow, eidx, g);
+    }
+}
+
+template <typename T, int BLOCK, int NVEC, int TMODE, bool SOFTCAP>
+hipError_t launch_fused(const FusedParams& p, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((fused_kernel<T, BLOCK, NVEC, TMODE, SOFTCAP>), grid, dim3(BLOCK), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace hl
+
+// Instantiation helper for the per-(dtype, mode) translation units.
+#define HL_FUSED_CASE(T, BLOCK, NVEC, TMODE)                                 \
+    if (block == BLOCK && nvec == NVEC)                                      \
+        return softcap ? &hl::launch_fused<T, BLOCK, NVEC, TMODE, true>      \
+                       : &hl::launch_fused<T, BLOCK, NVEC, TMODE, false>;

@@ -1,0 +1,338 @@
+// Host side of the C ABI declared in include/headloss.h: plan validation,
+// kernel-variant choice, workspace layout and the per-call launch sequence.
+#include "headloss.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "hl_internal.h"
+
+using namespace hl;
+
+struct hl_plan_s {
+    int64_t V;
+    hl_dtype dtype;
+    uint32_t flags;
+    hl_weights w;
+    float temperature;
+    float eps;
+    float logit_scale;
+    float softcap;
+    int tmode;
+    int forced_chunks;
+    Geometry geo;
+    FusedLauncher fused;
+    void* ws;
+    size_t ws_bytes;
+    bool ws_owned;
+    int64_t last_rows;
+    hipEvent_t ev_before;
+    hipEvent_t ev_after;
+};
+
+namespace {
+
+constexpr uint32_t kLossBits = HL_CE | HL_ZLOSS | HL_FKL | HL_RKL | HL_GRPO | HL_ENTROPY;
+constexpr uint32_t kKnownBits = kLossBits | HL_ACCUMULATE;
+constexpr int kMaxChunks = 64;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+    size_t ctrl, counters, chunk_rec, row_rec, rows, total;
+};
+
+Layout layout_for(const hl_plan_s* p, int64_t n) {
+    Layout L;
+    const size_t N = n > 0 ? (size_t)n : 0;
+    L.ctrl = 0;
+    L.counters = align256(NCTRL * sizeof(uint32_t));
+    L.chunk_rec = L.counters + align256(N * sizeof(uint32_t));
+    const size_t rec_bytes = p->geo.chunks > 1 ? N * p->geo.chunks * REC * sizeof(float) : 0;
+    L.row_rec = L.chunk_rec + align256(rec_bytes);
+    L.rows = L.row_rec + align256(N * REC * sizeof(float));
+    L.total = L.rows + align256(N * NCOL * sizeof(float));
+    return L;
+}
+
+int round_up_to(const int* set, int n_set, int need) {
+    for (int i = 0; i < n_set; ++i)
+        if (set[i] >= need) return set[i];
+    return -1;
+}
+
+FusedLauncher lookup(hl_dtype dt, int tmode, int block, int nvec, bool softcap) {
+    if (dt == HL_F32) {
+        if (tmode == TM_NONE) return get_fused_f32_none(block, nvec, softcap);
+        if (tmode == TM_FKL) return get_fused_f32_fkl(block, nvec, softcap);
+        return get_fused_f32_rkl(block, nvec, softcap);
+    }
+    if (tmode == TM_NONE) return get_fused_bf16_none(block, nvec, softcap);
+    if (tmode == TM_FKL) return get_fused_bf16_fkl(block, nvec, softcap);
+    return get_fused_bf16_rkl(block, nvec, softcap);
+}
+
+// Geometry for C chunks per row, or chunks = 0 when none fits. The register
+// budget per thread is 20 vectors (80 VGPRs) for the student alone and 10 +
+// 10 with a teacher, so that a 1024-thread workgroup stays within 128 VGPRs.
+Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C) {
+    const int vec = dt == HL_F32 ? 4 : 8;
+    int64_t nvec_row = V / vec;
+    if (nvec_row < 1) nvec_row = 1;
+    const int64_t per = (nvec_row + C - 1) / C;
+    Geometry g{0, 0, 0};
+    if (per <= (int64_t)kSmallBlock * 4) {
+        const int need = (int)((per + kSmallBlock - 1) / kSmallBlock);
+        g = Geometry{C, kSmallBlock, round_up_to(kSmallNvec, 3, need)};
+        return g;
+    }
+    const int* set = tmode == TM_NONE ? kLargeNvecStudent : kLargeNvecTeacher;
+    const int n_set = tmode == TM_NONE ? 10 : 5;
+    const int64_t need = (per + kLargeBlock - 1) / kLargeBlock;
+    if (need > set[n_set - 1]) return g;
+    return Geometry{C, kLargeBlock, round_up_to(set, n_set, (int)need)};
+}
+
+hl_status choose(hl_plan_s* p) {
+    if (p->forced_chunks > 0) {
+        Geometry g = geometry_for(p->V, p->dtype, p->tmode, p->forced_chunks);
+        if (g.chunks == 0) return HL_ERR_UNSUPPORTED;
+        p->geo = g;
+    } else {
+        Geometry g{0, 0, 0};
+        for (int C = 1; C <= kMaxChunks && g.chunks == 0; ++C) g = geometry_for(p->V, p->dtype, p->tmode, C);
+        if (g.chunks == 0) return HL_ERR_UNSUPPORTED;
+        p->geo = g;
+    }
+    p->fused = lookup(p->dtype, p->tmode, p->geo.block, p->geo.nvec, p->softcap > 0.f);
+    return p->fused ? HL_OK : HL_ERR_UNSUPPORTED;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags,
+                  const hl_weights* weights, float temperature, float eps,
+                  float logit_scale, float softcap) {
+    if (out == nullptr) return HL_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (V < 1 || weights == nullptr) return HL_ERR_INVALID_ARG;
+    if (dtype != HL_F32 && dtype != HL_BF16) return HL_ERR_INVALID_ARG;
+    if ((loss_flags & ~kKnownBits) != 0u || (loss_flags & kLossBits) == 0u) return HL_ERR_INVALID_ARG;
+    if ((loss_flags & HL_FKL) && (loss_flags & HL_RKL)) return HL_ERR_INVALID_ARG;
+    const bool distill = (loss_flags & (HL_FKL | HL_RKL)) != 0u;
+    if (distill && !(finite(temperature) && temperature > 0.f)) return HL_ERR_INVALID_ARG;
+    if ((loss_flags & HL_GRPO) && !(finite(eps) && eps > 0.f && eps < 1.f)) return HL_ERR_INVALID_ARG;
+    if (!(finite(logit_scale) && logit_scale > 0.f)) return HL_ERR_INVALID_ARG;
+    if (!(finite(softcap) && softcap >= 0.f)) return HL_ERR_INVALID_ARG;
+    const hl_weights& w = *weights;
+    if (!(finite(w.ce) && finite(w.z) && finite(w.distill) && finite(w.grpo) &&
+          finite(w.grad_scale) && finite(w.divisor)))
+        return HL_ERR_INVALID_ARG;
+
+    hl_plan_s* p = new (std::nothrow) hl_plan_s;
+    if (p == nullptr) return HL_ERR_INVALID_ARG;
+    std::memset(p, 0, sizeof(*p));
+    p->V = V;
+    p->dtype = dtype;
+    p->flags = loss_flags;
+    p->w = w;
+    p->temperature = distill ? temperature : 1.f;
+    p->eps = eps;
+    p->logit_scale = logit_scale;
+    p->softcap = softcap;
+    p->tmode = (loss_flags & HL_FKL) ? TM_FKL : (loss_flags & HL_RKL) ? TM_RKL : TM_NONE;
+    const hl_status st = choose(p);
+    if (st != HL_OK) {
+        delete p;
+        return st;
+    }
+    *out = p;
+    return HL_OK;
+}
+
+void hl_plan_destroy(hl_plan_t plan) {
+    if (plan == nullptr) return;
+    if (plan->ws_owned && plan->ws) (void)hipFree(plan->ws);
+    delete plan;
+}
+
+size_t hl_workspace_bytes(hl_plan_t plan, int64_t n_rows) {
+    if (plan == nullptr || n_rows < 0) return 0;
+    return layout_for(plan, n_rows).total;
+}
+
+hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t bytes) {
+    if (plan == nullptr || dev_workspace == nullptr) return HL_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(dev_workspace) & 255u) != 0) return HL_ERR_INVALID_ARG;
+    if (plan->ws_owned && plan->ws) (void)hipFree(plan->ws);
+    plan->ws = dev_workspace;
+    plan->ws_bytes = bytes;
+    plan->ws_owned = false;
+    return HL_OK;
+}
+
+hl_status hl_plan_set_chunks(hl_plan_t plan, int chunks) {
+    if (plan == nullptr || chunks < 0 || chunks > kMaxChunks) return HL_ERR_INVALID_ARG;
+    const int prev = plan->forced_chunks;
+    const Geometry prev_geo = plan->geo;
+    const FusedLauncher prev_fn = plan->fused;
+    plan->forced_chunks = chunks;
+    const hl_status st = choose(plan);
+    if (st != HL_OK) {
+        plan->forced_chunks = prev;
+        plan->geo = prev_geo;
+        plan->fused = prev_fn;
+    }
+    return st;
+}
+
+hl_status hl_plan_describe(hl_plan_t plan, int* chunks, int* block, int* vec_per_thread) {
+    if (plan == nullptr) return HL_ERR_INVALID_ARG;
+    if (chunks) *chunks = plan->geo.chunks;
+    if (block) *block = plan->geo.block;
+    if (vec_per_thread) *vec_per_thread = plan->geo.nvec;
+    return HL_OK;
+}
+
+hl_status hl_plan_set_timing_events(hl_plan_t plan, hipEvent_t before, hipEvent_t after) {
+    if (plan == nullptr) return HL_ERR_INVALID_ARG;
+    plan->ev_before = before;
+    plan->ev_after = after;
+    return HL_OK;
+}
+
+const float* hl_row_values(hl_plan_t plan) {
+    if (plan == nullptr || plan->ws == nullptr) return nullptr;
+    const Layout L = layout_for(plan, plan->last_rows);
+    return reinterpret_cast<const float*>(static_cast<const char*>(plan->ws) + L.rows);
+}
+
+hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits,
+                              const int64_t* labels, const uint8_t* mask,
+                              const void* teacher_logits, const float* old_logprobs,
+                              const float* advantages, void* grad_out,
+                              float* scalars_out, hipStream_t stream) {
+    if (plan == nullptr || n_rows < 0 || scalars_out == nullptr) return HL_ERR_INVALID_ARG;
+    if (n_rows > 0 && logits == nullptr) return HL_ERR_INVALID_ARG;
+    const uint32_t f = plan->flags;
+    if (n_rows > 0) {
+        if ((f & (HL_CE | HL_GRPO)) && labels == nullptr) return HL_ERR_MISSING_INPUT;
+        if ((f & (HL_FKL | HL_RKL)) && teacher_logits == nullptr) return HL_ERR_MISSING_INPUT;
+        if ((f & HL_GRPO) && (old_logprobs == nullptr || advantages == nullptr)) return HL_ERR_MISSING_INPUT;
+        if (!aligned16(logits)) return HL_ERR_INVALID_ARG;
+        if (plan->tmode != TM_NONE && !aligned16(teacher_logits)) return HL_ERR_INVALID_ARG;
+        if (grad_out != nullptr && !aligned16(grad_out)) return HL_ERR_INVALID_ARG;
+        if ((uint64_t)n_rows * (uint64_t)plan->geo.chunks > 0x7fffffffull) return HL_ERR_UNSUPPORTED;
+    }
+
+    const Layout L = layout_for(plan, n_rows);
+    if (plan->ws == nullptr || plan->ws_bytes < L.total) {
+        if (plan->ws != nullptr && !plan->ws_owned) return HL_ERR_WORKSPACE;
+        if (plan->ws_owned && plan->ws) {
+            (void)hipFree(plan->ws);
+            plan->ws = nullptr;
+            plan->ws_bytes = 0;
+        }
+        void* mem = nullptr;
+        if (hipMalloc(&mem, L.total) != hipSuccess) return HL_ERR_HIP;
+        plan->ws = mem;
+        plan->ws_bytes = L.total;
+        plan->ws_owned = true;
+    }
+    plan->last_rows = n_rows;
+    char* ws = static_cast<char*>(plan->ws);
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
+    uint32_t* counters = reinterpret_cast<uint32_t*>(ws + L.counters);
+    float* chunk_rec = reinterpret_cast<float*>(ws + L.chunk_rec);
+    float* row_rec = reinterpret_cast<float*>(ws + L.row_rec);
+    float* rows = reinterpret_cast<float*>(ws + L.rows);
+    const int C = plan->geo.chunks;
+
+    CountParams cp;
+    cp.labels = labels;
+    cp.mask = mask;
+    cp.ctrl = ctrl;
+    cp.row_counters = C > 1 ? counters : nullptr;
+    cp.n_rows = n_rows;
+    cp.V = plan->V;
+    if (launch_count(cp, stream) != hipSuccess) return HL_ERR_HIP;
+
+    if (n_rows > 0) {
+        FusedParams fp;
+        fp.logits = logits;
+        fp.teacher = plan->tmode != TM_NONE ? teacher_logits : nullptr;
+        fp.labels = labels;
+        fp.mask = mask;
+        fp.old_logprobs = (f & HL_GRPO) ? old_logprobs : nullptr;
+        fp.advantages = (f & HL_GRPO) ? advantages : nullptr;
+        fp.grad = grad_out;
+        fp.row_rec = row_rec;
+        fp.chunk_rec = chunk_rec;
+        fp.row_counters = counters;
+        fp.ctrl = ctrl;
+        fp.n_rows = n_rows;
+        fp.V = plan->V;
+        fp.chunks = C;
+        fp.accumulate = (f & HL_ACCUMULATE) ? 1 : 0;
+        fp.flags = f;
+        const float log2e = 1.44269504088896340736f;
+        fp.k = plan->logit_scale;
+        fp.K1 = plan->logit_scale * log2e;
+        fp.K2 = log2e / plan->temperature;
+        fp.cap = plan->softcap;
+        fp.kc = plan->softcap > 0.f ? plan->logit_scale / plan->softcap : 0.f;
+        fp.w_ce = plan->w.ce;
+        fp.w_z = plan->w.z;
+        fp.w_d = plan->w.distill;
+        fp.w_g = plan->w.grpo;
+        fp.grad_scale = plan->w.grad_scale;
+        fp.divisor = plan->w.divisor;
+        fp.eps = plan->eps;
+        const dim3 grid((unsigned)(n_rows * C));
+        if (plan->ev_before && hipEventRecord(plan->ev_before, stream) != hipSuccess) return HL_ERR_HIP;
+        if (plan->fused(fp, grid, stream) != hipSuccess) return HL_ERR_HIP;
+        if (plan->ev_after && hipEventRecord(plan->ev_after, stream) != hipSuccess) return HL_ERR_HIP;
+    }
+
+    ReduceParams rp;
+    rp.row_rec = row_rec;
+    rp.labels = labels;
+    rp.old_logprobs = (f & HL_GRPO) ? old_logprobs : nullptr;
+    rp.advantages = (f & HL_GRPO) ? advantages : nullptr;
+    rp.rows = rows;
+    rp.ctrl = ctrl;
+    rp.k = plan->logit_scale;
+    rp.cap = plan->softcap;
+    rp.eps = plan->eps;
+    rp.scalars = scalars_out;
+    rp.n_rows = n_rows;
+    rp.flags = f;
+    rp.w_ce = plan->w.ce;
+    rp.w_z = plan->w.z;
+    rp.w_d = plan->w.distill;
+    rp.w_g = plan->w.grpo;
+    rp.divisor = plan->w.divisor;
+    if (launch_reduce(rp, stream) != hipSuccess) return HL_ERR_HIP;
+    return HL_OK;
+}
+
+const char* hl_status_str(hl_status status) {
+    switch (status) {
+        case HL_OK: return "ok";
+        case HL_ERR_INVALID_ARG: return "invalid argument";
+        case HL_ERR_MISSING_INPUT: return "an enabled loss is missing one of its inputs";
+        case HL_ERR_UNSUPPORTED: return "unsupported request";
+        case HL_ERR_WORKSPACE: return "workspace missing or too small";
+        case HL_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

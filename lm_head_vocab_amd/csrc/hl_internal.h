@@ -1,0 +1,115 @@
+// Internal types shared by the host library and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hl {
+
+// Distillation mode baked into a kernel instance.
+enum TeacherMode : int { TM_NONE = 0, TM_FKL = 1, TM_RKL = 2 };
+
+// Loss bits (same values as the public HL_* flags).
+enum : uint32_t {
+    F_CE = 1u << 0, F_Z = 1u << 1, F_FKL = 1u << 2, F_RKL = 1u << 3,
+    F_GRPO = 1u << 4, F_ENT = 1u << 5, F_ACC = 1u << 16,
+};
+
+// Per-row value columns (same order as the public HL_R_* enum).
+enum RowCol : int {
+    RC_CE = 0, RC_Z, RC_KL, RC_GRPO, RC_LOGP, RC_RATIO, RC_CLIP, RC_K3, RC_ADV,
+    RC_ENT, RC_VALID, RC_PAD, NCOL
+};
+constexpr int NSUM = RC_VALID;        // columns the batch reduction sums
+constexpr int NSCALARS = 13;
+
+// Softmax statistics of a slice of one row, in the log2 domain:
+//   M  = shift, Z = sum 2^(A_j - M), S = sum 2^(A_j - M) (A_j - M)
+//   Mt, Zt = the same for the teacher, SX = the distillation cross sum.
+// The per-row record written by the fused kernel adds the raw label logit
+// and a valid flag.
+enum RecField : int { R_M = 0, R_Z, R_S, R_MT, R_ZT, R_SX, R_XY, R_VALID, REC };
+
+// Control words at the start of the workspace.
+enum Ctrl : int { CTRL_NVALID = 0, CTRL_NBAD = 1, CTRL_CLAIM = 2, CTRL_ERROR = 3, NCTRL = 64 };
+
+struct Geometry {
+    int chunks;      // workgroups per row
+    int block;       // threads per workgroup
+    int nvec;        // 16-byte vectors per thread per tensor
+};
+
+struct FusedParams {
+    const void* logits;
+    const void* teacher;
+    const int64_t* labels;
+    const uint8_t* mask;
+    const float* old_logprobs;
+    const float* advantages;
+    void* grad;
+    float* row_rec;           // [N, REC]
+    float* chunk_rec;         // [N, C, REC]
+    uint32_t* row_counters;   // [N]
+    uint32_t* ctrl;           // [NCTRL]
+    int64_t n_rows;
+    int64_t V;
+    int chunks;
+    int accumulate;
+    uint32_t flags;
+    float k;          // logit scale
+    float K1;         // k * log2(e)
+    float K2;         // log2(e) / temperature
+    float cap;        // softcap c (0 = off)
+    float kc;         // k / c
+    float w_ce, w_z, w_d, w_g;
+    float grad_scale;
+    float divisor;
+    float eps;
+};
+
+struct CountParams {
+    const int64_t* labels;
+    const uint8_t* mask;
+    uint32_t* ctrl;
+    uint32_t* row_counters;   // zeroed when non-null
+    int64_t n_rows;
+    int64_t V;
+};
+
+struct ReduceParams {
+    const float* row_rec;     // [N, REC] from the fused kernel
+    const int64_t* labels;
+    const float* old_logprobs;
+    const float* advantages;
+    const uint32_t* ctrl;
+    float* rows;              // [N, NCOL] per-row values (written)
+    float* scalars;
+    int64_t n_rows;
+    uint32_t flags;
+    float k, cap, eps;
+    float w_ce, w_z, w_d, w_g;
+    float divisor;
+};
+
+typedef hipError_t (*FusedLauncher)(const FusedParams&, dim3 grid, hipStream_t);
+
+// One getter per (dtype, teacher mode) translation unit; nullptr when the
+// requested (block, nvec, softcap) instance does not exist.
+FusedLauncher get_fused_f32_none(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f32_fkl(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f32_rkl(int block, int nvec, bool softcap);
+FusedLauncher get_fused_bf16_none(int block, int nvec, bool softcap);
+FusedLauncher get_fused_bf16_fkl(int block, int nvec, bool softcap);
+FusedLauncher get_fused_bf16_rkl(int block, int nvec, bool softcap);
+
+hipError_t launch_count(const CountParams& p, hipStream_t s);
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
+
+// Vector counts that have a kernel instance, per block size.
+constexpr int kSmallBlock = 256;
+constexpr int kLargeBlock = 1024;
+constexpr int kSmallNvec[] = {1, 2, 4};
+constexpr int kLargeNvecStudent[] = {2, 4, 6, 8, 10, 12, 14, 16, 18, 20};
+constexpr int kLargeNvecTeacher[] = {2, 4, 6, 8, 10};
+
+}  // namespace hl

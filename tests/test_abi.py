@@ -1,0 +1,150 @@
+"""Host-side checks of the C ABI (no GPU needed: nothing here launches work).
+
+The library must load, export every function include/headloss.h declares,
+and reject every invalid argument on the host with the documented status.
+"""
+
+import ctypes
+import math
+
+import pytest
+
+import lm_head_vocab_amd as hl
+from lm_head_vocab_amd._binding import Weights
+
+lib = hl.load_library()
+VP = ctypes.c_void_p
+
+
+def _plan(V=1000, dtype=hl.HL_BF16, flags=hl.CE, w=None, tau=1.0, eps=0.2, scale=1.0, cap=0.0):
+    h = VP()
+    w = w or Weights(1.0, 0.0, 0.0, 0.0, 1.0, 0.0)
+    st = lib.hl_plan(ctypes.byref(h), V, dtype, flags, ctypes.byref(w), tau, eps, scale, cap)
+    return st, h
+
+
+def test_every_declared_symbol_is_exported():
+    names = hl.exported_functions_in_header()
+    assert {"hl_plan", "hl_forward_backward", "hl_plan_destroy", "hl_workspace_bytes",
+            "hl_plan_set_workspace", "hl_status_str"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(6):
+        assert isinstance(hl.status_str(code), str) and hl.status_str(code)
+    assert hl.status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(V=0), hl.HL_ERR_INVALID_ARG),
+    (dict(V=-5), hl.HL_ERR_INVALID_ARG),
+    (dict(dtype=7), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=0), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.ACCUMULATE), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=1 << 9), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.FKL | hl.RKL), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.FKL, tau=0.0), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.RKL, tau=-1.0), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.RKL, tau=math.inf), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.GRPO, eps=0.0), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.GRPO, eps=1.0), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.GRPO, eps=math.nan), hl.HL_ERR_INVALID_ARG),
+    (dict(scale=0.0), hl.HL_ERR_INVALID_ARG),
+    (dict(scale=-1.0), hl.HL_ERR_INVALID_ARG),
+    (dict(scale=math.inf), hl.HL_ERR_INVALID_ARG),
+    (dict(cap=-1.0), hl.HL_ERR_INVALID_ARG),
+    (dict(cap=math.nan), hl.HL_ERR_INVALID_ARG),
+    (dict(w=Weights(math.nan, 0, 0, 0, 1, 0)), hl.HL_ERR_INVALID_ARG),
+    (dict(w=Weights(1, 0, 0, 0, math.inf, 0)), hl.HL_ERR_INVALID_ARG),
+    (dict(V=10**9), hl.HL_ERR_UNSUPPORTED),
+])
+def test_plan_rejects(kwargs, status):
+    st, h = _plan(**kwargs)
+    assert st == status
+    assert not h.value
+
+
+def test_plan_accepts_and_describes_the_baseline_shapes():
+    cases = [  # (V, dtype, flags, expected chunks)
+        (1024, hl.HL_F32, hl.CE | hl.ZLOSS, 1),
+        (128256, hl.HL_BF16, hl.CE | hl.ZLOSS, 1),
+        (151936, hl.HL_BF16, hl.CE | hl.FKL, 2),
+        (151936, hl.HL_BF16, hl.CE | hl.RKL, 2),
+        (151936, hl.HL_BF16, hl.GRPO | hl.ZLOSS | hl.ENTROPY, 1),
+        (256000, hl.HL_BF16, hl.CE | hl.ZLOSS | hl.RKL | hl.GRPO | hl.ENTROPY | hl.ACCUMULATE, 4),
+    ]
+    for V, dt, flags, chunks in cases:
+        st, h = _plan(V=V, dtype=dt, flags=flags, cap=30.0 if V == 256000 else 0.0)
+        assert st == hl.HL_OK, (V, flags)
+        c, b, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        assert lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), ctypes.byref(n)) == 0
+        assert c.value == chunks, (V, flags, c.value)
+        vec = 4 if dt == hl.HL_F32 else 8
+        # every body vector of a chunk has a thread slot
+        assert c.value * b.value * n.value * vec >= V - 2 * vec
+        assert lib.hl_workspace_bytes(h, 1000) > 0
+        assert lib.hl_workspace_bytes(h, -1) == 0
+        lib.hl_plan_destroy(h)
+
+
+def test_set_chunks_and_errors():
+    st, h = _plan(V=20000)
+    assert st == 0
+    assert lib.hl_plan_set_chunks(h, -1) == hl.HL_ERR_INVALID_ARG
+    assert lib.hl_plan_set_chunks(h, 65) == hl.HL_ERR_INVALID_ARG
+    assert lib.hl_plan_set_chunks(h, 3) == hl.HL_OK
+    c = ctypes.c_int()
+    lib.hl_plan_describe(h, ctypes.byref(c), None, None)
+    assert c.value == 3
+    assert lib.hl_plan_set_chunks(h, 0) == hl.HL_OK
+    lib.hl_plan_describe(h, ctypes.byref(c), None, None)
+    assert c.value == 1
+    lib.hl_plan_destroy(h)
+    # a chunk count that leaves a too-long slice is refused and the plan kept
+    st, h = _plan(V=256000, flags=hl.CE | hl.RKL)
+    assert lib.hl_plan_set_chunks(h, 1) == hl.HL_ERR_UNSUPPORTED
+    lib.hl_plan_describe(h, ctypes.byref(c), None, None)
+    assert c.value == 4
+    lib.hl_plan_destroy(h)
+
+
+def test_forward_backward_host_checks_enqueue_nothing():
+    # every case below fails before any HIP call (works without a GPU)
+    st, h = _plan(V=64, flags=hl.CE | hl.GRPO | hl.FKL, w=Weights(1, 0, 1, 1, 1, 0))
+    assert st == 0
+    fake = VP(4096)           # 16-byte aligned stand-in pointer, never dereferenced
+    mis = VP(4098)
+    fb = lib.hl_forward_backward
+    assert fb(None, 4, fake, fake, None, fake, fake, fake, fake, fake, None) == hl.HL_ERR_INVALID_ARG
+    assert fb(h, -1, fake, fake, None, fake, fake, fake, fake, fake, None) == hl.HL_ERR_INVALID_ARG
+    assert fb(h, 4, fake, fake, None, fake, fake, fake, fake, None, None) == hl.HL_ERR_INVALID_ARG
+    assert fb(h, 4, None, fake, None, fake, fake, fake, fake, fake, None) == hl.HL_ERR_INVALID_ARG
+    assert fb(h, 4, fake, None, None, fake, fake, fake, fake, fake, None) == hl.HL_ERR_MISSING_INPUT
+    assert fb(h, 4, fake, fake, None, None, fake, fake, fake, fake, None) == hl.HL_ERR_MISSING_INPUT
+    assert fb(h, 4, fake, fake, None, fake, None, fake, fake, fake, None) == hl.HL_ERR_MISSING_INPUT
+    assert fb(h, 4, fake, fake, None, fake, fake, None, fake, fake, None) == hl.HL_ERR_MISSING_INPUT
+    assert fb(h, 4, mis, fake, None, fake, fake, fake, fake, fake, None) == hl.HL_ERR_INVALID_ARG
+    assert fb(h, 4, fake, fake, None, mis, fake, fake, fake, fake, None) == hl.HL_ERR_INVALID_ARG
+    assert fb(h, 4, fake, fake, None, fake, fake, fake, mis, fake, None) == hl.HL_ERR_INVALID_ARG
+    # a caller workspace that is too small
+    assert lib.hl_plan_set_workspace(h, None, 0) == hl.HL_ERR_INVALID_ARG
+    assert lib.hl_plan_set_workspace(h, VP(4096 + 16), 1 << 20) == hl.HL_ERR_INVALID_ARG
+    assert lib.hl_plan_set_workspace(h, fake, 8) == hl.HL_OK
+    assert fb(h, 4, fake, fake, None, fake, fake, fake, fake, fake, None) == hl.HL_ERR_WORKSPACE
+    lib.hl_plan_destroy(h)
+    lib.hl_plan_destroy(None)
+
+
+def test_binding_marshalling_errors_without_gpu():
+    torch = pytest.importorskip("torch")
+    p = hl.Plan(64, torch.bfloat16, hl.CE)
+    with pytest.raises(ValueError):
+        p(torch.zeros(4, 63, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        p(torch.zeros(4, 64, dtype=torch.bfloat16), labels=torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(hl.HeadLossError):
+        hl.Plan(64, torch.bfloat16, hl.FKL | hl.RKL)
+    with pytest.raises(ValueError):
+        hl.Plan(64, torch.float16, hl.CE)

@@ -1,0 +1,320 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small batches are compared element by element, at sizes that span several
+workgroup tiles and ragged row tails; the full benchmark configurations are
+checked on sampled rows (gradient rows and per-row values against the
+oracle) and by properties that hold at any size (every masked row exactly
+zero, the batch scalars equal the fixed-order mean of the per-row values).
+
+Tolerances: fp32 inputs, scalars 1e-5 relative and gradient 1e-6 absolute;
+bf16 inputs, scalars 1e-4 relative and gradient rms-relative 4e-3 over the
+tensor and over its non-label entries. Slots whose batch mean can sit near
+zero are measured against max(|mean|, mean |per-row value|). A GRPO token
+whose ratio lies within 1e-5 of 1 +/- eps may take either branch (both
+sides decide in floating point); such rows are excluded from the gradient
+and clip-count comparisons.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import lm_head_vocab_amd as hl
+import oracle
+import workloads
+from gpu_support import (TOL, assert_scalars, grad_check, make_plan, oracle_old_logprobs,
+                         run_hip, run_oracle, say, spec_from, to_np, torch_old_logprobs)
+from oracle import SLOT
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+CE, Z, FKL, RKL, GRPO, ENT, ACC = (oracle.CE, oracle.ZLOSS, oracle.FKL, oracle.RKL, oracle.GRPO,
+                                   oracle.ENTROPY, oracle.ACCUMULATE)
+
+COMBOS = {
+    "ce": (CE, dict(ce=1.0)),
+    "ce_z": (CE | Z, dict(ce=1.0, z=0.1)),
+    "z_ent": (Z | ENT, dict(ce=0.0, z=1.0)),
+    "grpo_z_ent": (GRPO | Z | ENT, dict(ce=0.0, z=0.01, grpo=1.0)),
+    "ce_fkl": (CE | FKL, dict(ce=0.5, distill=1.0)),
+    "ce_rkl": (CE | RKL, dict(ce=0.5, distill=1.0)),
+    "fkl_ent": (FKL | ENT, dict(ce=0.0, distill=1.0)),
+    "all_rkl": (CE | Z | RKL | GRPO | ENT, dict(ce=1.0, z=1e-3, distill=0.5, grpo=1.0, grad_scale=0.25)),
+    "all_fkl": (CE | Z | FKL | GRPO | ENT, dict(ce=0.7, z=1e-2, distill=0.9, grpo=0.6, grad_scale=2.0)),
+}
+# (N, V): aligned and ragged rows, tiny rows, both block sizes
+SHAPES = [(37, 1000), (16, 4099), (9, 33000), (5, 3), (3, 1), (64, 300), (11, 2053)]
+
+
+def _grpo_boundary_rows(spec, inp_cpu, eps_tol=1e-5):
+    if not spec.has(GRPO):
+        return np.zeros(inp_cpu["logits"].shape[0], dtype=bool)
+    vals = oracle.row_values(spec, to_np(inp_cpu["logits"]), to_np(inp_cpu["labels"]).astype(np.int64),
+                             None, to_np(inp_cpu["old_logprobs"]), to_np(inp_cpu["advantages"]))
+    r = vals["ratio"]
+    return (np.abs(r - (1 + spec.eps)) < eps_tol) | (np.abs(r - (1 - spec.eps)) < eps_tol)
+
+
+def _small(dtype, combo, N, V, seed, softcap=0.0, scale=1.0, accumulate=False, temperature=1.5,
+           logit_std=2.0, **gen):
+    flags, w = COMBOS[combo]
+    if accumulate:
+        flags |= ACC
+    spec = spec_from(V, flags, w, temperature=temperature, eps=0.2, logit_scale=scale, softcap=softcap)
+    inp = workloads.small_inputs(N, V, dtype, "cpu", seed, teacher=bool(flags & (FKL | RKL)),
+                                 grpo=bool(flags & GRPO), accumulate=accumulate,
+                                 logit_std=logit_std, **gen)
+    if flags & GRPO:
+        inp["old_logprobs"] = oracle_old_logprobs(spec, inp["logits"], inp["labels"], inp["old_noise"])
+    return spec, inp
+
+
+def _to_dev(inp):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def _check_small(spec, inp, dtype, chunks=0, grad_mode=None):
+    grad_mode = grad_mode or ("accumulate" if spec.has(ACC) else "overwrite")
+    plan = make_plan(spec, TDT[dtype], chunks)
+    say(f"[gpu] N={inp['logits'].shape[0]} V={spec.V} {dtype} flags={spec.flags:#x} "
+        f"chunks={plan.describe()} grad={grad_mode}")
+    sc, g = run_hip(plan, _to_dev(inp), grad_mode)
+    ref_sc, ref_g, _ = run_oracle(spec, inp, want_grad=grad_mode != "none")
+    vals = oracle.row_values(spec, to_np(inp["logits"]),
+                             to_np(inp["labels"]).astype(np.int64) if inp["labels"] is not None else None,
+                             to_np(inp["teacher"]), to_np(inp.get("old_logprobs")), to_np(inp.get("advantages")))
+    valid, _ = oracle.row_validity(spec.V and inp["logits"].shape[0], spec.V,
+                                   to_np(inp["labels"]).astype(np.int64) if inp["labels"] is not None else None,
+                                   to_np(inp["mask"]))
+    boundary = _grpo_boundary_rows(spec, inp) & valid
+    assert_scalars(spec, sc, ref_sc, dtype, vals, valid, skip=("CLIPFRAC",) if boundary.any() else ())
+    if spec.has(GRPO) and not boundary.any():
+        n = ref_sc[SLOT["N_VALID"]] if spec.divisor <= 0 else spec.divisor
+        assert round(sc[SLOT["CLIPFRAC"]] * n) == round(ref_sc[SLOT["CLIPFRAC"]] * n)
+    if grad_mode == "none":
+        return plan, sc, None
+    gk = g.detach().cpu()
+    keep = ~boundary
+    metrics = grad_check(gk[torch.from_numpy(keep)], ref_g[keep], dtype,
+                         labels=to_np(inp["labels"])[keep] if inp["labels"] is not None else None)
+    # masked rows: +0.0 in overwrite mode, bit-identical existing values in accumulate mode
+    inval = torch.from_numpy(~valid)
+    if grad_mode == "overwrite":
+        assert torch.equal(gk[inval].view(torch.int16 if dtype == "bf16" else torch.int32),
+                           torch.zeros_like(gk[inval]).view(torch.int16 if dtype == "bf16" else torch.int32))
+    else:
+        assert torch.equal(gk[inval], inp["grad_init"][inval])
+    return plan, sc, metrics
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{n}x{v}" for n, v in SHAPES])
+@pytest.mark.parametrize("combo", list(COMBOS))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_parity(dtype, combo, shape):
+    N, V = shape
+    spec, inp = _small(dtype, combo, N, V, seed=11 * N + V, bad_labels=1 if N > 4 else 0,
+                       mask_frac=0.15 if N > 8 else 0.0)
+    _check_small(spec, inp, dtype)
+
+
+@pytest.mark.parametrize("logit_std", [2.0, 40.0], ids=["poly", "exp_branch"])
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "grpo_z_ent"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_softcap_and_scale(dtype, combo, logit_std):
+    spec, inp = _small(dtype, combo, 24, 2053, seed=7, softcap=7.0, scale=0.5, logit_std=logit_std)
+    _check_small(spec, inp, dtype)
+
+
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "z_ent"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1000, 20011])
+def test_accumulate(dtype, combo, V):
+    spec, inp = _small(dtype, combo, 19, V, seed=3, accumulate=True, mask_frac=0.2, softcap=30.0, scale=0.5)
+    _check_small(spec, inp, dtype)
+
+
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "grpo_z_ent"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_only_matches_and_writes_nothing(dtype, combo):
+    spec, inp = _small(dtype, combo, 21, 3001, seed=5)
+    _, sc_fo, _ = _check_small(spec, inp, dtype, grad_mode="none")
+    plan = make_plan(spec, TDT[dtype])
+    sc_full, _ = run_hip(plan, _to_dev(inp), "overwrite")
+    np.testing.assert_array_equal(sc_fo, sc_full)
+
+
+@pytest.mark.parametrize("chunks", [2, 3, 5])
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "ce_fkl"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_vocab_variant(dtype, combo, chunks):
+    # forced chunking exercises the cross-workgroup combine at small sizes
+    for V, N in ((20011, 7), (70000, 5)):
+        spec, inp = _small(dtype, combo, N, V, seed=chunks * 100 + N, softcap=15.0, scale=0.8)
+        _check_small(spec, inp, dtype, chunks=chunks)
+
+
+def test_split_vocab_accumulate_and_masking():
+    spec, inp = _small("bf16", "all_rkl", 12, 50003, seed=9, accumulate=True, mask_frac=0.3, bad_labels=2)
+    _check_small(spec, inp, "bf16", chunks=4)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_edge_cases(dtype):
+    dt = TDT[dtype]
+    # empty batch: every slot 0
+    spec = spec_from(100, CE | Z | ENT, dict(ce=1.0, z=0.1))
+    plan = make_plan(spec, dt)
+    say(f"[gpu] empty batch {dtype}")
+    sc = plan(torch.empty(0, 100, dtype=dt, device=DEV), labels=torch.empty(0, dtype=torch.int64, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.all(sc.cpu() == 0)
+    # every row masked: zeros, zero gradient
+    spec, inp = _small(dtype, "all_rkl", 6, 777, seed=1, ignore_frac=1.0)
+    _check_small(spec, inp, dtype)
+    # single row, V = 1 (softmax is exactly 1)
+    spec, inp = _small(dtype, "ce_z", 1, 1, seed=2, ignore_frac=0.0)
+    _check_small(spec, inp, dtype)
+    # bad labels are counted and masked
+    spec, inp = _small(dtype, "ce", 30, 500, seed=3, bad_labels=5)
+    plan, sc, _ = _check_small(spec, inp, dtype)
+    assert sc[SLOT["N_BADLABEL"]] == 5
+    # a caller divisor replaces the valid-row count
+    spec, inp = _small(dtype, "all_fkl", 10, 999, seed=4)
+    spec.divisor = 123.0
+    _check_small(spec, inp, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_weight_keeps_scalars_and_drops_gradient_term(dtype):
+    spec, inp = _small(dtype, "all_rkl", 17, 1500, seed=21)
+    spec0 = spec_from(spec.V, spec.flags, dict(ce=1.0, z=1e-3, distill=0.5, grpo=0.0, grad_scale=0.25),
+                      temperature=spec.temperature)
+    plan_full, sc_full, _ = _check_small(spec, inp, dtype)
+    plan0, sc0, _ = _check_small(spec0, inp, dtype)
+    for name in ("GRPO", "NEWLOGP", "RATIO", "CLIPFRAC", "KL_OLD_NEW", "ADV_MEAN"):
+        assert sc0[SLOT[name]] == sc_full[SLOT[name]], name
+
+
+def test_bitwise_determinism():
+    for chunks, combo in ((0, "grpo_z_ent"), (3, "all_rkl")):
+        spec, inp = _small("bf16", combo, 33, 40000, seed=8, accumulate=True, softcap=20.0)
+        plan = make_plan(spec, torch.bfloat16, chunks)
+        d = _to_dev(inp)
+        say(f"[gpu] determinism chunks={chunks} {combo}")
+        sc1, g1 = run_hip(plan, d, "accumulate")
+        sc2, g2 = run_hip(plan, d, "accumulate")
+        np.testing.assert_array_equal(sc1, sc2)
+        assert torch.equal(g1.view(torch.int16), g2.view(torch.int16))
+        rv1 = plan.row_values().clone()
+        run_hip(plan, d, "accumulate")
+        assert torch.equal(rv1, plan.row_values())
+
+
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl"])
+def test_fused_equals_separate_passes(combo):
+    """The per-loss loop (one single-loss plan per loss, accumulating into one
+    fp32 buffer) equals the fused pass up to rounding (fp32 inputs)."""
+    spec, inp = _small("f32", combo, 29, 3333, seed=12)
+    d = _to_dev(inp)
+    fused = make_plan(spec, torch.float32)
+    sc_f, g_f = run_hip(fused, d, "overwrite")
+    weights = {CE: ("ce", spec.w_ce), Z: ("z", spec.w_z), FKL: ("distill", spec.w_distill),
+               RKL: ("distill", spec.w_distill), GRPO: ("grpo", spec.w_grpo)}
+    g = torch.zeros_like(d["logits"])
+    first = True
+    for flag, (key, wv) in weights.items():
+        if not spec.has(flag):
+            continue
+        w = dict(ce=0.0, grad_scale=spec.grad_scale)
+        w[key] = wv
+        single = spec_from(spec.V, flag | (0 if first else ACC), w, temperature=spec.temperature)
+        p = make_plan(single, torch.float32)
+        p(d["logits"], labels=d["labels"], mask=d["mask"], teacher=d["teacher"],
+          old_logprobs=d.get("old_logprobs"), advantages=d.get("advantages"), grad=g)
+        first = False
+    torch.cuda.synchronize()
+    assert (g - g_f).abs().max().item() <= 1e-6
+
+
+# ---------------------------------------------------------------------------
+# The benchmark configurations at full size
+# ---------------------------------------------------------------------------
+FULL = ["ce_z_tiny_f32", "ce_z_bf16", "ce_fkl_bf16", "ce_rkl_bf16", "grpo_z_ent_bf16", "all_combined_bf16"]
+
+
+def _full_inputs(name):
+    w = workloads.WORKLOADS[name]
+    say(f"[gpu] generate {name} N={w.N} V={w.V} seed={workloads.seed_for(name)}")
+    inp = workloads.generate(w, DEV)
+    spec = spec_from(w.V, w.flags, dict(ce=w.weights.get("ce", 1.0), **{k: v for k, v in w.weights.items() if k != "ce"}),
+                     temperature=w.temperature, eps=w.eps, logit_scale=w.logit_scale, softcap=w.softcap)
+    if w.flags & GRPO:
+        inp["old_logprobs"] = torch_old_logprobs(spec, inp["logits"], inp["labels"], inp["old_noise"])
+    return w, spec, inp
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_config_sampled(name):
+    w, spec, inp = _full_inputs(name)
+    plan = make_plan(spec, w.torch_dtype)
+    grad_mode = "accumulate" if w.flags & ACC else "overwrite"
+    say(f"[gpu] run {name} plan={plan.describe()} grad={grad_mode}")
+    sc, g = run_hip(plan, inp, grad_mode)
+    rows_val = plan.row_values().cpu().double().numpy()
+    N = w.N
+    labels = to_np(inp["labels"]).astype(np.int64)
+    mask = to_np(inp["mask"]) if inp["mask"] is not None else None
+    valid, bad = oracle.row_validity(N, w.V, labels, mask)
+    n_valid = int(valid.sum())
+    assert sc[SLOT["N_VALID"]] == n_valid and sc[SLOT["N_BADLABEL"]] == int(bad.sum())
+    # property at any size: every masked row is +0.0 (or untouched)
+    inval = torch.from_numpy(~valid).to(DEV)
+    if grad_mode == "overwrite" and inval.any():
+        assert torch.count_nonzero(g[inval].view(torch.int16 if w.dtype == "bf16" else torch.int32)).item() == 0
+    elif inval.any():
+        assert torch.equal(g[inval], inp["grad_init"][inval])
+    # property: scalars are the fixed-order means of the per-row values
+    n = spec.divisor if spec.divisor > 0 else n_valid
+    cols = {"CE": 0, "Z": 1, "DISTILL": 2, "GRPO": 3, "NEWLOGP": 4, "RATIO": 5, "CLIPFRAC": 6,
+            "KL_OLD_NEW": 7, "ADV_MEAN": 8, "ENTROPY": 9}
+    enabled = {"CE": CE, "Z": Z, "DISTILL": FKL | RKL, "GRPO": GRPO, "NEWLOGP": GRPO, "RATIO": GRPO,
+               "CLIPFRAC": GRPO, "KL_OLD_NEW": GRPO, "ADV_MEAN": GRPO, "ENTROPY": ENT}
+    for sname, c in cols.items():
+        expect = rows_val[:, c].sum() / n if (spec.flags & enabled[sname]) else 0.0
+        assert abs(sc[SLOT[sname]] - expect) <= 2e-6 * max(1.0, abs(expect)), (sname, sc[SLOT[sname]], expect)
+    # sampled rows against the oracle: first, last, spread, and random rows
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, N - 1], np.linspace(0, N - 1, 24).astype(int),
+                                     rng.integers(0, N, 24)]))
+    sub = {k: (v[torch.from_numpy(rows).to(DEV)].cpu() if isinstance(v, torch.Tensor) else v)
+           for k, v in inp.items()}
+    _, ref_g, (vals, v_ok, _) = run_oracle(spec, sub, rows=slice(None), n=float(n))
+    say(f"[gpu] oracle checked {len(rows)} sampled rows of {name}")
+    boundary = np.zeros(len(rows), dtype=bool)
+    if spec.has(GRPO):
+        r = vals["ratio"]
+        boundary = (np.abs(r - (1 + spec.eps)) < 1e-5) | (np.abs(r - (1 - spec.eps)) < 1e-5)
+    keep = v_ok & ~boundary
+    # per-row values of the valid sampled rows
+    rv = rows_val[rows]
+    tol = TOL[w.dtype]["scalar_rel"]
+    checks = [("ce", 0, CE), ("z", 1, Z), ("entropy", 9, ENT), ("logp", 4, GRPO), ("ratio", 5, GRPO),
+              ("grpo", 3, GRPO), ("k3", 7, GRPO)]
+    if spec.has(FKL):
+        checks.append(("fkl", 2, FKL))
+    if spec.has(RKL):
+        checks.append(("rkl", 2, RKL))
+    for key, c, flag in checks:
+        if not spec.has(flag):
+            continue
+        ref = vals[key][keep]
+        got = rv[keep, c]
+        scale = max(np.max(np.abs(ref)), 1e-3) if key in ("grpo", "k3", "fkl", "rkl", "logp") else np.abs(ref)
+        err = np.max(np.abs(got - ref) / np.maximum(scale, 1e-30)) if ref.size else 0.0
+        assert err <= tol, (key, err)
+    if spec.has(GRPO):
+        assert np.array_equal(rv[keep, 6] != 0, vals["clipped"][keep])
+    gk = g[torch.from_numpy(rows).to(DEV)].cpu()
+    grad_check(gk[torch.from_numpy(keep)], ref_g[keep], w.dtype, labels=labels[rows][keep])
