@@ -203,6 +203,10 @@ hl_status hl_plan_describe(hl_plan_t plan, int* chunks, int* block, int* vec_per
  * profiler can time the dominant kernel alone. */
 hl_status hl_plan_set_timing_events(hl_plan_t plan, hipEvent_t before, hipEvent_t after);
 
+/* Text of the last HIP failure seen by this thread (which call, the HIP
+ * error string and code), or "" if none. Valid until the next failing call. */
+const char* hl_last_error(void);
+
 /* Static text for a status code. */
 const char* hl_status_str(hl_status status);
 

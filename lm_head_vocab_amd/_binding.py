@@ -51,7 +51,10 @@ class Weights(ctypes.Structure):
 class HeadLossError(RuntimeError):
     def __init__(self, where: str, status: int):
         self.status = status
-        super().__init__(f"{where}: {status_str(status)} (status {status})")
+        detail = ""
+        if status == HL_ERR_HIP:
+            detail = " - " + load_library().hl_last_error().decode()
+        super().__init__(f"{where}: {status_str(status)} (status {status}){detail}")
 
 
 _lib = None
@@ -75,6 +78,11 @@ def load_library(path: str | None = None):
         raise RuntimeError(
             f"{path} is not built; run `python -m lm_head_vocab_amd.build` "
             "(there is no CPU fallback)")
+    # One HIP runtime per process: PyTorch ships its own libamdhip64.so.7.
+    # Loading torch first makes the library's libamdhip64.so.7 dependency
+    # resolve to that already-loaded runtime instead of a second copy (two
+    # runtimes in one process cannot both open the device).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, i64, u32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
     lib.hl_plan.argtypes = [ctypes.POINTER(vp), i64, ctypes.c_int, u32,
@@ -97,6 +105,8 @@ def load_library(path: str | None = None):
     lib.hl_plan_describe.restype = ctypes.c_int
     lib.hl_plan_set_timing_events.argtypes = [vp, vp, vp]
     lib.hl_plan_set_timing_events.restype = ctypes.c_int
+    lib.hl_last_error.argtypes = []
+    lib.hl_last_error.restype = ctypes.c_char_p
     lib.hl_status_str.argtypes = [ctypes.c_int]
     lib.hl_status_str.restype = ctypes.c_char_p
     _lib = lib

@@ -145,11 +145,13 @@ __global__ __launch_bounds__(1024) void reduce_kernel(const ReduceParams p) {
 }
 
 hipError_t launch_count(const CountParams& p, hipStream_t s) {
+    (void)hipGetLastError();   // drop an error left by an earlier, unrelated call
     hipLaunchKernelGGL(count_kernel, dim3(1), dim3(1024), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
+    (void)hipGetLastError();
     hipLaunchKernelGGL(reduce_kernel, dim3(1), dim3(1024), 0, s, p);
     return hipGetLastError();
 }

@@ -575,6 +575,7 @@ __global__ __launch_bounds__(BLOCK) void fused_kernel(const FusedParams p) {
 
 template <typename T, int BLOCK, int NVEC, int TMODE, bool SOFTCAP>
 hipError_t launch_fused(const FusedParams& p, dim3 grid, hipStream_t s) {
+    (void)hipGetLastError();   // drop an error left by an earlier, unrelated call
     hipLaunchKernelGGL((fused_kernel<T, BLOCK, NVEC, TMODE, SOFTCAP>), grid, dim3(BLOCK), 0, s, p);
     return hipGetLastError();
 }

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 #include <new>
 
@@ -33,6 +34,13 @@ struct hl_plan_s {
 };
 
 namespace {
+
+thread_local char g_last_error[256] = "";
+
+hl_status hip_fail(const char* where, hipError_t e) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+    return HL_ERR_HIP;
+}
 
 constexpr uint32_t kLossBits = HL_CE | HL_ZLOSS | HL_FKL | HL_RKL | HL_GRPO | HL_ENTROPY;
 constexpr uint32_t kKnownBits = kLossBits | HL_ACCUMULATE;
@@ -241,7 +249,8 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
             plan->ws_bytes = 0;
         }
         void* mem = nullptr;
-        if (hipMalloc(&mem, L.total) != hipSuccess) return HL_ERR_HIP;
+        const hipError_t me = hipMalloc(&mem, L.total);
+        if (me != hipSuccess) return hip_fail("hipMalloc(workspace)", me);
         plan->ws = mem;
         plan->ws_bytes = L.total;
         plan->ws_owned = true;
@@ -262,7 +271,8 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
     cp.row_counters = C > 1 ? counters : nullptr;
     cp.n_rows = n_rows;
     cp.V = plan->V;
-    if (launch_count(cp, stream) != hipSuccess) return HL_ERR_HIP;
+    hipError_t e = launch_count(cp, stream);
+    if (e != hipSuccess) return hip_fail("count kernel launch", e);
 
     if (n_rows > 0) {
         FusedParams fp;
@@ -296,9 +306,12 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
         fp.divisor = plan->w.divisor;
         fp.eps = plan->eps;
         const dim3 grid((unsigned)(n_rows * C));
-        if (plan->ev_before && hipEventRecord(plan->ev_before, stream) != hipSuccess) return HL_ERR_HIP;
-        if (plan->fused(fp, grid, stream) != hipSuccess) return HL_ERR_HIP;
-        if (plan->ev_after && hipEventRecord(plan->ev_after, stream) != hipSuccess) return HL_ERR_HIP;
+        if (plan->ev_before && (e = hipEventRecord(plan->ev_before, stream)) != hipSuccess)
+            return hip_fail("hipEventRecord(before)", e);
+        e = plan->fused(fp, grid, stream);
+        if (e != hipSuccess) return hip_fail("fused kernel launch", e);
+        if (plan->ev_after && (e = hipEventRecord(plan->ev_after, stream)) != hipSuccess)
+            return hip_fail("hipEventRecord(after)", e);
     }
 
     ReduceParams rp;
@@ -319,9 +332,12 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
     rp.w_d = plan->w.distill;
     rp.w_g = plan->w.grpo;
     rp.divisor = plan->w.divisor;
-    if (launch_reduce(rp, stream) != hipSuccess) return HL_ERR_HIP;
+    e = launch_reduce(rp, stream);
+    if (e != hipSuccess) return hip_fail("reduce kernel launch", e);
     return HL_OK;
 }
+
+const char* hl_last_error(void) { return g_last_error; }
 
 const char* hl_status_str(hl_status status) {
     switch (status) {
