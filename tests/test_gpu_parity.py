@@ -8,8 +8,9 @@ zero, the batch scalars equal the fixed-order mean of the per-row values).
 
 Tolerances: fp32 inputs, scalars 1e-5 relative and gradient 1e-6 absolute;
 bf16 inputs, scalars 1e-4 relative and gradient rms-relative 4e-3 over the
-tensor and over its non-label entries. Slots whose batch mean can sit near
-zero are measured against max(|mean|, mean |per-row value|). A GRPO token
+tensor and over its non-label entries. Slots whose batch mean can sit at or
+near zero (distillation KL, GRPO objective and statistics, the total) are
+measured against max(|mean|, mean |per-row value|, 1e-2). A GRPO token
 whose ratio lies within 1e-5 of 1 +/- eps may take either branch (both
 sides decide in floating point); such rows are excluded from the gradient
 and clip-count comparisons.
@@ -85,7 +86,7 @@ def _check_small(spec, inp, dtype, chunks=0, grad_mode=None):
     vals = oracle.row_values(spec, to_np(inp["logits"]),
                              to_np(inp["labels"]).astype(np.int64) if inp["labels"] is not None else None,
                              to_np(inp["teacher"]), to_np(inp.get("old_logprobs")), to_np(inp.get("advantages")))
-    valid, _ = oracle.row_validity(spec.V and inp["logits"].shape[0], spec.V,
+    valid, _ = oracle.row_validity(inp["logits"].shape[0], spec.V,
                                    to_np(inp["labels"]).astype(np.int64) if inp["labels"] is not None else None,
                                    to_np(inp["mask"]))
     boundary = _grpo_boundary_rows(spec, inp) & valid
