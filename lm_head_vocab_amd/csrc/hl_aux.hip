@@ -9,6 +9,7 @@ namespace hl {
 __global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
     __shared__ uint32_t s_v[16], s_b[16];
     uint32_t nv = 0, nb = 0;
+#pragma unroll 8
     for (int64_t r = threadIdx.x; r < p.n_rows; r += 1024) {
         bool valid, bad;
         int64_t y;
@@ -31,27 +32,32 @@ __global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
         p.ctrl[CTRL_NBAD] = tb;
         p.ctrl[CTRL_CLAIM] = 0u;
         p.ctrl[CTRL_ERROR] = 0u;
+        p.ctrl[CTRL_DONE] = 0u;
     }
 }
 
 // ---------------------------------------------------------------------------
-// reduce_kernel: one workgroup of 1024 threads. Turns each row's softmax
-// record into the reported per-row values in fp64 (lse = M + log2 Z in the
-// log2 domain, entropy, KL, CE, new log-prob, GRPO objective and statistics),
-// stores them for hl_row_values, and sums them in a fixed order.
+// reduce_kernel: one row per thread, kReduceBlock rows per workgroup. Turns
+// each row's softmax record into the reported per-row values in fp64 (lse =
+// M + log2 Z in the log2 domain, entropy, KL, CE, new log-prob, GRPO
+// objective and statistics), stores them for hl_row_values, and sums them:
+// a fixed butterfly inside each wave, the waves in order, then the last
+// workgroup to finish adds the workgroup sums in workgroup order. Every step
+// has a fixed order, so the scalars are identical run to run.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void reduce_kernel(const ReduceParams p) {
+__global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams p) {
     constexpr double LN2 = 0.69314718055994530942;
-    __shared__ double s_acc[16][NSUM];
-    double acc[NSUM];
-#pragma unroll
-    for (int c = 0; c < NSUM; ++c) acc[c] = 0.0;
+    constexpr int NWR = kReduceBlock / 64;
+    __shared__ double s_acc[NWR][NSUM];
+    __shared__ double s_sum[NSUM];
+    __shared__ uint32_t s_last;
     const uint32_t f = p.flags;
-    for (int64_t r = threadIdx.x; r < p.n_rows; r += 1024) {
-        const float* rec = p.row_rec + r * REC;
-        double v[NCOL];
+    const int64_t r = (int64_t)blockIdx.x * kReduceBlock + threadIdx.x;
+    double v[NCOL];
 #pragma unroll
-        for (int c = 0; c < NCOL; ++c) v[c] = 0.0;
+    for (int c = 0; c < NCOL; ++c) v[c] = 0.0;
+    if (r < p.n_rows) {
+        const float* rec = p.row_rec + r * REC;
         if (rec[R_VALID] != 0.f) {
             const double Z = rec[R_Z];
             const double l2Z = log2(Z);
@@ -89,29 +95,42 @@ __global__ __launch_bounds__(1024) void reduce_kernel(const ReduceParams p) {
         float* out = p.rows + r * NCOL;
 #pragma unroll
         for (int c = 0; c < NCOL; ++c) out[c] = (float)v[c];
-#pragma unroll
-        for (int c = 0; c < NSUM; ++c) acc[c] += v[c];
-    }
-    // fixed butterfly within the wave, then waves in order
-#pragma unroll
-    for (int c = 0; c < NSUM; ++c) {
-        double x = acc[c];
-        for (int m = 1; m < 64; m <<= 1) x = __dadd_rn(x, __shfl_xor(x, m, 64));
-        acc[c] = x;
     }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (lane == 0) {
 #pragma unroll
-        for (int c = 0; c < NSUM; ++c) s_acc[wave][c] = acc[c];
+    for (int c = 0; c < NSUM; ++c) {
+        double x = v[c];
+        for (int m = 1; m < 64; m <<= 1) x = __dadd_rn(x, __shfl_xor(x, m, 64));
+        if (lane == 0) s_acc[wave][c] = x;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double* mine = p.partials + (int64_t)blockIdx.x * NSUM;
+        for (int c = 0; c < NSUM; ++c) {
+            double x = 0.0;
+            for (int w = 0; w < NWR; ++w) x += s_acc[w][c];
+            mine[c] = x;
+        }
+        __threadfence();
+        const uint32_t done = atomicAdd(&p.ctrl[CTRL_DONE], 1u);
+        s_last = (done == gridDim.x - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (s_last == 0u) return;
+    __threadfence();
+    if (threadIdx.x < NSUM) {
+        const int c = threadIdx.x;
+        double x = 0.0;
+        for (uint32_t g = 0; g < gridDim.x; ++g) {
+            const uint64_t bits = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p.partials + (int64_t)g * NSUM + c),
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            x += __longlong_as_double((long long)bits);
+        }
+        s_sum[c] = x;
     }
     __syncthreads();
     if (threadIdx.x != 0) return;
-    double sum[NSUM];
-    for (int c = 0; c < NSUM; ++c) {
-        double x = 0.0;
-        for (int w = 0; w < 16; ++w) x += s_acc[w][c];
-        sum[c] = x;
-    }
+    const double* sum = s_sum;
     const uint32_t n_valid = p.ctrl[CTRL_NVALID];
     const double n = p.divisor > 0.f ? (double)p.divisor : (double)n_valid;
     float out[NSCALARS];
@@ -152,7 +171,8 @@ hipError_t launch_count(const CountParams& p, hipStream_t s) {
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL(reduce_kernel, dim3(1), dim3(1024), 0, s, p);
+    const int64_t groups = p.n_rows > 0 ? (p.n_rows + kReduceBlock - 1) / kReduceBlock : 1;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)groups), dim3(kReduceBlock), 0, s, p);
     return hipGetLastError();
 }
 

@@ -49,7 +49,7 @@ constexpr int kMaxChunks = 64;
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-    size_t ctrl, counters, chunk_rec, row_rec, rows, total;
+    size_t ctrl, counters, chunk_rec, row_rec, rows, partials, total;
 };
 
 Layout layout_for(const hl_plan_s* p, int64_t n) {
@@ -61,7 +61,9 @@ Layout layout_for(const hl_plan_s* p, int64_t n) {
     const size_t rec_bytes = p->geo.chunks > 1 ? N * p->geo.chunks * REC * sizeof(float) : 0;
     L.row_rec = L.chunk_rec + align256(rec_bytes);
     L.rows = L.row_rec + align256(N * REC * sizeof(float));
-    L.total = L.rows + align256(N * NCOL * sizeof(float));
+    L.partials = L.rows + align256(N * NCOL * sizeof(float));
+    const size_t groups = N > 0 ? (N + kReduceBlock - 1) / kReduceBlock : 1;
+    L.total = L.partials + align256(groups * NSUM * sizeof(double));
     return L;
 }
 
@@ -316,6 +318,7 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
 
     ReduceParams rp;
     rp.row_rec = row_rec;
+    rp.partials = reinterpret_cast<double*>(ws + L.partials);
     rp.labels = labels;
     rp.old_logprobs = (f & HL_GRPO) ? old_logprobs : nullptr;
     rp.advantages = (f & HL_GRPO) ? advantages : nullptr;

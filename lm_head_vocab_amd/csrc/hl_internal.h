@@ -31,7 +31,7 @@ constexpr int NSCALARS = 13;
 enum RecField : int { R_M = 0, R_Z, R_S, R_MT, R_ZT, R_SX, R_XY, R_VALID, REC };
 
 // Control words at the start of the workspace.
-enum Ctrl : int { CTRL_NVALID = 0, CTRL_NBAD = 1, CTRL_CLAIM = 2, CTRL_ERROR = 3, NCTRL = 64 };
+enum Ctrl : int { CTRL_NVALID = 0, CTRL_NBAD = 1, CTRL_CLAIM = 2, CTRL_ERROR = 3, CTRL_DONE = 4, NCTRL = 64 };
 
 struct Geometry {
     int chunks;      // workgroups per row
@@ -76,12 +76,15 @@ struct CountParams {
     int64_t V;
 };
 
+constexpr int kReduceBlock = 256;   // rows per reduction workgroup
+
 struct ReduceParams {
     const float* row_rec;     // [N, REC] from the fused kernel
+    double* partials;         // [G, NSUM] per-workgroup sums
     const int64_t* labels;
     const float* old_logprobs;
     const float* advantages;
-    const uint32_t* ctrl;
+    uint32_t* ctrl;
     float* rows;              // [N, NCOL] per-row values (written)
     float* scalars;
     int64_t n_rows;
