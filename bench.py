@@ -139,6 +139,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-separate", action="store_true")
     ap.add_argument("--chunks", type=int, default=0, help="force the split-vocab chunk count")
+    ap.add_argument("--block", type=int, default=0, help="force the threads per workgroup (with --chunks)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -180,7 +181,9 @@ def main(argv=None):
     n_valid = int(valid.sum().item())
     acc = bool(w.flags & workloads.ACCUMULATE)
     grad = inp["grad_init"].clone() if acc else torch.empty_like(inp["logits"])
-    plan = hl.Plan(w.V, w.torch_dtype, w.flags, chunks=args.chunks, **plan_kwargs(w))
+    plan = hl.Plan(w.V, w.torch_dtype, w.flags, **plan_kwargs(w))
+    if args.chunks or args.block:
+        plan.set_variant(args.chunks, args.block)
     geo = plan.describe()
     log(f"plan {geo}")
 

@@ -194,6 +194,12 @@ const float* hl_row_values(hl_plan_t plan);
  * fits V with that many chunks). */
 hl_status hl_plan_set_chunks(hl_plan_t plan, int chunks);
 
+/* Tuning form of hl_plan_set_chunks that also fixes the threads per
+ * workgroup (256, 512 or 1024; 0 = automatic, which requires chunks = 0 too
+ * or picks the smallest block that fits). Same errors as hl_plan_set_chunks,
+ * plus HL_ERR_INVALID_ARG for another block size or a block without chunks. */
+hl_status hl_plan_set_variant(hl_plan_t plan, int chunks, int block);
+
 /* Describe the chosen variant: chunks per row, threads per workgroup, 16-byte
  * vectors held per thread per tensor. Any pointer may be NULL. */
 hl_status hl_plan_describe(hl_plan_t plan, int* chunks, int* block, int* vec_per_thread);

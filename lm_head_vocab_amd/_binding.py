@@ -100,6 +100,8 @@ def load_library(path: str | None = None):
     lib.hl_row_values.restype = vp
     lib.hl_plan_set_chunks.argtypes = [vp, ctypes.c_int]
     lib.hl_plan_set_chunks.restype = ctypes.c_int
+    lib.hl_plan_set_variant.argtypes = [vp, ctypes.c_int, ctypes.c_int]
+    lib.hl_plan_set_variant.restype = ctypes.c_int
     lib.hl_plan_describe.argtypes = [vp, ctypes.POINTER(ctypes.c_int),
                                      ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     lib.hl_plan_describe.restype = ctypes.c_int
@@ -168,6 +170,10 @@ class Plan:
     def set_chunks(self, chunks: int):
         _check("hl_plan_set_chunks", self._lib.hl_plan_set_chunks(self._h, int(chunks)))
         self._ws = None   # layout depends on the chunk count
+
+    def set_variant(self, chunks: int, block: int = 0):
+        _check("hl_plan_set_variant", self._lib.hl_plan_set_variant(self._h, int(chunks), int(block)))
+        self._ws = None
 
     def describe(self) -> dict:
         c, b, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()

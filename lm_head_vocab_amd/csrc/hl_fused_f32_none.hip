@@ -17,6 +17,10 @@ FusedLauncher get_fused_f32_none(int block, int nvec, bool softcap) {
     HL_FUSED_CASE(hl::F32T, 1024, 16, hl::TM_NONE)
     HL_FUSED_CASE(hl::F32T, 1024, 18, hl::TM_NONE)
     HL_FUSED_CASE(hl::F32T, 1024, 20, hl::TM_NONE)
+    HL_FUSED_CASE(hl::F32T, 512, 10, hl::TM_NONE)
+    HL_FUSED_CASE(hl::F32T, 512, 12, hl::TM_NONE)
+    HL_FUSED_CASE(hl::F32T, 512, 16, hl::TM_NONE)
+    HL_FUSED_CASE(hl::F32T, 512, 20, hl::TM_NONE)
     return nullptr;
 }
 

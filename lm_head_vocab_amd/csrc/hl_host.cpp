@@ -23,6 +23,7 @@ struct hl_plan_s {
     float softcap;
     int tmode;
     int forced_chunks;
+    int forced_block;
     Geometry geo;
     FusedLauncher fused;
     void* ws;
@@ -84,20 +85,28 @@ FusedLauncher lookup(hl_dtype dt, int tmode, int block, int nvec, bool softcap) 
     return get_fused_bf16_rkl(block, nvec, softcap);
 }
 
-// Geometry for C chunks per row, or chunks = 0 when none fits. The register
-// budget per thread is 20 vectors (80 VGPRs) for the student alone and 10 +
-// 10 with a teacher, so that a 1024-thread workgroup stays within 128 VGPRs.
-Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C) {
+// Geometry for C chunks per row with a given block size (0: the smallest
+// block that fits), or chunks = 0 when none fits. The register budget per
+// thread is 20 vectors (80 VGPRs) for the student alone and 10 + 10 with a
+// teacher, so that a 1024-thread workgroup stays within 128 VGPRs.
+Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C, int block = 0) {
     const int vec = dt == HL_F32 ? 4 : 8;
     int64_t nvec_row = V / vec;
     if (nvec_row < 1) nvec_row = 1;
     const int64_t per = (nvec_row + C - 1) / C;
     Geometry g{0, 0, 0};
-    if (per <= (int64_t)kSmallBlock * 4) {
+    if ((block == 0 || block == kSmallBlock) && per <= (int64_t)kSmallBlock * 4) {
         const int need = (int)((per + kSmallBlock - 1) / kSmallBlock);
-        g = Geometry{C, kSmallBlock, round_up_to(kSmallNvec, 3, need)};
-        return g;
+        return Geometry{C, kSmallBlock, round_up_to(kSmallNvec, 3, need)};
     }
+    if (block == kMidBlock) {
+        const int* set = tmode == TM_NONE ? kMidNvecStudent : kMidNvecTeacher;
+        const int n_set = tmode == TM_NONE ? 4 : 3;
+        const int64_t need = (per + kMidBlock - 1) / kMidBlock;
+        if (need > set[n_set - 1]) return g;
+        return Geometry{C, kMidBlock, round_up_to(set, n_set, (int)need)};
+    }
+    if (block != 0 && block != kLargeBlock) return g;
     const int* set = tmode == TM_NONE ? kLargeNvecStudent : kLargeNvecTeacher;
     const int n_set = tmode == TM_NONE ? 10 : 5;
     const int64_t need = (per + kLargeBlock - 1) / kLargeBlock;
@@ -107,7 +116,7 @@ Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C) {
 
 hl_status choose(hl_plan_s* p) {
     if (p->forced_chunks > 0) {
-        Geometry g = geometry_for(p->V, p->dtype, p->tmode, p->forced_chunks);
+        Geometry g = geometry_for(p->V, p->dtype, p->tmode, p->forced_chunks, p->forced_block);
         if (g.chunks == 0) return HL_ERR_UNSUPPORTED;
         p->geo = g;
     } else {
@@ -190,13 +199,34 @@ hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t byte
 
 hl_status hl_plan_set_chunks(hl_plan_t plan, int chunks) {
     if (plan == nullptr || chunks < 0 || chunks > kMaxChunks) return HL_ERR_INVALID_ARG;
-    const int prev = plan->forced_chunks;
+    const int prev = plan->forced_chunks, prev_b = plan->forced_block;
     const Geometry prev_geo = plan->geo;
     const FusedLauncher prev_fn = plan->fused;
     plan->forced_chunks = chunks;
+    plan->forced_block = 0;
     const hl_status st = choose(plan);
     if (st != HL_OK) {
         plan->forced_chunks = prev;
+        plan->forced_block = prev_b;
+        plan->geo = prev_geo;
+        plan->fused = prev_fn;
+    }
+    return st;
+}
+
+hl_status hl_plan_set_variant(hl_plan_t plan, int chunks, int block) {
+    if (plan == nullptr || chunks < 0 || chunks > kMaxChunks) return HL_ERR_INVALID_ARG;
+    if (block != 0 && block != kSmallBlock && block != kMidBlock && block != kLargeBlock) return HL_ERR_INVALID_ARG;
+    if (block != 0 && chunks == 0) return HL_ERR_INVALID_ARG;
+    const int prev_c = plan->forced_chunks, prev_b = plan->forced_block;
+    const Geometry prev_geo = plan->geo;
+    const FusedLauncher prev_fn = plan->fused;
+    plan->forced_chunks = chunks;
+    plan->forced_block = block;
+    const hl_status st = choose(plan);
+    if (st != HL_OK) {
+        plan->forced_chunks = prev_c;
+        plan->forced_block = prev_b;
         plan->geo = prev_geo;
         plan->fused = prev_fn;
     }

@@ -110,8 +110,11 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 
 // Vector counts that have a kernel instance, per block size.
 constexpr int kSmallBlock = 256;
+constexpr int kMidBlock = 512;
 constexpr int kLargeBlock = 1024;
 constexpr int kSmallNvec[] = {1, 2, 4};
+constexpr int kMidNvecStudent[] = {10, 12, 16, 20};
+constexpr int kMidNvecTeacher[] = {6, 8, 10};
 constexpr int kLargeNvecStudent[] = {2, 4, 6, 8, 10, 12, 14, 16, 18, 20};
 constexpr int kLargeNvecTeacher[] = {2, 4, 6, 8, 10};
 

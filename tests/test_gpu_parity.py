@@ -156,6 +156,28 @@ def test_split_vocab_variant(dtype, combo, chunks):
         _check_small(spec, inp, dtype, chunks=chunks)
 
 
+@pytest.mark.parametrize("variant", [(2, 512), (4, 512), (3, 1024), (1, 1024), (6, 256)])
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "grpo_z_ent", "ce_fkl"])
+def test_forced_variants(combo, variant):
+    """Every (chunks, threads per workgroup) layout gives the same answer."""
+    chunks, block = variant
+    spec, inp = _small("bf16", combo, 6, 60013, seed=31 + chunks, softcap=12.0, scale=0.9, mask_frac=0.2)
+    plan = make_plan(spec, torch.bfloat16)
+    try:
+        plan.set_variant(chunks, block)
+    except hl.HeadLossError as e:
+        assert e.status == hl.HL_ERR_UNSUPPORTED
+        pytest.skip(f"no instance for {variant} at V={spec.V}")
+    say(f"[gpu] variant {variant} -> {plan.describe()}")
+    sc, g = run_hip(plan, _to_dev(inp), "overwrite")
+    ref_sc, ref_g, _ = run_oracle(spec, inp)
+    valid, _ = oracle.row_validity(6, spec.V, to_np(inp["labels"]).astype(np.int64), to_np(inp["mask"]))
+    vals = oracle.row_values(spec, to_np(inp["logits"]), to_np(inp["labels"]).astype(np.int64),
+                             to_np(inp["teacher"]), to_np(inp.get("old_logprobs")), to_np(inp.get("advantages")))
+    assert_scalars(spec, sc, ref_sc, "bf16", vals, valid)
+    grad_check(g.cpu(), ref_g, "bf16", labels=to_np(inp["labels"]))
+
+
 def test_split_vocab_accumulate_and_masking():
     spec, inp = _small("bf16", "all_rkl", 12, 50003, seed=9, accumulate=True, mask_frac=0.3, bad_labels=2)
     _check_small(spec, inp, "bf16", chunks=4)
