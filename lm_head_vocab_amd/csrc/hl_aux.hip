@@ -118,16 +118,34 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
     __syncthreads();
     if (s_last == 0u) return;
     __threadfence();
-    if (threadIdx.x < NSUM) {
-        const int c = threadIdx.x;
-        double x = 0.0;
-        for (uint32_t g = 0; g < gridDim.x; ++g) {
-            const uint64_t bits = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p.partials + (int64_t)g * NSUM + c),
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            x += __longlong_as_double((long long)bits);
+    // last workgroup: thread t adds workgroup sums t, t + 256, ... in order,
+    // then a fixed pairwise tree over the 256 threads
+    __shared__ double s_tree[NSUM][kReduceBlock];
+    {
+        double acc2[NSUM];
+#pragma unroll
+        for (int c = 0; c < NSUM; ++c) acc2[c] = 0.0;
+        for (uint32_t g = threadIdx.x; g < gridDim.x; g += kReduceBlock) {
+#pragma unroll
+            for (int c = 0; c < NSUM; ++c) {
+                const uint64_t bits = __hip_atomic_load(
+                    reinterpret_cast<const uint64_t*>(p.partials + (int64_t)g * NSUM + c),
+                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                acc2[c] += __longlong_as_double((long long)bits);
+            }
         }
-        s_sum[c] = x;
+#pragma unroll
+        for (int c = 0; c < NSUM; ++c) s_tree[c][threadIdx.x] = acc2[c];
     }
+    __syncthreads();
+    for (int half = kReduceBlock / 2; half >= 1; half >>= 1) {
+        if ((int)threadIdx.x < half) {
+#pragma unroll
+            for (int c = 0; c < NSUM; ++c) s_tree[c][threadIdx.x] += s_tree[c][threadIdx.x + half];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x < NSUM) s_sum[threadIdx.x] = s_tree[threadIdx.x][0];
     __syncthreads();
     if (threadIdx.x != 0) return;
     const double* sum = s_sum;

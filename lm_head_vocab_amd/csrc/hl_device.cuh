@@ -262,25 +262,29 @@ __global__ __launch_bounds__(BLOCK) void fused_kernel(const FusedParams p) {
     __shared__ float s_rec[16][REC];
     __shared__ float s_fin[REC];
     __shared__ float s_row[8];
-    __shared__ uint32_t s_item;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
     // Which (row, chunk) this workgroup owns. With several chunks per row the
-    // items are claimed in order from a counter, so every chunk a workgroup
-    // waits for has already been claimed by a running workgroup.
-    uint32_t item;
+    // chunks of one row are consecutive workgroups of one XCD: workgroups are
+    // dealt to the 8 XCDs round-robin (blockIdx mod 8) and each XCD starts its
+    // own in order, so XCD x takes rows [x * rows_per_xcd, ...) one row's
+    // chunks after another. A workgroup then only waits for siblings that its
+    // XCD starts right next to it; the wait below is bounded regardless.
+    int64_t row;
+    int c;
     if (p.chunks > 1) {
-        if (tid == 0) s_item = atomicAdd(&p.ctrl[CTRL_CLAIM], 1u);
-        __syncthreads();
-        item = s_item;
+        const uint32_t x = blockIdx.x & 7u, k = blockIdx.x >> 3;
+        const uint32_t rloc = k / (uint32_t)p.chunks;
+        c = (int)(k % (uint32_t)p.chunks);
+        row = (int64_t)x * p.rows_per_xcd + rloc;
+        if (rloc >= (uint32_t)p.rows_per_xcd || row >= p.n_rows) return;
     } else {
-        item = blockIdx.x;
+        row = blockIdx.x;
+        c = 0;
     }
-    const int64_t row = item / (uint32_t)p.chunks;
-    const int c = (int)(item % (uint32_t)p.chunks);
 
     bool valid, bad;
     int64_t y;
@@ -428,16 +432,25 @@ __global__ __launch_bounds__(BLOCK) void fused_kernel(const FusedParams p) {
     }
 
     // ---- split-vocab: publish this chunk's record, wait for the others ----
+    // The record is written with agent-scope atomic stores (they write through
+    // to the device-coherent level, past the per-XCD L2), completed with
+    // s_waitcnt before the counter increment, and read back with agent-scope
+    // atomic loads; no L2 write-back or invalidate is needed.
     if (p.chunks > 1) {
         if (tid == 0) {
             float* mine = p.chunk_rec + ((int64_t)row * p.chunks + c) * REC;
-            mine[0] = r.M; mine[1] = r.Z; mine[2] = r.S;
-            mine[3] = r.Mt; mine[4] = r.Zt; mine[5] = r.SX;
+            __hip_atomic_store(mine + 0, r.M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mine + 1, r.Z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mine + 2, r.S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mine + 3, r.Mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mine + 4, r.Zt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mine + 5, r.SX, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             uint32_t* cnt = p.row_counters + row;
-            __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             uint32_t spins = 0;
-            while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.chunks) {
-                __builtin_amdgcn_s_sleep(2);
+            while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.chunks) {
+                __builtin_amdgcn_s_sleep(1);
                 if (++spins > kSpinLimit) {
                     __hip_atomic_store(&p.ctrl[CTRL_ERROR], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;

@@ -46,6 +46,7 @@ hl_status hip_fail(const char* where, hipError_t e) {
 constexpr uint32_t kLossBits = HL_CE | HL_ZLOSS | HL_FKL | HL_RKL | HL_GRPO | HL_ENTROPY;
 constexpr uint32_t kKnownBits = kLossBits | HL_ACCUMULATE;
 constexpr int kMaxChunks = 64;
+constexpr int kTwoPerCuNvec = 10;   // 64 VGPRs at 1024 threads: two workgroups per CU
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -114,6 +115,10 @@ Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C, int block = 0) {
     return Geometry{C, kLargeBlock, round_up_to(set, n_set, (int)need)};
 }
 
+// Automatic choice: the fewest chunks per row whose slice fits the register
+// budget, except that a student-only 1024-thread slice is kept to at most 10
+// vectors per thread (64 VGPRs), so that two workgroups share a CU and one
+// loads while the other computes.
 hl_status choose(hl_plan_s* p) {
     if (p->forced_chunks > 0) {
         Geometry g = geometry_for(p->V, p->dtype, p->tmode, p->forced_chunks, p->forced_block);
@@ -121,7 +126,12 @@ hl_status choose(hl_plan_s* p) {
         p->geo = g;
     } else {
         Geometry g{0, 0, 0};
-        for (int C = 1; C <= kMaxChunks && g.chunks == 0; ++C) g = geometry_for(p->V, p->dtype, p->tmode, C);
+        for (int C = 1; C <= kMaxChunks; ++C) {
+            g = geometry_for(p->V, p->dtype, p->tmode, C);
+            if (g.chunks == 0) continue;
+            if (p->tmode == TM_NONE && g.block == kLargeBlock && g.nvec > kTwoPerCuNvec) continue;
+            break;
+        }
         if (g.chunks == 0) return HL_ERR_UNSUPPORTED;
         p->geo = g;
     }
@@ -269,7 +279,7 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
         if (!aligned16(logits)) return HL_ERR_INVALID_ARG;
         if (plan->tmode != TM_NONE && !aligned16(teacher_logits)) return HL_ERR_INVALID_ARG;
         if (grad_out != nullptr && !aligned16(grad_out)) return HL_ERR_INVALID_ARG;
-        if ((uint64_t)n_rows * (uint64_t)plan->geo.chunks > 0x7fffffffull) return HL_ERR_UNSUPPORTED;
+        if ((uint64_t)(n_rows + 7) * (uint64_t)plan->geo.chunks > 0x7fffffffull) return HL_ERR_UNSUPPORTED;
     }
 
     const Layout L = layout_for(plan, n_rows);
@@ -322,6 +332,7 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
         fp.n_rows = n_rows;
         fp.V = plan->V;
         fp.chunks = C;
+        fp.rows_per_xcd = (int)((n_rows + 7) / 8);
         fp.accumulate = (f & HL_ACCUMULATE) ? 1 : 0;
         fp.flags = f;
         const float log2e = 1.44269504088896340736f;
@@ -337,7 +348,8 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
         fp.grad_scale = plan->w.grad_scale;
         fp.divisor = plan->w.divisor;
         fp.eps = plan->eps;
-        const dim3 grid((unsigned)(n_rows * C));
+        // split-vocab: 8 XCD groups of rows_per_xcd rows, C workgroups per row
+        const dim3 grid(C > 1 ? (unsigned)(8 * fp.rows_per_xcd * C) : (unsigned)n_rows);
         if (plan->ev_before && (e = hipEventRecord(plan->ev_before, stream)) != hipSuccess)
             return hip_fail("hipEventRecord(before)", e);
         e = plan->fused(fp, grid, stream);

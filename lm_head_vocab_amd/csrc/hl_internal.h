@@ -54,6 +54,7 @@ struct FusedParams {
     int64_t n_rows;
     int64_t V;
     int chunks;
+    int rows_per_xcd;     // split-vocab item mapping: rows handled per XCD group
     int accumulate;
     uint32_t flags;
     float k;          // logit scale

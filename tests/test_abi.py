@@ -69,10 +69,11 @@ def test_plan_rejects(kwargs, status):
 def test_plan_accepts_and_describes_the_baseline_shapes():
     cases = [  # (V, dtype, flags, expected chunks)
         (1024, hl.HL_F32, hl.CE | hl.ZLOSS, 1),
-        (128256, hl.HL_BF16, hl.CE | hl.ZLOSS, 1),
+        (128256, hl.HL_BF16, hl.CE | hl.ZLOSS, 2),
         (151936, hl.HL_BF16, hl.CE | hl.FKL, 2),
         (151936, hl.HL_BF16, hl.CE | hl.RKL, 2),
-        (151936, hl.HL_BF16, hl.GRPO | hl.ZLOSS | hl.ENTROPY, 1),
+        (151936, hl.HL_BF16, hl.GRPO | hl.ZLOSS | hl.ENTROPY, 2),
+        (60000, hl.HL_BF16, hl.CE, 1),
         (256000, hl.HL_BF16, hl.CE | hl.ZLOSS | hl.RKL | hl.GRPO | hl.ENTROPY | hl.ACCUMULATE, 4),
     ]
     for V, dt, flags, chunks in cases:
