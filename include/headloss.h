@@ -135,8 +135,9 @@ size_t hl_workspace_bytes(hl_plan_t plan, int64_t n_rows);
 
 /* Give the plan caller-owned device workspace (256-byte aligned, at least
  * hl_workspace_bytes(plan, n_rows) for every later call). Replaces any
- * workspace the library allocated. Errors: HL_ERR_INVALID_ARG (NULL plan or
- * pointer, misaligned pointer). */
+ * workspace the library allocated. The library zeroes it before returning
+ * (a blocking memset on the default stream). Errors: HL_ERR_INVALID_ARG (NULL
+ * plan or pointer, misaligned pointer), HL_ERR_HIP. */
 hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t bytes);
 
 /*
@@ -189,9 +190,11 @@ const float* hl_row_values(hl_plan_t plan);
 /* Override the number of vocabulary chunks per row (0 = automatic). More than
  * one chunk selects the split-vocab variant: each row is spread over several
  * workgroups whose softmax statistics are combined before the gradient pass
- * (the looped multi-block path of #558 Validation). Errors:
- * HL_ERR_INVALID_ARG (chunks < 0 or > 64), HL_ERR_UNSUPPORTED (no variant
- * fits V with that many chunks). */
+ * (the looped multi-block path of #558 Validation). A successful change
+ * releases a library-owned workspace; a caller-owned one must be set again
+ * with hl_plan_set_workspace before the next call (HL_ERR_WORKSPACE until
+ * then). Errors: HL_ERR_INVALID_ARG (chunks < 0 or > 10),
+ * HL_ERR_UNSUPPORTED (no variant fits V with that many chunks). */
 hl_status hl_plan_set_chunks(hl_plan_t plan, int chunks);
 
 /* Tuning form of hl_plan_set_chunks that also fixes the threads per

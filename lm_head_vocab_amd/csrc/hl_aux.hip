@@ -7,6 +7,11 @@ namespace hl {
 // count_kernel: one workgroup of 1024 threads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
+    if (p.fresh) {
+        const int64_t stride = (int64_t)gridDim.x * 1024;
+        for (int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x; i < p.fill_words; i += stride) p.fill[i] = 0ull;
+        if (blockIdx.x != 0) return;
+    }
     __shared__ uint32_t s_v[16], s_b[16];
     uint32_t nv = 0, nb = 0;
 #pragma unroll 8
@@ -16,7 +21,6 @@ __global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
         row_status(p.labels, p.mask, r, p.V, valid, bad, y);
         nv += valid;
         nb += bad;
-        if (p.row_counters) p.row_counters[r] = 0u;
     }
     for (int m = 32; m >= 1; m >>= 1) {
         nv += __shfl_xor(nv, m, 64);
@@ -30,7 +34,10 @@ __global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
         for (int w = 0; w < 16; ++w) { tv += s_v[w]; tb += s_b[w]; }
         p.ctrl[CTRL_NVALID] = tv;
         p.ctrl[CTRL_NBAD] = tb;
-        p.ctrl[CTRL_CLAIM] = 0u;
+        // tags this call's split-vocab records; a fresh workspace restarts at 1
+        // (its records were just zeroed, i.e. carry epoch 0)
+        const uint32_t next = p.ctrl[CTRL_EPOCH] + 1u;
+        p.ctrl[CTRL_EPOCH] = (p.fresh || next == 0u) ? 1u : next;
         p.ctrl[CTRL_ERROR] = 0u;
         p.ctrl[CTRL_DONE] = 0u;
     }
@@ -183,7 +190,12 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
 
 hipError_t launch_count(const CountParams& p, hipStream_t s) {
     (void)hipGetLastError();   // drop an error left by an earlier, unrelated call
-    hipLaunchKernelGGL(count_kernel, dim3(1), dim3(1024), 0, s, p);
+    int64_t groups = 1;
+    if (p.fresh) {
+        groups = (p.fill_words + 4095) / 4096;
+        groups = groups < 1 ? 1 : (groups > 1024 ? 1024 : groups);
+    }
+    hipLaunchKernelGGL(count_kernel, dim3((unsigned)groups), dim3(1024), 0, s, p);
     return hipGetLastError();
 }
 

@@ -250,10 +250,21 @@ __device__ __forceinline__ void row_status(const int64_t* labels, const uint8_t*
 // fused_kernel
 // ---------------------------------------------------------------------------
 // Bounded wait for the sibling chunks of a row (split-vocab variant only).
-constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+// Waves per SIMD the register allocation must allow (the second
+// __launch_bounds__ argument): student-only slices of at most 10 vectors per
+// thread (8 with softcap) are held to 64 VGPRs, i.e. 8 waves per SIMD, so that
+// 32 waves (two 1024-thread or four 512-thread workgroups) share a CU; every
+// other instance is held to 128 VGPRs (4 waves per SIMD), which all fit.
+template <int BLOCK, int NVEC, int TMODE, bool SOFTCAP>
+constexpr int min_waves_per_simd() {
+    return (TMODE == TM_NONE && NVEC <= (SOFTCAP ? 8 : 10)) ? 8 : 4;
+}
 
 template <typename T, int BLOCK, int NVEC, int TMODE, bool SOFTCAP>
-__global__ __launch_bounds__(BLOCK) void fused_kernel(const FusedParams p) {
+__global__ __launch_bounds__(BLOCK, (min_waves_per_simd<BLOCK, NVEC, TMODE, SOFTCAP>()))
+void fused_kernel(const FusedParams p) {
     constexpr int VEC = T::VEC;
     constexpr int ES = T::ESIZE;
     constexpr int NW = BLOCK / 64;
@@ -261,6 +272,7 @@ __global__ __launch_bounds__(BLOCK) void fused_kernel(const FusedParams p) {
 
     __shared__ float s_rec[16][REC];
     __shared__ float s_fin[REC];
+    __shared__ float s_xw[kMaxChunks * XWORDS];
     __shared__ float s_row[8];
 
     const int tid = threadIdx.x;
@@ -306,7 +318,9 @@ __global__ __launch_bounds__(BLOCK) void fused_kernel(const FusedParams p) {
     const int nv = ve > vb ? (int)(ve - vb) : 0;
     const int n_extra = (c == 0) ? head + tail : 0;
     const bool has_e = tid < n_extra;
-    const int64_t eidx = (tid < head) ? (int64_t)tid : (int64_t)head + nbv * VEC + (tid - head);
+    // row-local element index of this thread's head/tail element (rows are
+    // shorter than 2^31 elements: the plan caps V far below that)
+    const int eidx = (tid < head) ? tid : head + (int)nbv * VEC + (tid - head);
 
     const char* xrow = static_cast<const char*>(p.logits) + rowoff * ES;
     const char* trow = static_cast<const char*>(p.teacher) + rowoff * ES;
@@ -432,45 +446,53 @@ __global__ __launch_bounds__(BLOCK) void fused_kernel(const FusedParams p) {
     }
 
     // ---- split-vocab: publish this chunk's record, wait for the others ----
-    // The record is written with agent-scope atomic stores (they write through
-    // to the device-coherent level, past the per-XCD L2), completed with
-    // s_waitcnt before the counter increment, and read back with agent-scope
-    // atomic loads; no L2 write-back or invalidate is needed.
+    // Each statistic travels as one 64-bit atomic word: its float bits and the
+    // call's epoch (bumped by the count kernel before this kernel starts). A
+    // sibling's word is taken once it carries the current epoch, so nothing
+    // depends on the order in which different words become visible, and no
+    // L2 write-back or invalidate is needed. Wave 0 polls all C x 6 words in
+    // one load per lane per round, then merges the C records with the same
+    // fixed DPP tree in every workgroup of the row.
     if (p.chunks > 1) {
+        const uint64_t epoch = (uint64_t)p.ctrl[CTRL_EPOCH] << 32;
+        uint64_t* words = p.chunk_words + (int64_t)row * p.chunks * XWORDS;
         if (tid == 0) {
-            float* mine = p.chunk_rec + ((int64_t)row * p.chunks + c) * REC;
-            __hip_atomic_store(mine + 0, r.M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(mine + 1, r.Z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(mine + 2, r.S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(mine + 3, r.Mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(mine + 4, r.Zt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(mine + 5, r.SX, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            uint32_t* cnt = p.row_counters + row;
-            __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint64_t* mine = words + c * XWORDS;
+            const float f[XWORDS] = {r.M, r.Z, r.S, r.Mt, r.Zt, r.SX};
+#pragma unroll
+            for (int i = 0; i < XWORDS; ++i)
+                __hip_atomic_store(mine + i, epoch | __float_as_uint(f[i]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (wave == 0) {
+            const int nwords = p.chunks * XWORDS;
+            uint64_t w = 0;
             uint32_t spins = 0;
-            while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.chunks) {
+            while (true) {
+                if (lane < nwords) w = __hip_atomic_load(words + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const bool ok = (lane >= nwords) || ((w & 0xffffffff00000000ull) == epoch);
+                if (__all(ok)) break;
                 __builtin_amdgcn_s_sleep(1);
                 if (++spins > kSpinLimit) {
-                    __hip_atomic_store(&p.ctrl[CTRL_ERROR], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (lane == 0)
+                        __hip_atomic_store(&p.ctrl[CTRL_ERROR], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
             }
-            const float* all = p.chunk_rec + (int64_t)row * p.chunks * REC;
-            Rec acc = rec_empty();
-            for (int cc = 0; cc < p.chunks; ++cc) {
-                const float* q = all + cc * REC;
-                Rec b;
-                b.M = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                b.Z = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                b.S = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                b.Mt = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                b.Zt = __hip_atomic_load(q + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                b.SX = __hip_atomic_load(q + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                acc = rec_merge<TMODE>(acc, b);
+            if (lane < nwords) s_xw[lane] = __uint_as_float((uint32_t)w);
+            // lane l of every 16-lane row holds chunk l's record (empty beyond C)
+            const int l = lane & 15;
+            Rec cr = rec_empty();
+            if (l < p.chunks) {
+                cr.M = s_xw[l * XWORDS + 0]; cr.Z = s_xw[l * XWORDS + 1]; cr.S = s_xw[l * XWORDS + 2];
+                cr.Mt = s_xw[l * XWORDS + 3]; cr.Zt = s_xw[l * XWORDS + 4]; cr.SX = s_xw[l * XWORDS + 5];
+                if (cr.Z == 0.f) cr = rec_empty();
             }
-            s_fin[0] = acc.M; s_fin[1] = acc.Z; s_fin[2] = acc.S;
-            s_fin[3] = acc.Mt; s_fin[4] = acc.Zt; s_fin[5] = acc.SX;
+            cr = rec_reduce16<TMODE>(cr);
+            if (lane == 0) {
+                s_fin[0] = cr.M; s_fin[1] = cr.Z; s_fin[2] = cr.S;
+                s_fin[3] = cr.Mt; s_fin[4] = cr.Zt; s_fin[5] = cr.SX;
+            }
         }
         __syncthreads();
         r.M = s_fin[0]; r.Z = s_fin[1]; r.S = s_fin[2];
@@ -580,7 +602,7 @@ __global__ __launch_bounds__(BLOCK) void fused_kernel(const FusedParams p) {
         }
     }
     if (has_e) {
-        float g = grad_elem(xe, te, eidx == y ? beta : 0.f);
+        float g = grad_elem(xe, te, (int64_t)eidx == y ? beta : 0.f);
         if (p.accumulate) g = T::load1(grow, eidx) + g;
         T::store1(grow, eidx, g);
     }

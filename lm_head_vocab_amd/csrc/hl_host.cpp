@@ -29,6 +29,8 @@ struct hl_plan_s {
     void* ws;
     size_t ws_bytes;
     bool ws_owned;
+    bool ws_stale;      // the variant changed after a caller workspace was set
+    int64_t clean_rows; // rows whose split-vocab words are known zero or this plan's (-1: none)
     int64_t last_rows;
     hipEvent_t ev_before;
     hipEvent_t ev_after;
@@ -45,22 +47,21 @@ hl_status hip_fail(const char* where, hipError_t e) {
 
 constexpr uint32_t kLossBits = HL_CE | HL_ZLOSS | HL_FKL | HL_RKL | HL_GRPO | HL_ENTROPY;
 constexpr uint32_t kKnownBits = kLossBits | HL_ACCUMULATE;
-constexpr int kMaxChunks = 64;
-constexpr int kTwoPerCuNvec = 10;   // 64 VGPRs at 1024 threads: two workgroups per CU
+constexpr int kTwoPerCuNvec = 10;         // 64 VGPRs at 1024 threads: two workgroups per CU
+constexpr int kTwoPerCuNvecSoftcap = 8;   // the softcap instances need a few more registers
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-    size_t ctrl, counters, chunk_rec, row_rec, rows, partials, total;
+    size_t ctrl, chunk_rec, row_rec, rows, partials, total;
 };
 
 Layout layout_for(const hl_plan_s* p, int64_t n) {
     Layout L;
     const size_t N = n > 0 ? (size_t)n : 0;
     L.ctrl = 0;
-    L.counters = align256(NCTRL * sizeof(uint32_t));
-    L.chunk_rec = L.counters + align256(N * sizeof(uint32_t));
-    const size_t rec_bytes = p->geo.chunks > 1 ? N * p->geo.chunks * REC * sizeof(float) : 0;
+    L.chunk_rec = align256(NCTRL * sizeof(uint32_t));
+    const size_t rec_bytes = p->geo.chunks > 1 ? N * p->geo.chunks * XWORDS * sizeof(uint64_t) : 0;
     L.row_rec = L.chunk_rec + align256(rec_bytes);
     L.rows = L.row_rec + align256(N * REC * sizeof(float));
     L.partials = L.rows + align256(N * NCOL * sizeof(float));
@@ -129,7 +130,9 @@ hl_status choose(hl_plan_s* p) {
         for (int C = 1; C <= kMaxChunks; ++C) {
             g = geometry_for(p->V, p->dtype, p->tmode, C);
             if (g.chunks == 0) continue;
-            if (p->tmode == TM_NONE && g.block == kLargeBlock && g.nvec > kTwoPerCuNvec) continue;
+            if (p->tmode == TM_NONE && g.block == kLargeBlock &&
+                g.nvec > (p->softcap > 0.f ? kTwoPerCuNvecSoftcap : kTwoPerCuNvec))
+                continue;
             break;
         }
         if (g.chunks == 0) return HL_ERR_UNSUPPORTED;
@@ -141,6 +144,22 @@ hl_status choose(hl_plan_s* p) {
 
 bool finite(float x) { return std::isfinite(x); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The workspace layout depends on the variant: a library-owned buffer is
+// released (the next call allocates a zeroed one); a caller's buffer must be
+// handed over again with hl_plan_set_workspace.
+void invalidate_workspace(hl_plan_s* p) {
+    if (p->ws == nullptr) return;
+    if (p->ws_owned) {
+        (void)hipFree(p->ws);
+        p->ws = nullptr;
+        p->ws_bytes = 0;
+        p->ws_owned = false;
+    } else {
+        p->ws_stale = true;
+    }
+    p->clean_rows = -1;
+}
 
 }  // namespace
 
@@ -204,6 +223,8 @@ hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t byte
     plan->ws = dev_workspace;
     plan->ws_bytes = bytes;
     plan->ws_owned = false;
+    plan->ws_stale = false;
+    plan->clean_rows = -1;
     return HL_OK;
 }
 
@@ -220,6 +241,8 @@ hl_status hl_plan_set_chunks(hl_plan_t plan, int chunks) {
         plan->forced_block = prev_b;
         plan->geo = prev_geo;
         plan->fused = prev_fn;
+    } else {
+        invalidate_workspace(plan);
     }
     return st;
 }
@@ -239,6 +262,8 @@ hl_status hl_plan_set_variant(hl_plan_t plan, int chunks, int block) {
         plan->forced_block = prev_b;
         plan->geo = prev_geo;
         plan->fused = prev_fn;
+    } else {
+        invalidate_workspace(plan);
     }
     return st;
 }
@@ -283,6 +308,7 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
     }
 
     const Layout L = layout_for(plan, n_rows);
+    if (plan->ws_stale) return HL_ERR_WORKSPACE;
     if (plan->ws == nullptr || plan->ws_bytes < L.total) {
         if (plan->ws != nullptr && !plan->ws_owned) return HL_ERR_WORKSPACE;
         if (plan->ws_owned && plan->ws) {
@@ -291,17 +317,17 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
             plan->ws_bytes = 0;
         }
         void* mem = nullptr;
-        const hipError_t me = hipMalloc(&mem, L.total);
+        hipError_t me = hipMalloc(&mem, L.total);
         if (me != hipSuccess) return hip_fail("hipMalloc(workspace)", me);
         plan->ws = mem;
         plan->ws_bytes = L.total;
         plan->ws_owned = true;
+        plan->clean_rows = -1;
     }
     plan->last_rows = n_rows;
     char* ws = static_cast<char*>(plan->ws);
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
-    uint32_t* counters = reinterpret_cast<uint32_t*>(ws + L.counters);
-    float* chunk_rec = reinterpret_cast<float*>(ws + L.chunk_rec);
+    uint64_t* chunk_words = reinterpret_cast<uint64_t*>(ws + L.chunk_rec);
     float* row_rec = reinterpret_cast<float*>(ws + L.row_rec);
     float* rows = reinterpret_cast<float*>(ws + L.rows);
     const int C = plan->geo.chunks;
@@ -310,9 +336,16 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
     cp.labels = labels;
     cp.mask = mask;
     cp.ctrl = ctrl;
-    cp.row_counters = C > 1 ? counters : nullptr;
     cp.n_rows = n_rows;
     cp.V = plan->V;
+    // The split-vocab words of rows [0, clean_rows) hold zeros or this plan's
+    // own records (older epochs). Anything else (a new workspace, or a region
+    // another call's layout used for other data) is zero-filled by the count
+    // kernel first, and the epoch restarts.
+    const bool fresh = C > 1 && plan->clean_rows < n_rows;
+    cp.fresh = fresh ? 1 : 0;
+    cp.fill = chunk_words;
+    cp.fill_words = C > 1 ? n_rows * C * XWORDS : 0;
     hipError_t e = launch_count(cp, stream);
     if (e != hipSuccess) return hip_fail("count kernel launch", e);
 
@@ -326,8 +359,7 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
         fp.advantages = (f & HL_GRPO) ? advantages : nullptr;
         fp.grad = grad_out;
         fp.row_rec = row_rec;
-        fp.chunk_rec = chunk_rec;
-        fp.row_counters = counters;
+        fp.chunk_words = chunk_words;
         fp.ctrl = ctrl;
         fp.n_rows = n_rows;
         fp.V = plan->V;
@@ -379,6 +411,8 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
     rp.divisor = plan->w.divisor;
     e = launch_reduce(rp, stream);
     if (e != hipSuccess) return hip_fail("reduce kernel launch", e);
+    // this call's other regions may have written past its own record region
+    plan->clean_rows = fresh ? n_rows : (plan->clean_rows < n_rows ? plan->clean_rows : n_rows);
     return HL_OK;
 }
 

@@ -31,7 +31,12 @@ constexpr int NSCALARS = 13;
 enum RecField : int { R_M = 0, R_Z, R_S, R_MT, R_ZT, R_SX, R_XY, R_VALID, REC };
 
 // Control words at the start of the workspace.
-enum Ctrl : int { CTRL_NVALID = 0, CTRL_NBAD = 1, CTRL_CLAIM = 2, CTRL_ERROR = 3, CTRL_DONE = 4, NCTRL = 64 };
+enum Ctrl : int { CTRL_NVALID = 0, CTRL_NBAD = 1, CTRL_EPOCH = 2, CTRL_ERROR = 3, CTRL_DONE = 4, NCTRL = 64 };
+
+// Split-vocab exchange: each chunk publishes its 6 statistics as 64-bit words
+// (float bits low, call epoch high); at most kMaxChunks chunks per row.
+constexpr int XWORDS = 6;
+constexpr int kMaxChunks = 10;
 
 struct Geometry {
     int chunks;      // workgroups per row
@@ -48,8 +53,7 @@ struct FusedParams {
     const float* advantages;
     void* grad;
     float* row_rec;           // [N, REC]
-    float* chunk_rec;         // [N, C, REC]
-    uint32_t* row_counters;   // [N]
+    uint64_t* chunk_words;    // [N, C, XWORDS]
     uint32_t* ctrl;           // [NCTRL]
     int64_t n_rows;
     int64_t V;
@@ -72,9 +76,13 @@ struct CountParams {
     const int64_t* labels;
     const uint8_t* mask;
     uint32_t* ctrl;
-    uint32_t* row_counters;   // zeroed when non-null
     int64_t n_rows;
     int64_t V;
+    // First call on a new workspace: every workgroup zero-fills its stripe of
+    // the split-vocab words and workgroup 0 restarts the epoch at 1.
+    int fresh;
+    uint64_t* fill;
+    int64_t fill_words;
 };
 
 constexpr int kReduceBlock = 256;   // rows per reduction workgroup
@@ -106,7 +114,7 @@ FusedLauncher get_fused_bf16_none(int block, int nvec, bool softcap);
 FusedLauncher get_fused_bf16_fkl(int block, int nvec, bool softcap);
 FusedLauncher get_fused_bf16_rkl(int block, int nvec, bool softcap);
 
-hipError_t launch_count(const CountParams& p, hipStream_t s);
+hipError_t launch_count(const CountParams& p, hipStream_t s);  // grid grows when p.fresh
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 
 // Vector counts that have a kernel instance, per block size.
