@@ -117,9 +117,11 @@ Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C, int block = 0) {
 }
 
 // Automatic choice: the fewest chunks per row whose slice fits the register
-// budget, except that a student-only 1024-thread slice is kept to at most 10
-// vectors per thread (64 VGPRs), so that two workgroups share a CU and one
-// loads while the other computes.
+// budget while two workgroups still share a CU (one loads while the other
+// computes): a student-only slice at 1024 threads holds at most 10 vectors
+// per thread (8 with softcap, 64 VGPRs); a slice with a teacher uses 512
+// threads and at most 10 + 10 vectors (about 113 VGPRs). Short rows use one
+// 256-thread workgroup.
 hl_status choose(hl_plan_s* p) {
     if (p->forced_chunks > 0) {
         Geometry g = geometry_for(p->V, p->dtype, p->tmode, p->forced_chunks, p->forced_block);
@@ -130,10 +132,20 @@ hl_status choose(hl_plan_s* p) {
         for (int C = 1; C <= kMaxChunks; ++C) {
             g = geometry_for(p->V, p->dtype, p->tmode, C);
             if (g.chunks == 0) continue;
-            if (p->tmode == TM_NONE && g.block == kLargeBlock &&
-                g.nvec > (p->softcap > 0.f ? kTwoPerCuNvecSoftcap : kTwoPerCuNvec))
-                continue;
-            break;
+            if (g.block == kSmallBlock) break;
+            if (p->tmode == TM_NONE) {
+                if (g.nvec <= (p->softcap > 0.f ? kTwoPerCuNvecSoftcap : kTwoPerCuNvec)) break;
+            } else {
+                const Geometry mid = geometry_for(p->V, p->dtype, p->tmode, C, kMidBlock);
+                if (mid.chunks != 0) {
+                    g = mid;
+                    break;
+                }
+            }
+            g = Geometry{0, 0, 0};
+        }
+        if (g.chunks == 0) {   // very long rows: the fewest chunks that fit at all
+            for (int C = 1; C <= kMaxChunks && g.chunks == 0; ++C) g = geometry_for(p->V, p->dtype, p->tmode, C);
         }
         if (g.chunks == 0) return HL_ERR_UNSUPPORTED;
         p->geo = g;

@@ -67,21 +67,22 @@ def test_plan_rejects(kwargs, status):
 
 
 def test_plan_accepts_and_describes_the_baseline_shapes():
-    cases = [  # (V, dtype, flags, expected chunks)
-        (1024, hl.HL_F32, hl.CE | hl.ZLOSS, 1),
-        (128256, hl.HL_BF16, hl.CE | hl.ZLOSS, 2),
-        (151936, hl.HL_BF16, hl.CE | hl.FKL, 2),
-        (151936, hl.HL_BF16, hl.CE | hl.RKL, 2),
-        (151936, hl.HL_BF16, hl.GRPO | hl.ZLOSS | hl.ENTROPY, 2),
-        (60000, hl.HL_BF16, hl.CE, 1),
-        (256000, hl.HL_BF16, hl.CE | hl.ZLOSS | hl.RKL | hl.GRPO | hl.ENTROPY | hl.ACCUMULATE, 4),
+    cases = [  # (V, dtype, flags, expected chunks, expected threads per workgroup)
+        (1024, hl.HL_F32, hl.CE | hl.ZLOSS, 1, 256),
+        (128256, hl.HL_BF16, hl.CE | hl.ZLOSS, 2, 1024),
+        (151936, hl.HL_BF16, hl.CE | hl.FKL, 4, 512),
+        (151936, hl.HL_BF16, hl.CE | hl.RKL, 4, 512),
+        (151936, hl.HL_BF16, hl.GRPO | hl.ZLOSS | hl.ENTROPY, 2, 1024),
+        (60000, hl.HL_BF16, hl.CE, 1, 1024),
+        (256000, hl.HL_BF16, hl.CE | hl.ZLOSS | hl.RKL | hl.GRPO | hl.ENTROPY | hl.ACCUMULATE, 7, 512),
+        (1_500_000, hl.HL_BF16, hl.CE, 10, 1024),
     ]
-    for V, dt, flags, chunks in cases:
+    for V, dt, flags, chunks, block in cases:
         st, h = _plan(V=V, dtype=dt, flags=flags, cap=30.0 if V == 256000 else 0.0)
         assert st == hl.HL_OK, (V, flags)
         c, b, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
         assert lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), ctypes.byref(n)) == 0
-        assert c.value == chunks, (V, flags, c.value)
+        assert (c.value, b.value) == (chunks, block), (V, flags, c.value, b.value)
         vec = 4 if dt == hl.HL_F32 else 8
         # every body vector of a chunk has a thread slot
         assert c.value * b.value * n.value * vec >= V - 2 * vec
@@ -94,7 +95,9 @@ def test_set_chunks_and_errors():
     st, h = _plan(V=20000)
     assert st == 0
     assert lib.hl_plan_set_chunks(h, -1) == hl.HL_ERR_INVALID_ARG
-    assert lib.hl_plan_set_chunks(h, 65) == hl.HL_ERR_INVALID_ARG
+    assert lib.hl_plan_set_chunks(h, 11) == hl.HL_ERR_INVALID_ARG
+    assert lib.hl_plan_set_variant(h, 2, 300) == hl.HL_ERR_INVALID_ARG
+    assert lib.hl_plan_set_variant(h, 0, 512) == hl.HL_ERR_INVALID_ARG
     assert lib.hl_plan_set_chunks(h, 3) == hl.HL_OK
     c = ctypes.c_int()
     lib.hl_plan_describe(h, ctypes.byref(c), None, None)
@@ -107,7 +110,21 @@ def test_set_chunks_and_errors():
     st, h = _plan(V=256000, flags=hl.CE | hl.RKL)
     assert lib.hl_plan_set_chunks(h, 1) == hl.HL_ERR_UNSUPPORTED
     lib.hl_plan_describe(h, ctypes.byref(c), None, None)
-    assert c.value == 4
+    assert c.value == 7
+    lib.hl_plan_destroy(h)
+
+
+def test_variant_change_invalidates_a_caller_workspace():
+    st, h = _plan(V=5000, flags=hl.CE)
+    fake = VP(4096)
+    fb = lib.hl_forward_backward
+    # a caller workspace that is too small is refused before any HIP call
+    assert lib.hl_plan_set_workspace(h, fake, 8) == hl.HL_OK
+    assert fb(h, 4, fake, fake, None, None, None, None, None, fake, None) == hl.HL_ERR_WORKSPACE
+    assert lib.hl_plan_set_workspace(h, fake, 1 << 30) == hl.HL_OK
+    assert lib.hl_plan_set_variant(h, 3, 256) == hl.HL_OK
+    # the layout changed: the caller's workspace must be handed over again
+    assert fb(h, 4, fake, fake, None, None, None, None, None, fake, None) == hl.HL_ERR_WORKSPACE
     lib.hl_plan_destroy(h)
 
 

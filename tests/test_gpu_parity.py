@@ -178,6 +178,23 @@ def test_forced_variants(combo, variant):
     grad_check(g.cpu(), ref_g, "bf16", labels=to_np(inp["labels"]))
 
 
+def test_split_vocab_calls_with_changing_batch_sizes():
+    """One plan, calls of different sizes: the workspace layout moves between
+    calls and every call must still combine only its own chunk records."""
+    spec, _ = _small("bf16", "all_fkl", 2, 60013, seed=1)
+    plan = make_plan(spec, torch.bfloat16, chunks=3)
+    for i, N in enumerate((8, 3, 8, 12, 5)):
+        _, inp = _small("bf16", "all_fkl", N, 60013, seed=100 + i, mask_frac=0.2)
+        say(f"[gpu] changing batch N={N}")
+        sc, g = run_hip(plan, _to_dev(inp), "overwrite")
+        ref_sc, ref_g, _ = run_oracle(spec, inp)
+        valid, _ = oracle.row_validity(N, spec.V, to_np(inp["labels"]).astype(np.int64), to_np(inp["mask"]))
+        vals = oracle.row_values(spec, to_np(inp["logits"]), to_np(inp["labels"]).astype(np.int64),
+                                 to_np(inp["teacher"]), to_np(inp["old_logprobs"]), to_np(inp["advantages"]))
+        assert_scalars(spec, sc, ref_sc, "bf16", vals, valid)
+        grad_check(g.cpu(), ref_g, "bf16", labels=to_np(inp["labels"]))
+
+
 def test_split_vocab_accumulate_and_masking():
     spec, inp = _small("bf16", "all_rkl", 12, 50003, seed=9, accumulate=True, mask_frac=0.3, bad_labels=2)
     _check_small(spec, inp, "bf16", chunks=4)
