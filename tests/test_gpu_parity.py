@@ -178,6 +178,39 @@ def test_forced_variants(combo, variant):
     grad_check(g.cpu(), ref_g, "bf16", labels=to_np(inp["labels"]))
 
 
+@pytest.mark.parametrize("chunks", [0, 3])
+@pytest.mark.parametrize("combo", ["all_rkl", "all_fkl"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_per_token_values(dtype, combo, chunks):
+    """hl_row_values: every per-token column (CE, z, KL, GRPO objective, new
+    log-prob, ratio, clip flag, k3, advantage, entropy, valid) row by row."""
+    spec, inp = _small(dtype, combo, 29, 20011, seed=41 + chunks, mask_frac=0.2, bad_labels=2,
+                       softcap=9.0, scale=0.7)
+    plan = make_plan(spec, TDT[dtype], chunks)
+    say(f"[gpu] per-token values {dtype} {combo} {plan.describe()}")
+    run_hip(plan, _to_dev(inp), "none")
+    rv = plan.row_values().cpu().double().numpy()
+    N = inp["logits"].shape[0]
+    y = to_np(inp["labels"]).astype(np.int64)
+    valid, _ = oracle.row_validity(N, spec.V, y, to_np(inp["mask"]))
+    vals = oracle.row_values(spec, to_np(inp["logits"]), y, to_np(inp["teacher"]),
+                             to_np(inp["old_logprobs"]), to_np(inp["advantages"]))
+    kl = "fkl" if spec.has(FKL) else "rkl"
+    rel = TOL[dtype]["scalar_rel"]
+    np.testing.assert_array_equal(rv[:, 10], valid.astype(float))
+    assert np.all(rv[~valid] == 0.0)
+    for key, col in (("ce", 0), ("z", 1), (kl, 2), ("grpo", 3), ("logp", 4), ("ratio", 5),
+                     ("k3", 7), ("adv", 8), ("entropy", 9)):
+        ref = vals[key][valid]
+        got = rv[valid, col]
+        scale = np.maximum(np.abs(ref), 1e-2 * max(1.0, float(np.max(np.abs(ref)))))
+        err = np.max(np.abs(got - ref) / scale)
+        assert err <= rel, (key, err)
+    boundary = (np.abs(vals["ratio"] - 1.2) < 1e-5) | (np.abs(vals["ratio"] - 0.8) < 1e-5)
+    keep = valid & ~boundary
+    np.testing.assert_array_equal(rv[keep, 6] != 0, vals["clipped"][keep])
+
+
 def test_split_vocab_calls_with_changing_batch_sizes():
     """One plan, calls of different sizes: the workspace layout moves between
     calls and every call must still combine only its own chunk records."""
