@@ -47,8 +47,10 @@ typedef enum {
     HL_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
 } hl_status;
 
-/* Element type of logits, teacher logits and gradient (all three share it). */
-typedef enum { HL_F32 = 0, HL_BF16 = 1 } hl_dtype;
+/* Element type of logits, teacher logits and gradient (all three share it).
+ * fp16 inputs are among the dtypes the monolithic kernel is validated with
+ * (#558 Validation); an fp16 gradient underflows below 6e-8 (use grad_scale). */
+typedef enum { HL_F32 = 0, HL_BF16 = 1, HL_F16 = 2 } hl_dtype;
 
 /* Loss and metric flags (#507 Proposed direction: "a config / flag-set
  * describing which losses and metrics to emit"). At most one distillation

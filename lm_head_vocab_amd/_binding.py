@@ -26,6 +26,7 @@ HL_ERR_HIP = 5
 
 HL_F32 = 0
 HL_BF16 = 1
+HL_F16 = 2
 
 CE = 1 << 0
 ZLOSS = 1 << 1
@@ -135,7 +136,9 @@ def _dtype_code(dtype) -> int:
         return HL_F32
     if dtype in (torch.bfloat16, "bf16", "bfloat16"):
         return HL_BF16
-    raise ValueError(f"unsupported dtype {dtype!r}: use float32 or bfloat16")
+    if dtype in (torch.float16, "f16", "float16"):
+        return HL_F16
+    raise ValueError(f"unsupported dtype {dtype!r}: use float32, bfloat16 or float16")
 
 
 class Plan:
@@ -221,7 +224,7 @@ class Plan:
         if logits.dim() != 2 or logits.shape[1] != self.V:
             raise ValueError(f"logits must be [N, {self.V}], got {tuple(logits.shape)}")
         n = logits.shape[0]
-        dt = torch.float32 if self.dtype_code == HL_F32 else torch.bfloat16
+        dt = {HL_F32: torch.float32, HL_BF16: torch.bfloat16, HL_F16: torch.float16}[self.dtype_code]
         dev = logits.device
         if mask is not None and mask.dtype == torch.bool:
             mask = mask.view(torch.uint8)

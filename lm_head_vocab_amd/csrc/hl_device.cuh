@@ -27,6 +27,7 @@ namespace hl {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2f = 0.69314718055994530942f;
@@ -90,6 +91,40 @@ struct BF16T {
     }
     __device__ static __forceinline__ void store1(char* rowbase, int64_t i, float g) {
         reinterpret_cast<uint16_t*>(rowbase)[i] = static_cast<uint16_t>(pack2(g, 0.0f) & 0xffffu);
+    }
+    __device__ static __forceinline__ u32x4 pack(const float* g) {
+        u32x4 r;
+        r[0] = pack2(g[0], g[1]);
+        r[1] = pack2(g[2], g[3]);
+        r[2] = pack2(g[4], g[5]);
+        r[3] = pack2(g[6], g[7]);
+        return r;
+    }
+};
+
+struct F16T {
+    static constexpr int VEC = 8;
+    static constexpr int ESIZE = 2;
+    __device__ static __forceinline__ float get(const u32x4& w, int e) {
+        const uint32_t word = w[e >> 1];
+        const uint16_t h = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xffffu);
+        return (float)__builtin_bit_cast(_Float16, h);
+    }
+    __device__ static __forceinline__ float load1(const char* rowbase, int64_t i) {
+        return (float)reinterpret_cast<const _Float16*>(rowbase)[i];
+    }
+    __device__ static __forceinline__ float vmax(float acc, const u32x4& w) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) acc = fmaxf(acc, fmaxf(get(w, e), get(w, e + 1)));
+        return acc;
+    }
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+        f32x2 v = {lo, hi};
+        f16x2 h = __builtin_convertvector(v, f16x2);   // round to nearest even
+        return __builtin_bit_cast(uint32_t, h);
+    }
+    __device__ static __forceinline__ void store1(char* rowbase, int64_t i, float g) {
+        reinterpret_cast<_Float16*>(rowbase)[i] = (_Float16)g;
     }
     __device__ static __forceinline__ u32x4 pack(const float* g) {
         u32x4 r;

@@ -82,6 +82,11 @@ FusedLauncher lookup(hl_dtype dt, int tmode, int block, int nvec, bool softcap) 
         if (tmode == TM_FKL) return get_fused_f32_fkl(block, nvec, softcap);
         return get_fused_f32_rkl(block, nvec, softcap);
     }
+    if (dt == HL_F16) {
+        if (tmode == TM_NONE) return get_fused_f16_none(block, nvec, softcap);
+        if (tmode == TM_FKL) return get_fused_f16_fkl(block, nvec, softcap);
+        return get_fused_f16_rkl(block, nvec, softcap);
+    }
     if (tmode == TM_NONE) return get_fused_bf16_none(block, nvec, softcap);
     if (tmode == TM_FKL) return get_fused_bf16_fkl(block, nvec, softcap);
     return get_fused_bf16_rkl(block, nvec, softcap);
@@ -183,7 +188,7 @@ hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags
     if (out == nullptr) return HL_ERR_INVALID_ARG;
     *out = nullptr;
     if (V < 1 || weights == nullptr) return HL_ERR_INVALID_ARG;
-    if (dtype != HL_F32 && dtype != HL_BF16) return HL_ERR_INVALID_ARG;
+    if (dtype != HL_F32 && dtype != HL_BF16 && dtype != HL_F16) return HL_ERR_INVALID_ARG;
     if ((loss_flags & ~kKnownBits) != 0u || (loss_flags & kLossBits) == 0u) return HL_ERR_INVALID_ARG;
     if ((loss_flags & HL_FKL) && (loss_flags & HL_RKL)) return HL_ERR_INVALID_ARG;
     const bool distill = (loss_flags & (HL_FKL | HL_RKL)) != 0u;

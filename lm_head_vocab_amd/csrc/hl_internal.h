@@ -113,6 +113,9 @@ FusedLauncher get_fused_f32_rkl(int block, int nvec, bool softcap);
 FusedLauncher get_fused_bf16_none(int block, int nvec, bool softcap);
 FusedLauncher get_fused_bf16_fkl(int block, int nvec, bool softcap);
 FusedLauncher get_fused_bf16_rkl(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f16_none(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f16_fkl(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f16_rkl(int block, int nvec, bool softcap);
 
 hipError_t launch_count(const CountParams& p, hipStream_t s);  // grid grows when p.fresh
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);

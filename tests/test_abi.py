@@ -165,4 +165,4 @@ def test_binding_marshalling_errors_without_gpu():
     with pytest.raises(hl.HeadLossError):
         hl.Plan(64, torch.bfloat16, hl.FKL | hl.RKL)
     with pytest.raises(ValueError):
-        hl.Plan(64, torch.float16, hl.CE)
+        hl.Plan(64, torch.int8, hl.CE)

@@ -29,7 +29,11 @@ from oracle import SLOT
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+INT_VIEW = {"f32": torch.int32, "bf16": torch.int16, "f16": torch.int16}
+# fp16 gradients of small softmax entries sit below fp16's normal range; the
+# fp16 cases use a loss scale (grad_scale) of 1024, as fp16 training does.
+F16_LOSS_SCALE = 1024.0
 
 CE, Z, FKL, RKL, GRPO, ENT, ACC = (oracle.CE, oracle.ZLOSS, oracle.FKL, oracle.RKL, oracle.GRPO,
                                    oracle.ENTROPY, oracle.ACCUMULATE)
@@ -61,6 +65,8 @@ def _grpo_boundary_rows(spec, inp_cpu, eps_tol=1e-5):
 def _small(dtype, combo, N, V, seed, softcap=0.0, scale=1.0, accumulate=False, temperature=1.5,
            logit_std=2.0, **gen):
     flags, w = COMBOS[combo]
+    if dtype == "f16":
+        w = dict(w, grad_scale=w.get("grad_scale", 1.0) * F16_LOSS_SCALE)
     if accumulate:
         flags |= ACC
     spec = spec_from(V, flags, w, temperature=temperature, eps=0.2, logit_scale=scale, softcap=softcap)
@@ -103,8 +109,7 @@ def _check_small(spec, inp, dtype, chunks=0, grad_mode=None):
     # masked rows: +0.0 in overwrite mode, bit-identical existing values in accumulate mode
     inval = torch.from_numpy(~valid)
     if grad_mode == "overwrite":
-        assert torch.equal(gk[inval].view(torch.int16 if dtype == "bf16" else torch.int32),
-                           torch.zeros_like(gk[inval]).view(torch.int16 if dtype == "bf16" else torch.int32))
+        assert torch.equal(gk[inval].view(INT_VIEW[dtype]), torch.zeros_like(gk[inval]).view(INT_VIEW[dtype]))
     else:
         assert torch.equal(gk[inval], inp["grad_init"][inval])
     return plan, sc, metrics
@@ -112,7 +117,7 @@ def _check_small(spec, inp, dtype, chunks=0, grad_mode=None):
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{n}x{v}" for n, v in SHAPES])
 @pytest.mark.parametrize("combo", list(COMBOS))
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_small_parity(dtype, combo, shape):
     N, V = shape
     spec, inp = _small(dtype, combo, N, V, seed=11 * N + V, bad_labels=1 if N > 4 else 0,
@@ -122,14 +127,14 @@ def test_small_parity(dtype, combo, shape):
 
 @pytest.mark.parametrize("logit_std", [2.0, 40.0], ids=["poly", "exp_branch"])
 @pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "grpo_z_ent"])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_softcap_and_scale(dtype, combo, logit_std):
     spec, inp = _small(dtype, combo, 24, 2053, seed=7, softcap=7.0, scale=0.5, logit_std=logit_std)
     _check_small(spec, inp, dtype)
 
 
 @pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "z_ent"])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("V", [1000, 20011])
 def test_accumulate(dtype, combo, V):
     spec, inp = _small(dtype, combo, 19, V, seed=3, accumulate=True, mask_frac=0.2, softcap=30.0, scale=0.5)
@@ -148,7 +153,7 @@ def test_forward_only_matches_and_writes_nothing(dtype, combo):
 
 @pytest.mark.parametrize("chunks", [2, 3, 5])
 @pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "ce_fkl"])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_split_vocab_variant(dtype, combo, chunks):
     # forced chunking exercises the cross-workgroup combine at small sizes
     for V, N in ((20011, 7), (70000, 5)):
@@ -180,7 +185,7 @@ def test_forced_variants(combo, variant):
 
 @pytest.mark.parametrize("chunks", [0, 3])
 @pytest.mark.parametrize("combo", ["all_rkl", "all_fkl"])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_per_token_values(dtype, combo, chunks):
     """hl_row_values: every per-token column (CE, z, KL, GRPO objective, new
     log-prob, ratio, clip flag, k3, advantage, entropy, valid) row by row."""
@@ -314,7 +319,8 @@ def test_fused_equals_separate_passes(combo):
 # ---------------------------------------------------------------------------
 # The benchmark configurations at full size
 # ---------------------------------------------------------------------------
-FULL = ["ce_z_tiny_f32", "ce_z_bf16", "ce_fkl_bf16", "ce_rkl_bf16", "grpo_z_ent_bf16", "all_combined_bf16"]
+FULL = ["ce_z_tiny_f32", "ce_z_bf16", "ce_fkl_bf16", "ce_rkl_bf16", "grpo_z_ent_bf16", "all_combined_bf16",
+        "ce_z_f16"]
 
 
 def _full_inputs(name):
@@ -345,7 +351,7 @@ def test_full_config_sampled(name):
     # property at any size: every masked row is +0.0 (or untouched)
     inval = torch.from_numpy(~valid).to(DEV)
     if grad_mode == "overwrite" and inval.any():
-        assert torch.count_nonzero(g[inval].view(torch.int16 if w.dtype == "bf16" else torch.int32)).item() == 0
+        assert torch.count_nonzero(g[inval].view(INT_VIEW[w.dtype])).item() == 0
     elif inval.any():
         assert torch.equal(g[inval], inp["grad_init"][inval])
     # property: scalars are the fixed-order means of the per-row values

@@ -41,7 +41,7 @@ class Workload:
 
     @property
     def torch_dtype(self):
-        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[self.dtype]
 
     @property
     def elem_bytes(self) -> int:
@@ -58,6 +58,11 @@ WORKLOADS = {
         weights=dict(ce=1.0, z=1e-4),
         description="CE + z-loss (1e-4), logits ~ N(0, 3^2) with one +8 confident column per row; "
                     "label = that column on 70% of rows; 10% label=-100"),
+    "ce_z_f16": Workload(
+        "ce_z_f16", N=8192, V=128256, dtype="f16", flags=CE | ZLOSS,
+        weights=dict(ce=1.0, z=1e-4, grad_scale=float(2 ** 24)),
+        description="the ce_z_bf16 recipe with fp16 logits and gradient; loss scale 2^24 keeps the "
+                    "gradient inside fp16's normal range"),
     "ce_fkl_bf16": Workload(
         "ce_fkl_bf16", N=4096, V=151936, dtype="bf16", flags=CE | FKL,
         weights=dict(ce=0.5, distill=1.0), temperature=2.0,
@@ -93,7 +98,7 @@ HEADLINE = "grpo_z_ent_bf16"
 
 def seed_for(name: str, subcase: int = 0) -> int:
     order = ["ce_z_tiny_f32", "ce_z_bf16", "ce_fkl_bf16", "grpo_z_ent_bf16", "all_combined_bf16"]
-    base = "ce_fkl_bf16" if name == "ce_rkl_bf16" else name
+    base = {"ce_rkl_bf16": "ce_fkl_bf16", "ce_z_f16": "ce_z_bf16"}.get(name, name)
     return 1000 * (order.index(base) + 1) + subcase
 
 
@@ -141,7 +146,7 @@ def generate(w: Workload | str, device="cpu", seed: int | None = None, n_rows: i
         y = uniform_labels(N)
         y[bernoulli(N, 0.1)] = -100
         out["labels"] = y
-    elif w.name == "ce_z_bf16":
+    elif w.name in ("ce_z_bf16", "ce_z_f16"):
         x = torch.empty((N, V), dtype=dt, device=device)
         cols = uniform_labels(N)
         for r0 in range(0, N, chunk_rows):
@@ -233,7 +238,7 @@ def small_inputs(N: int, V: int, dtype: str, device="cpu", seed: int = 0, *, tea
     """
     device = torch.device(device)
     g = _gen(device, seed)
-    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
     x32 = torch.empty((N, V), dtype=torch.float32, device=device).normal_(0.0, logit_std, generator=g)
     out = {"logits": x32.to(dt), "labels": None, "mask": None, "teacher": None,
            "advantages": None, "old_noise": None, "grad_init": None}
