@@ -59,7 +59,9 @@ FKL = 4
 RKL = 8
 GRPO = 16
 ENTROPY = 32
+FDCE = 64
 ACCUMULATE = 1 << 16
+DISTILL_FLAGS = FKL | RKL | FDCE
 
 IGNORE_INDEX = -100
 
@@ -203,6 +205,9 @@ def row_values(spec: Spec, x, labels=None, teacher=None, old_logprobs=None,
         # reverse = KL(student || teacher).
         out["fkl"] = np.sum(p * (logp_t - logq), axis=-1)
         out["rkl"] = np.sum(q * (logq - logp_t), axis=-1)
+        # [#549 Loss coverage] "from-distribution cross-entropy": the cross
+        # entropy of the student against the teacher distribution.
+        out["fdce"] = -np.sum(p * logq, axis=-1)
 
     if labels is not None and old_logprobs is not None and advantages is not None:
         old = np.asarray(old_logprobs, dtype=np.float64).reshape(-1)
@@ -245,6 +250,7 @@ def loss_gradients_wrt_s(spec: Spec, vals: dict) -> dict:
       CE:   q - onehot(y)
       z:    2 * lse * q
       FKL:  q - p
+      FDCE: q - p          (the teacher entropy does not depend on the student)
       RKL:  q * (log q - log p - RKL)
       GRPO: -act * A * r * (onehot(y) - q)      (d logp_y / ds = onehot - q)
     """
@@ -255,7 +261,7 @@ def loss_gradients_wrt_s(spec: Spec, vals: dict) -> dict:
         g["ce"] = q - _onehot(vals["y"], V)
     if spec.has(ZLOSS):
         g["z"] = 2.0 * vals["lse"][:, None] * q
-    if spec.has(FKL):
+    if spec.has(FKL) or spec.has(FDCE):
         g["distill"] = q - vals["p"]
     if spec.has(RKL):
         g["distill"] = q * (vals["logq"] - vals["logp_t"] - vals["rkl"][:, None])
@@ -266,11 +272,11 @@ def loss_gradients_wrt_s(spec: Spec, vals: dict) -> dict:
 
 
 def _check_inputs(spec: Spec, labels, teacher, old_logprobs, advantages):
-    if spec.has(FKL) and spec.has(RKL):
-        raise ValueError("at most one distillation direction per plan")
+    if bin(spec.flags & DISTILL_FLAGS).count("1") > 1:
+        raise ValueError("at most one distillation loss per plan")
     if (spec.has(CE) or spec.has(GRPO)) and labels is None:
         raise ValueError("CE and GRPO need labels")
-    if (spec.has(FKL) or spec.has(RKL)) and teacher is None:
+    if (spec.flags & DISTILL_FLAGS) and teacher is None:
         raise ValueError("distillation needs teacher logits")
     if spec.has(GRPO) and (old_logprobs is None or advantages is None):
         raise ValueError("GRPO needs old_logprobs and advantages")
@@ -339,6 +345,8 @@ def scalars_from_rows(spec: Spec, vals: dict, valid: np.ndarray, bad: np.ndarray
         out[SLOT["DISTILL"]] = mean("fkl")
     if spec.has(RKL):
         out[SLOT["DISTILL"]] = mean("rkl")
+    if spec.has(FDCE):
+        out[SLOT["DISTILL"]] = mean("fdce")
     if spec.has(GRPO):
         out[SLOT["GRPO"]] = mean("grpo")
         out[SLOT["NEWLOGP"]] = mean("logp")
@@ -392,6 +400,7 @@ READINGS = {
     "temperature": "The temperature divides the teacher logits only, with no tau**2 factor.",
     "teacher_transform": "Logit scale and softcap apply to the student only.",
     "kl_direction": "Forward KL = KL(teacher || student); reverse KL = KL(student || teacher).",
+    "fdce": "From-distribution cross-entropy = -sum_j p_j log q_j with the tempered teacher p; gradient q - p.",
     "grpo": "Per-token PPO-clip with symmetric eps, no KL penalty, loss = -objective, mean over valid tokens.",
     "grpo_ties": "At r exactly 1 +/- eps the gradient flows (clip only on a strict inequality).",
     "clip_stat": "CLIPFRAC = mean of [|r - 1| > eps].",

@@ -155,6 +155,27 @@ def test_kl_vs_torch_kl_div(tau):
     np.testing.assert_allclose(vals["rkl"], rkl, rtol=1e-11, atol=1e-14)
 
 
+@pytest.mark.parametrize("tau", [1.0, 2.0])
+def test_fdce_vs_torch_soft_target_cross_entropy(tau):
+    """From-distribution CE: torch's cross_entropy with probability targets,
+    and the identity FDCE = FKL + H(teacher) with H from Categorical."""
+    rng = _rng(19)
+    N, V = 6, 43
+    t = rng.normal(0, 3.0, size=(N, V))
+    x = 0.8 * t + rng.normal(0, 1.0, size=(N, V))
+    spec = Spec(V=V, flags=oracle.FDCE, w_ce=0.0, w_distill=0.7, temperature=tau, grad_scale=0.3)
+    sc, grad = oracle.forward_backward(spec, x, teacher=t)
+    p = torch.softmax(torch.tensor(t) / tau, -1)
+    xt = torch.tensor(x, requires_grad=True)
+    ce = F.cross_entropy(xt, p, reduction="mean")
+    (0.3 * 0.7 * ce).backward()
+    assert sc[SLOT["DISTILL"]] == pytest.approx(ce.item(), rel=1e-12)
+    np.testing.assert_allclose(grad, xt.grad.numpy(), atol=1e-15, rtol=1e-11)
+    vals = ho.row_values(spec, x, teacher=t)
+    h_t = torch.distributions.Categorical(probs=p).entropy().numpy()
+    np.testing.assert_allclose(vals["fdce"], vals["fkl"] + h_t, rtol=1e-12)
+
+
 def test_newlogp_vs_torch_log_softmax():
     rng = _rng(4)
     N, V = 11, 29
@@ -190,12 +211,14 @@ def _torch_total(spec, x, y, mask, t, old, adv):
         total = total + spec.w_ce * F.cross_entropy(sv, yv[valid], reduction="sum") / n
     if spec.flags & oracle.ZLOSS:
         total = total + spec.w_z * (torch.logsumexp(sv, -1) ** 2).sum() / n
-    if spec.flags & (oracle.FKL | oracle.RKL):
+    if spec.flags & oracle.DISTILL_FLAGS:
         logp = torch.log_softmax(torch.tensor(t)[valid] / spec.temperature, -1)
         if spec.flags & oracle.FKL:
             kl = F.kl_div(logq, logp, log_target=True, reduction="sum")
-        else:
+        elif spec.flags & oracle.RKL:
             kl = F.kl_div(logp, logq, log_target=True, reduction="sum")
+        else:
+            kl = F.cross_entropy(sv, logp.exp(), reduction="sum")
         total = total + spec.w_distill * kl / n
     if spec.flags & oracle.GRPO:
         lp = logq.gather(-1, yv[valid][:, None])[:, 0]
@@ -207,7 +230,7 @@ def _torch_total(spec, x, y, mask, t, old, adv):
     return xt.grad.numpy()
 
 
-@pytest.mark.parametrize("mode", ["fkl", "rkl"])
+@pytest.mark.parametrize("mode", ["fkl", "rkl", "fdce"])
 @pytest.mark.parametrize("softcap", [0.0, 4.0])
 def test_total_gradient_vs_torch_autograd(mode, softcap):
     rng = _rng(5)
@@ -219,7 +242,7 @@ def test_total_gradient_vs_torch_autograd(mode, softcap):
     mask = np.ones(N, dtype=np.uint8)
     mask[5] = 0
     flags = oracle.CE | oracle.ZLOSS | oracle.GRPO | oracle.ENTROPY
-    flags |= oracle.FKL if mode == "fkl" else oracle.RKL
+    flags |= {"fkl": oracle.FKL, "rkl": oracle.RKL, "fdce": oracle.FDCE}[mode]
     spec = Spec(V=V, flags=flags, w_ce=1.0, w_z=0.3, w_distill=0.5, w_grpo=0.8,
                 grad_scale=0.25, temperature=1.5, eps=0.2, logit_scale=0.5,
                 softcap=softcap)
@@ -245,7 +268,7 @@ def _fd_check(spec, x, y, mask, t, old, adv, h=1e-6, tol=2e-8):
     np.testing.assert_allclose(grad, fd, atol=tol, rtol=0)
 
 
-@pytest.mark.parametrize("mode", ["fkl", "rkl"])
+@pytest.mark.parametrize("mode", ["fkl", "rkl", "fdce"])
 @pytest.mark.parametrize("softcap,scale", [(0.0, 1.0), (2.5, 0.7)])
 def test_finite_differences_all_losses(mode, softcap, scale):
     rng = _rng(6)
@@ -253,7 +276,7 @@ def test_finite_differences_all_losses(mode, softcap, scale):
     t = rng.normal(0, 2.0, size=(N, V))
     x = rng.normal(0, 2.0, size=(N, V))
     y = rng.integers(0, V, size=N)
-    flags = ALL_LOSSES | (oracle.FKL if mode == "fkl" else oracle.RKL)
+    flags = ALL_LOSSES | {"fkl": oracle.FKL, "rkl": oracle.RKL, "fdce": oracle.FDCE}[mode]
     spec = Spec(V=V, flags=flags, w_ce=0.9, w_z=0.2, w_distill=0.6, w_grpo=1.1,
                 grad_scale=0.5, temperature=1.7, eps=0.2, logit_scale=scale,
                 softcap=softcap)
