@@ -27,7 +27,7 @@ import workloads  # noqa: E402
 METRIC = "tokens/s + achieved HBM GB/s (% peak), CE+z+GRPO+entropy, V=151936 bf16, 1 GPU"
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, vendor figure
 FUSED_KERNEL = "fused_kernel"
-LOSS_NAMES = {1: "CE", 2: "z", 4: "FKL", 8: "RKL", 16: "GRPO", 32: "entropy"}
+LOSS_NAMES = {1: "CE", 2: "z", 4: "FKL", 8: "RKL", 64: "FDCE", 16: "GRPO", 32: "entropy"}
 
 
 def log(msg):
@@ -216,7 +216,7 @@ def main(argv=None):
             if not (w.flags & bit):
                 continue
             kw = plan_kwargs(w)
-            keep = {1: "ce", 2: "z", 4: "distill", 8: "distill", 16: "grpo"}.get(bit)
+            keep = {1: "ce", 2: "z", 4: "distill", 8: "distill", 64: "distill", 16: "grpo"}.get(bit)
             for key in ("ce", "z", "distill", "grpo"):
                 if key != keep:
                     kw[key] = 0.0

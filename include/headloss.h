@@ -52,9 +52,9 @@ typedef enum {
  * (#558 Validation); an fp16 gradient underflows below 6e-8 (use grad_scale). */
 typedef enum { HL_F32 = 0, HL_BF16 = 1, HL_F16 = 2 } hl_dtype;
 
-/* Loss and metric flags (#507 Proposed direction: "a config / flag-set
- * describing which losses and metrics to emit"). At most one distillation
- * direction per plan (#558 What it does: at most one of each kind). */
+/* Loss and metric flags (#507 Proposed direction: a flag set naming the
+ * losses and metrics to emit). At most one of HL_FKL, HL_RKL, HL_FDCE per plan
+ * (#558 What it does: at most one loss of each kind). */
 enum {
     HL_CE = 1u << 0,       /* label cross-entropy  -log softmax_y            */
     HL_ZLOSS = 1u << 1,    /* z-loss  (log sum_j exp s_j)^2                  */
@@ -63,6 +63,10 @@ enum {
     HL_GRPO = 1u << 4,     /* GRPO clipped objective + new-logprob/ratio/
                               clamp/KL/advantage statistics                  */
     HL_ENTROPY = 1u << 5,  /* entropy metric (no gradient)                   */
+    HL_FDCE = 1u << 6,     /* distillation, cross-entropy of the student
+                              against the teacher distribution, -sum p log q
+                              (#549 Loss coverage: from-distribution
+                              cross-entropy); gradient as HL_FKL            */
     HL_ACCUMULATE = 1u << 16 /* mode bit: add into grad_out instead of
                                 overwriting it (#558 Validation: gradient
                                 accumulation)                                */
@@ -119,7 +123,7 @@ typedef struct hl_plan_s* hl_plan_t;
  *                plan = one scale (#549 Approach: one softmax = one scale).
  *   softcap      0 = off; > 0: s = softcap * tanh(logit_scale * x / softcap).
  * Makes no HIP call. Errors: HL_ERR_INVALID_ARG (V < 1, unknown flag bits,
- * no loss flag, both HL_FKL and HL_RKL, temperature <= 0 with distillation,
+ * no loss flag, two distillation flags, temperature <= 0 with distillation,
  * eps outside (0,1) with GRPO, bad scale or softcap, non-finite weight),
  * HL_ERR_UNSUPPORTED (V too long for any kernel variant).
  */
@@ -154,7 +158,7 @@ hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t byte
  *   mask            device uint8[N] or NULL; 0 = masked token. Masking
  *                   applies to every loss and metric.
  *   teacher_logits  device [N, V], plan dtype, 16-byte aligned base, or
- *                   NULL; needed by HL_FKL / HL_RKL.
+ *                   NULL; needed by HL_FKL / HL_RKL / HL_FDCE.
  *   old_logprobs    device float[N] or NULL; needed by HL_GRPO.
  *   advantages      device float[N] (per token) or NULL; needed by HL_GRPO.
  *   grad_out        device [N, V], plan dtype, 16-byte aligned base, or NULL
@@ -195,7 +199,7 @@ const float* hl_row_values(hl_plan_t plan);
  * (the looped multi-block path of #558 Validation). A successful change
  * releases a library-owned workspace; a caller-owned one must be set again
  * with hl_plan_set_workspace before the next call (HL_ERR_WORKSPACE until
- * then). Errors: HL_ERR_INVALID_ARG (chunks < 0 or > 10),
+ * then). Errors: HL_ERR_INVALID_ARG (chunks < 0 or > 9),
  * HL_ERR_UNSUPPORTED (no variant fits V with that many chunks). */
 hl_status hl_plan_set_chunks(hl_plan_t plan, int chunks);
 

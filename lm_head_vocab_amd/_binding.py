@@ -34,6 +34,7 @@ FKL = 1 << 2
 RKL = 1 << 3
 GRPO = 1 << 4
 ENTROPY = 1 << 5
+FDCE = 1 << 6
 ACCUMULATE = 1 << 16
 
 SLOTS = ("CE", "Z", "DISTILL", "GRPO", "NEWLOGP", "RATIO", "CLIPFRAC",

@@ -71,11 +71,16 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
             const double lse = ((double)rec[R_M] + l2Z) * LN2;
             v[RC_Z] = lse * lse;
             v[RC_ENT] = LN2 * (l2Z - (double)rec[R_S] / Z);
-            if (f & (F_FKL | F_RKL)) {
+            if (f & F_DISTILL) {
                 const double Zt = rec[R_ZT];
                 const double l2Zt = log2(Zt);
-                v[RC_KL] = (f & F_FKL) ? LN2 * ((double)rec[R_SX] / Zt - l2Zt + l2Z)
-                                       : LN2 * ((double)rec[R_SX] / Z - l2Z + l2Zt);
+                if (f & F_RKL) {
+                    v[RC_KL] = LN2 * ((double)rec[R_SX] / Z - l2Z + l2Zt);
+                } else {
+                    v[RC_KL] = LN2 * ((double)rec[R_SX] / Zt - l2Zt + l2Z);      // forward KL
+                    if (f & F_FDCE)                                                 // + teacher entropy
+                        v[RC_KL] += LN2 * (l2Zt - (double)rec[R_ST] / Zt);
+                }
             }
             if (p.labels != nullptr) {
                 const double xy = rec[R_XY];
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
         double ce = 0, z = 0, kl = 0, grpo = 0;
         if (f & F_CE) { ce = sum[RC_CE] * inv; out[0] = (float)ce; }
         if (f & F_Z) { z = sum[RC_Z] * inv; out[1] = (float)z; }
-        if (f & (F_FKL | F_RKL)) { kl = sum[RC_KL] * inv; out[2] = (float)kl; }
+        if (f & F_DISTILL) { kl = sum[RC_KL] * inv; out[2] = (float)kl; }
         if (f & F_GRPO) {
             grpo = sum[RC_GRPO] * inv;
             out[3] = (float)grpo;

@@ -209,10 +209,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 // merge(a, b) == merge(b, a) bit for bit; an empty slice has Z == 0.
 // ---------------------------------------------------------------------------
 struct Rec {
-    float M, Z, S, Mt, Zt, SX;
+    float M, Z, S, Mt, Zt, SX, St;
 };
 
-__device__ __forceinline__ Rec rec_empty() { return Rec{kNegInf, 0.f, 0.f, kNegInf, 0.f, 0.f}; }
+__device__ __forceinline__ Rec rec_empty() { return Rec{kNegInf, 0.f, 0.f, kNegInf, 0.f, 0.f, 0.f}; }
 
 template <int TMODE>
 __device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b) {
@@ -231,7 +231,7 @@ __device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b) {
         const float fta = fast_exp2(dta), ftb = fast_exp2(dtb);
         r.Mt = Mt;
         r.Zt = __fadd_rn(__fmul_rn(a.Zt, fta), __fmul_rn(b.Zt, ftb));
-        if (TMODE == TM_FKL) {
+        if (fkl_like(TMODE)) {
             // SX = sum_j 2^u_j (u_j - a_j): both offsets move
             r.SX = __fadd_rn(__fmul_rn(fta, __fadd_rn(a.SX, __fmul_rn(__fsub_rn(dta, da), a.Zt))),
                              __fmul_rn(ftb, __fadd_rn(b.SX, __fmul_rn(__fsub_rn(dtb, db), b.Zt))));
@@ -240,8 +240,13 @@ __device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b) {
             r.SX = __fadd_rn(__fmul_rn(fa, __fadd_rn(a.SX, __fmul_rn(__fsub_rn(da, dta), a.Z))),
                              __fmul_rn(fb, __fadd_rn(b.SX, __fmul_rn(__fsub_rn(db, dtb), b.Z))));
         }
+        // St = sum_j 2^u_j u_j: the teacher offset moves, as S does for the student
+        r.St = (TMODE == TM_FDCE)
+                   ? __fadd_rn(__fmul_rn(fta, __fadd_rn(a.St, __fmul_rn(dta, a.Zt))),
+                               __fmul_rn(ftb, __fadd_rn(b.St, __fmul_rn(dtb, b.Zt))))
+                   : 0.f;
     } else {
-        r.Mt = 0.f; r.Zt = 0.f; r.SX = 0.f;
+        r.Mt = 0.f; r.Zt = 0.f; r.SX = 0.f; r.St = 0.f;
     }
     if (ea) r = b;
     if (eb) r = a;
@@ -258,8 +263,9 @@ __device__ __forceinline__ Rec rec_dpp_step(const Rec& a) {
         b.Mt = dpp<CTRL>(a.Mt);
         b.Zt = dpp<CTRL>(a.Zt);
         b.SX = dpp<CTRL>(a.SX);
+        b.St = (TMODE == TM_FDCE) ? dpp<CTRL>(a.St) : 0.f;
     } else {
-        b.Mt = 0.f; b.Zt = 0.f; b.SX = 0.f;
+        b.Mt = 0.f; b.Zt = 0.f; b.SX = 0.f; b.St = 0.f;
     }
     return rec_merge<TMODE>(a, b);
 }
@@ -431,8 +437,8 @@ void fused_kernel(const FusedParams p) {
     if (TMODE != TM_NONE) Mt = wave_max(mt) * p.K2;
 
     // ---- pass 1b: sums relative to the wave shift, in the log2 domain ----
-    float Z = 0.f, S = 0.f, Zt = 0.f, SX = 0.f;
-    auto accumulate = [&](float x, float t, float& z, float& s, float& zt, float& sx) {
+    float Z = 0.f, S = 0.f, Zt = 0.f, SX = 0.f, St = 0.f;
+    auto accumulate = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st) {
         const float a = SOFTCAP ? fmaf(p.cap * hl_tanh(x * p.kc), kLog2e, -M) : fmaf(x, p.K1, -M);
         const float ex = fast_exp2(a);
         z += ex;
@@ -441,21 +447,22 @@ void fused_kernel(const FusedParams p) {
             const float u = fmaf(t, p.K2, -Mt);
             const float et = fast_exp2(u);
             zt += et;
-            if (TMODE == TM_FKL) sx = fmaf(et, u - a, sx);
+            if (fkl_like(TMODE)) sx = fmaf(et, u - a, sx);
             else sx = fmaf(ex, a - u, sx);
+            if (TMODE == TM_FDCE) st = fmaf(et, u, st);
         }
     };
 #pragma unroll
     for (int v = 0; v < NVEC; ++v) {
         if (tid < nv - v * BLOCK) {
-            float z = 0.f, s = 0.f, zt = 0.f, sx = 0.f;
+            float z = 0.f, s = 0.f, zt = 0.f, sx = 0.f, st = 0.f;
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
-                accumulate(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z, s, zt, sx);
-            Z += z; S += s; Zt += zt; SX += sx;
+                accumulate(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z, s, zt, sx, st);
+            Z += z; S += s; Zt += zt; SX += sx; St += st;
         }
     }
-    if (has_e) accumulate(xe, te, Z, S, Zt, SX);
+    if (has_e) accumulate(xe, te, Z, S, Zt, SX, St);
 
     Z = wave_sum(Z);
     S = wave_sum(S);
@@ -463,6 +470,7 @@ void fused_kernel(const FusedParams p) {
         Zt = wave_sum(Zt);
         SX = wave_sum(SX);
     }
+    if (TMODE == TM_FDCE) St = wave_sum(St);
     if (lane == 0) {
         s_rec[wave][0] = M;
         s_rec[wave][1] = Z;
@@ -470,6 +478,7 @@ void fused_kernel(const FusedParams p) {
         s_rec[wave][3] = Mt;
         s_rec[wave][4] = Zt;
         s_rec[wave][5] = SX;
+        s_rec[wave][6] = St;
     }
     __syncthreads();
 
@@ -481,9 +490,12 @@ void fused_kernel(const FusedParams p) {
             r.M = s_rec[w][0];
             r.Z = s_rec[w][1];
             r.S = s_rec[w][2];
-            r.Mt = s_rec[w][3];
-            r.Zt = s_rec[w][4];
-            r.SX = s_rec[w][5];
+            if (TMODE != TM_NONE) {
+                r.Mt = s_rec[w][3];
+                r.Zt = s_rec[w][4];
+                r.SX = s_rec[w][5];
+                if (TMODE == TM_FDCE) r.St = s_rec[w][6];
+            }
             if (r.Z == 0.f) r = rec_empty();
         }
         r = rec_reduce16<TMODE>(r);
@@ -498,22 +510,26 @@ void fused_kernel(const FusedParams p) {
     // one load per lane per round, then merges the C records with the same
     // fixed DPP tree in every workgroup of the row.
     if (p.chunks > 1) {
+        // statistics this mode exchanges: M, Z, S (+ Mt, Zt, SX (+ St))
+        constexpr int NXW = TMODE == TM_NONE ? 3 : (TMODE == TM_FDCE ? 7 : 6);
         const uint64_t epoch = (uint64_t)p.ctrl[CTRL_EPOCH] << 32;
         uint64_t* words = p.chunk_words + (int64_t)row * p.chunks * XWORDS;
         if (tid == 0) {
             uint64_t* mine = words + c * XWORDS;
-            const float f[XWORDS] = {r.M, r.Z, r.S, r.Mt, r.Zt, r.SX};
+            const float f[XWORDS] = {r.M, r.Z, r.S, r.Mt, r.Zt, r.SX, r.St};
 #pragma unroll
-            for (int i = 0; i < XWORDS; ++i)
+            for (int i = 0; i < NXW; ++i)
                 __hip_atomic_store(mine + i, epoch | __float_as_uint(f[i]), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
         if (wave == 0) {
-            const int nwords = p.chunks * XWORDS;
+            // lane l polls word (l % NXW) of chunk (l / NXW)
+            const int nwords = p.chunks * NXW;
+            const int lw = (lane / NXW) * XWORDS + lane % NXW;
             uint64_t w = 0;
             uint32_t spins = 0;
             while (true) {
-                if (lane < nwords) w = __hip_atomic_load(words + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (lane < nwords) w = __hip_atomic_load(words + lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const bool ok = (lane >= nwords) || ((w & 0xffffffff00000000ull) == epoch);
                 if (__all(ok)) break;
                 __builtin_amdgcn_s_sleep(1);
@@ -528,26 +544,30 @@ void fused_kernel(const FusedParams p) {
             const int l = lane & 15;
             Rec cr = rec_empty();
             if (l < p.chunks) {
-                cr.M = s_xw[l * XWORDS + 0]; cr.Z = s_xw[l * XWORDS + 1]; cr.S = s_xw[l * XWORDS + 2];
-                cr.Mt = s_xw[l * XWORDS + 3]; cr.Zt = s_xw[l * XWORDS + 4]; cr.SX = s_xw[l * XWORDS + 5];
+                cr.M = s_xw[l * NXW + 0]; cr.Z = s_xw[l * NXW + 1]; cr.S = s_xw[l * NXW + 2];
+                if (TMODE != TM_NONE) {
+                    cr.Mt = s_xw[l * NXW + 3]; cr.Zt = s_xw[l * NXW + 4]; cr.SX = s_xw[l * NXW + 5];
+                    if (TMODE == TM_FDCE) cr.St = s_xw[l * NXW + 6];
+                }
                 if (cr.Z == 0.f) cr = rec_empty();
             }
             cr = rec_reduce16<TMODE>(cr);
             if (lane == 0) {
                 s_fin[0] = cr.M; s_fin[1] = cr.Z; s_fin[2] = cr.S;
-                s_fin[3] = cr.Mt; s_fin[4] = cr.Zt; s_fin[5] = cr.SX;
+                s_fin[3] = cr.Mt; s_fin[4] = cr.Zt; s_fin[5] = cr.SX; s_fin[6] = cr.St;
             }
         }
         __syncthreads();
         r.M = s_fin[0]; r.Z = s_fin[1]; r.S = s_fin[2];
-        r.Mt = s_fin[3]; r.Zt = s_fin[4]; r.SX = s_fin[5];
+        r.Mt = s_fin[3]; r.Zt = s_fin[4]; r.SX = s_fin[5]; r.St = s_fin[6];
     }
 
     // ---- per-row record for the batch reduction ----
     if (c == 0 && tid == 0) {
         float* out = p.row_rec + row * REC;
         out[R_M] = r.M; out[R_Z] = r.Z; out[R_S] = r.S;
-        out[R_MT] = r.Mt; out[R_ZT] = r.Zt; out[R_SX] = r.SX;
+        out[R_MT] = r.Mt; out[R_ZT] = r.Zt; out[R_SX] = r.SX; out[R_ST] = r.St;
+        out[R_PAD] = 0.0f;
         out[R_XY] = s_row[0];
         out[R_VALID] = 1.0f;
     }
@@ -584,8 +604,8 @@ void fused_kernel(const FusedParams p) {
     if ((f & F_CE) && p.w_ce != 0.f) { P += p.w_ce; L += p.w_ce; }
     if ((f & F_Z) && p.w_z != 0.f) P += 2.f * p.w_z * lse;
     if ((f & F_GRPO) && p.w_g != 0.f) { P += p.w_g * a_g; L += p.w_g * a_g; }
-    if ((f & (F_FKL | F_RKL)) && p.w_d != 0.f) wd = p.w_d;
-    if (TMODE == TM_FKL) P += wd;
+    if ((f & F_DISTILL) && p.w_d != 0.f) wd = p.w_d;
+    if (fkl_like(TMODE)) P += wd;
     const float alpha = scale * P;             // prob_coeff (times G k / n)
     const float beta = scale * L;              // label_coeff
     const float gam = scale * wd;              // forward-KL teacher coefficient
@@ -606,7 +626,7 @@ void fused_kernel(const FusedParams p) {
         float g;
         if (TMODE == TM_NONE) {
             g = fmaf(alpha, q, -lab);
-        } else if (TMODE == TM_FKL) {
+        } else if (fkl_like(TMODE)) {
             const float pt = fast_exp2(fmaf(t, p.K2, -Bt2));
             g = fmaf(alpha, q, fmaf(-gam, pt, -lab));
         } else {

@@ -45,7 +45,8 @@ hl_status hip_fail(const char* where, hipError_t e) {
     return HL_ERR_HIP;
 }
 
-constexpr uint32_t kLossBits = HL_CE | HL_ZLOSS | HL_FKL | HL_RKL | HL_GRPO | HL_ENTROPY;
+constexpr uint32_t kDistillBits = HL_FKL | HL_RKL | HL_FDCE;
+constexpr uint32_t kLossBits = HL_CE | HL_ZLOSS | kDistillBits | HL_GRPO | HL_ENTROPY;
 constexpr uint32_t kKnownBits = kLossBits | HL_ACCUMULATE;
 constexpr int kTwoPerCuNvec = 10;         // 64 VGPRs at 1024 threads: two workgroups per CU
 constexpr int kTwoPerCuNvecSoftcap = 8;   // the softcap instances need a few more registers
@@ -77,6 +78,11 @@ int round_up_to(const int* set, int n_set, int need) {
 }
 
 FusedLauncher lookup(hl_dtype dt, int tmode, int block, int nvec, bool softcap) {
+    if (tmode == TM_FDCE) {
+        if (dt == HL_F32) return get_fused_f32_fdce(block, nvec, softcap);
+        if (dt == HL_F16) return get_fused_f16_fdce(block, nvec, softcap);
+        return get_fused_bf16_fdce(block, nvec, softcap);
+    }
     if (dt == HL_F32) {
         if (tmode == TM_NONE) return get_fused_f32_none(block, nvec, softcap);
         if (tmode == TM_FKL) return get_fused_f32_fkl(block, nvec, softcap);
@@ -190,8 +196,9 @@ hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags
     if (V < 1 || weights == nullptr) return HL_ERR_INVALID_ARG;
     if (dtype != HL_F32 && dtype != HL_BF16 && dtype != HL_F16) return HL_ERR_INVALID_ARG;
     if ((loss_flags & ~kKnownBits) != 0u || (loss_flags & kLossBits) == 0u) return HL_ERR_INVALID_ARG;
-    if ((loss_flags & HL_FKL) && (loss_flags & HL_RKL)) return HL_ERR_INVALID_ARG;
-    const bool distill = (loss_flags & (HL_FKL | HL_RKL)) != 0u;
+    const uint32_t dbits = loss_flags & kDistillBits;
+    if (dbits & (dbits - 1u)) return HL_ERR_INVALID_ARG;   // at most one distillation loss
+    const bool distill = dbits != 0u;
     if (distill && !(finite(temperature) && temperature > 0.f)) return HL_ERR_INVALID_ARG;
     if ((loss_flags & HL_GRPO) && !(finite(eps) && eps > 0.f && eps < 1.f)) return HL_ERR_INVALID_ARG;
     if (!(finite(logit_scale) && logit_scale > 0.f)) return HL_ERR_INVALID_ARG;
@@ -212,7 +219,9 @@ hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags
     p->eps = eps;
     p->logit_scale = logit_scale;
     p->softcap = softcap;
-    p->tmode = (loss_flags & HL_FKL) ? TM_FKL : (loss_flags & HL_RKL) ? TM_RKL : TM_NONE;
+    p->tmode = (loss_flags & HL_FKL) ? TM_FKL
+             : (loss_flags & HL_RKL) ? TM_RKL
+             : (loss_flags & HL_FDCE) ? TM_FDCE : TM_NONE;
     const hl_status st = choose(p);
     if (st != HL_OK) {
         delete p;
@@ -316,7 +325,7 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
     const uint32_t f = plan->flags;
     if (n_rows > 0) {
         if ((f & (HL_CE | HL_GRPO)) && labels == nullptr) return HL_ERR_MISSING_INPUT;
-        if ((f & (HL_FKL | HL_RKL)) && teacher_logits == nullptr) return HL_ERR_MISSING_INPUT;
+        if ((f & kDistillBits) && teacher_logits == nullptr) return HL_ERR_MISSING_INPUT;
         if ((f & HL_GRPO) && (old_logprobs == nullptr || advantages == nullptr)) return HL_ERR_MISSING_INPUT;
         if (!aligned16(logits)) return HL_ERR_INVALID_ARG;
         if (plan->tmode != TM_NONE && !aligned16(teacher_logits)) return HL_ERR_INVALID_ARG;

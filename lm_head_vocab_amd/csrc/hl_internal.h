@@ -7,12 +7,16 @@
 namespace hl {
 
 // Distillation mode baked into a kernel instance.
-enum TeacherMode : int { TM_NONE = 0, TM_FKL = 1, TM_RKL = 2 };
+enum TeacherMode : int { TM_NONE = 0, TM_FKL = 1, TM_RKL = 2, TM_FDCE = 3 };
+
+// Forward KL and from-distribution CE share the gradient q - p.
+constexpr bool fkl_like(int t) { return t == TM_FKL || t == TM_FDCE; }
 
 // Loss bits (same values as the public HL_* flags).
 enum : uint32_t {
     F_CE = 1u << 0, F_Z = 1u << 1, F_FKL = 1u << 2, F_RKL = 1u << 3,
-    F_GRPO = 1u << 4, F_ENT = 1u << 5, F_ACC = 1u << 16,
+    F_GRPO = 1u << 4, F_ENT = 1u << 5, F_FDCE = 1u << 6, F_ACC = 1u << 16,
+    F_DISTILL = F_FKL | F_RKL | F_FDCE,
 };
 
 // Per-row value columns (same order as the public HL_R_* enum).
@@ -26,17 +30,19 @@ constexpr int NSCALARS = 13;
 // Softmax statistics of a slice of one row, in the log2 domain:
 //   M  = shift, Z = sum 2^(A_j - M), S = sum 2^(A_j - M) (A_j - M)
 //   Mt, Zt = the same for the teacher, SX = the distillation cross sum.
+//   St = sum 2^(U_j - Mt) (U_j - Mt), the teacher entropy sum (FDCE only).
 // The per-row record written by the fused kernel adds the raw label logit
 // and a valid flag.
-enum RecField : int { R_M = 0, R_Z, R_S, R_MT, R_ZT, R_SX, R_XY, R_VALID, REC };
+enum RecField : int { R_M = 0, R_Z, R_S, R_MT, R_ZT, R_SX, R_ST, R_XY, R_VALID, R_PAD, REC };
 
 // Control words at the start of the workspace.
 enum Ctrl : int { CTRL_NVALID = 0, CTRL_NBAD = 1, CTRL_EPOCH = 2, CTRL_ERROR = 3, CTRL_DONE = 4, NCTRL = 64 };
 
-// Split-vocab exchange: each chunk publishes its 6 statistics as 64-bit words
+// Split-vocab exchange: each chunk publishes its 7 statistics as 64-bit words
 // (float bits low, call epoch high); at most kMaxChunks chunks per row.
-constexpr int XWORDS = 6;
-constexpr int kMaxChunks = 10;
+constexpr int XWORDS = 7;
+constexpr int kMaxChunks = 9;
+static_assert(kMaxChunks * XWORDS <= 64, "one wave polls every exchanged word of a row");
 
 struct Geometry {
     int chunks;      // workgroups per row
@@ -116,6 +122,9 @@ FusedLauncher get_fused_bf16_rkl(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f16_none(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f16_fkl(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f16_rkl(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f32_fdce(int block, int nvec, bool softcap);
+FusedLauncher get_fused_bf16_fdce(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f16_fdce(int block, int nvec, bool softcap);
 
 hipError_t launch_count(const CountParams& p, hipStream_t s);  // grid grows when p.fresh
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);

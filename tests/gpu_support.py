@@ -128,7 +128,7 @@ def scalar_errors(spec, got, ref, vals=None, valid=None):
         denom = abs(r)
         key = NEAR_ZERO_SLOTS.get(name, "missing")
         if key == "distill" and vals is not None:
-            key = "fkl" if spec.has(oracle.FKL) else "rkl"
+            key = "fkl" if spec.has(oracle.FKL) else ("rkl" if spec.has(oracle.RKL) else "fdce")
         if vals is not None and valid is not None and key not in (None, "missing") and key in vals:
             denom = max(denom, float(np.mean(np.abs(vals[key][valid]))) if valid.any() else 0.0)
         if key != "missing":

@@ -45,6 +45,9 @@ def test_status_strings():
     (dict(flags=hl.ACCUMULATE), hl.HL_ERR_INVALID_ARG),
     (dict(flags=1 << 9), hl.HL_ERR_INVALID_ARG),
     (dict(flags=hl.FKL | hl.RKL), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.FKL | hl.FDCE), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.RKL | hl.FDCE), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.FDCE, tau=0.0), hl.HL_ERR_INVALID_ARG),
     (dict(flags=hl.FKL, tau=0.0), hl.HL_ERR_INVALID_ARG),
     (dict(flags=hl.RKL, tau=-1.0), hl.HL_ERR_INVALID_ARG),
     (dict(flags=hl.RKL, tau=math.inf), hl.HL_ERR_INVALID_ARG),
@@ -59,6 +62,7 @@ def test_status_strings():
     (dict(w=Weights(math.nan, 0, 0, 0, 1, 0)), hl.HL_ERR_INVALID_ARG),
     (dict(w=Weights(1, 0, 0, 0, math.inf, 0)), hl.HL_ERR_INVALID_ARG),
     (dict(V=10**9), hl.HL_ERR_UNSUPPORTED),
+    (dict(V=1_500_000), hl.HL_ERR_UNSUPPORTED),
 ])
 def test_plan_rejects(kwargs, status):
     st, h = _plan(**kwargs)
@@ -75,7 +79,9 @@ def test_plan_accepts_and_describes_the_baseline_shapes():
         (151936, hl.HL_BF16, hl.GRPO | hl.ZLOSS | hl.ENTROPY, 2, 1024),
         (60000, hl.HL_BF16, hl.CE, 1, 1024),
         (256000, hl.HL_BF16, hl.CE | hl.ZLOSS | hl.RKL | hl.GRPO | hl.ENTROPY | hl.ACCUMULATE, 7, 512),
-        (1_500_000, hl.HL_BF16, hl.CE, 10, 1024),
+        (1_400_000, hl.HL_BF16, hl.CE, 9, 1024),
+        (151936, hl.HL_BF16, hl.CE | hl.FDCE, 4, 512),
+        (151936, hl.HL_F16, hl.CE | hl.ZLOSS, 2, 1024),
     ]
     for V, dt, flags, chunks, block in cases:
         st, h = _plan(V=V, dtype=dt, flags=flags, cap=30.0 if V == 256000 else 0.0)
@@ -95,7 +101,7 @@ def test_set_chunks_and_errors():
     st, h = _plan(V=20000)
     assert st == 0
     assert lib.hl_plan_set_chunks(h, -1) == hl.HL_ERR_INVALID_ARG
-    assert lib.hl_plan_set_chunks(h, 11) == hl.HL_ERR_INVALID_ARG
+    assert lib.hl_plan_set_chunks(h, 10) == hl.HL_ERR_INVALID_ARG
     assert lib.hl_plan_set_variant(h, 2, 300) == hl.HL_ERR_INVALID_ARG
     assert lib.hl_plan_set_variant(h, 0, 512) == hl.HL_ERR_INVALID_ARG
     assert lib.hl_plan_set_chunks(h, 3) == hl.HL_OK

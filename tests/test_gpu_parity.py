@@ -37,6 +37,8 @@ F16_LOSS_SCALE = 1024.0
 
 CE, Z, FKL, RKL, GRPO, ENT, ACC = (oracle.CE, oracle.ZLOSS, oracle.FKL, oracle.RKL, oracle.GRPO,
                                    oracle.ENTROPY, oracle.ACCUMULATE)
+FDCE = oracle.FDCE
+DISTILL = FKL | RKL | FDCE
 
 COMBOS = {
     "ce": (CE, dict(ce=1.0)),
@@ -48,6 +50,8 @@ COMBOS = {
     "fkl_ent": (FKL | ENT, dict(ce=0.0, distill=1.0)),
     "all_rkl": (CE | Z | RKL | GRPO | ENT, dict(ce=1.0, z=1e-3, distill=0.5, grpo=1.0, grad_scale=0.25)),
     "all_fkl": (CE | Z | FKL | GRPO | ENT, dict(ce=0.7, z=1e-2, distill=0.9, grpo=0.6, grad_scale=2.0)),
+    "ce_fdce": (CE | FDCE, dict(ce=0.5, distill=1.0)),
+    "all_fdce": (CE | Z | FDCE | GRPO | ENT, dict(ce=0.3, z=1e-3, distill=1.1, grpo=0.8, grad_scale=0.5)),
 }
 # (N, V): aligned and ragged rows, tiny rows, both block sizes
 SHAPES = [(37, 1000), (16, 4099), (9, 33000), (5, 3), (3, 1), (64, 300), (11, 2053)]
@@ -70,7 +74,7 @@ def _small(dtype, combo, N, V, seed, softcap=0.0, scale=1.0, accumulate=False, t
     if accumulate:
         flags |= ACC
     spec = spec_from(V, flags, w, temperature=temperature, eps=0.2, logit_scale=scale, softcap=softcap)
-    inp = workloads.small_inputs(N, V, dtype, "cpu", seed, teacher=bool(flags & (FKL | RKL)),
+    inp = workloads.small_inputs(N, V, dtype, "cpu", seed, teacher=bool(flags & DISTILL),
                                  grpo=bool(flags & GRPO), accumulate=accumulate,
                                  logit_std=logit_std, **gen)
     if flags & GRPO:
@@ -126,14 +130,14 @@ def test_small_parity(dtype, combo, shape):
 
 
 @pytest.mark.parametrize("logit_std", [2.0, 40.0], ids=["poly", "exp_branch"])
-@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "grpo_z_ent"])
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "grpo_z_ent", "all_fdce"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_softcap_and_scale(dtype, combo, logit_std):
     spec, inp = _small(dtype, combo, 24, 2053, seed=7, softcap=7.0, scale=0.5, logit_std=logit_std)
     _check_small(spec, inp, dtype)
 
 
-@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "z_ent"])
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "z_ent", "all_fdce"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("V", [1000, 20011])
 def test_accumulate(dtype, combo, V):
@@ -151,8 +155,8 @@ def test_forward_only_matches_and_writes_nothing(dtype, combo):
     np.testing.assert_array_equal(sc_fo, sc_full)
 
 
-@pytest.mark.parametrize("chunks", [2, 3, 5])
-@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "ce_fkl"])
+@pytest.mark.parametrize("chunks", [2, 3, 5, 9])
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "ce_fkl", "all_fdce"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_split_vocab_variant(dtype, combo, chunks):
     # forced chunking exercises the cross-workgroup combine at small sizes
@@ -184,7 +188,7 @@ def test_forced_variants(combo, variant):
 
 
 @pytest.mark.parametrize("chunks", [0, 3])
-@pytest.mark.parametrize("combo", ["all_rkl", "all_fkl"])
+@pytest.mark.parametrize("combo", ["all_rkl", "all_fkl", "all_fdce"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_per_token_values(dtype, combo, chunks):
     """hl_row_values: every per-token column (CE, z, KL, GRPO objective, new
@@ -200,7 +204,7 @@ def test_per_token_values(dtype, combo, chunks):
     valid, _ = oracle.row_validity(N, spec.V, y, to_np(inp["mask"]))
     vals = oracle.row_values(spec, to_np(inp["logits"]), y, to_np(inp["teacher"]),
                              to_np(inp["old_logprobs"]), to_np(inp["advantages"]))
-    kl = "fkl" if spec.has(FKL) else "rkl"
+    kl = "fkl" if spec.has(FKL) else ("rkl" if spec.has(RKL) else "fdce")
     rel = TOL[dtype]["scalar_rel"]
     np.testing.assert_array_equal(rv[:, 10], valid.astype(float))
     assert np.all(rv[~valid] == 0.0)
@@ -290,7 +294,7 @@ def test_bitwise_determinism():
         assert torch.equal(rv1, plan.row_values())
 
 
-@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl"])
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "all_fdce"])
 def test_fused_equals_separate_passes(combo):
     """The per-loss loop (one single-loss plan per loss, accumulating into one
     fp32 buffer) equals the fused pass up to rounding (fp32 inputs)."""
@@ -299,7 +303,7 @@ def test_fused_equals_separate_passes(combo):
     fused = make_plan(spec, torch.float32)
     sc_f, g_f = run_hip(fused, d, "overwrite")
     weights = {CE: ("ce", spec.w_ce), Z: ("z", spec.w_z), FKL: ("distill", spec.w_distill),
-               RKL: ("distill", spec.w_distill), GRPO: ("grpo", spec.w_grpo)}
+               RKL: ("distill", spec.w_distill), FDCE: ("distill", spec.w_distill), GRPO: ("grpo", spec.w_grpo)}
     g = torch.zeros_like(d["logits"])
     first = True
     for flag, (key, wv) in weights.items():
@@ -320,7 +324,7 @@ def test_fused_equals_separate_passes(combo):
 # The benchmark configurations at full size
 # ---------------------------------------------------------------------------
 FULL = ["ce_z_tiny_f32", "ce_z_bf16", "ce_fkl_bf16", "ce_rkl_bf16", "grpo_z_ent_bf16", "all_combined_bf16",
-        "ce_z_f16"]
+        "ce_z_f16", "ce_fdce_bf16"]
 
 
 def _full_inputs(name):
@@ -358,7 +362,7 @@ def test_full_config_sampled(name):
     n = spec.divisor if spec.divisor > 0 else n_valid
     cols = {"CE": 0, "Z": 1, "DISTILL": 2, "GRPO": 3, "NEWLOGP": 4, "RATIO": 5, "CLIPFRAC": 6,
             "KL_OLD_NEW": 7, "ADV_MEAN": 8, "ENTROPY": 9}
-    enabled = {"CE": CE, "Z": Z, "DISTILL": FKL | RKL, "GRPO": GRPO, "NEWLOGP": GRPO, "RATIO": GRPO,
+    enabled = {"CE": CE, "Z": Z, "DISTILL": DISTILL, "GRPO": GRPO, "NEWLOGP": GRPO, "RATIO": GRPO,
                "CLIPFRAC": GRPO, "KL_OLD_NEW": GRPO, "ADV_MEAN": GRPO, "ENTROPY": ENT}
     for sname, c in cols.items():
         expect = rows_val[:, c].sum() / n if (spec.flags & enabled[sname]) else 0.0
@@ -385,6 +389,8 @@ def test_full_config_sampled(name):
         checks.append(("fkl", 2, FKL))
     if spec.has(RKL):
         checks.append(("rkl", 2, RKL))
+    if spec.has(FDCE):
+        checks.append(("fdce", 2, FDCE))
     for key, c, flag in checks:
         if not spec.has(flag):
             continue
