@@ -32,6 +32,11 @@ of the named quantity, and each reading of an open point is listed in the
   delta(j, label); z-loss adds to prob_coeff only; CE and GRPO share the
   label column) and Validation (masking, logit/grad scaling, gradient
   accumulation, a zero-weight loss that still reports its diagnostics).
+  The same Design section lists three dispatch cases; in the GSPO case a
+  per-segment step runs between the forward and a backward that reloads the
+  logits, and hands that backward a per-token coefficient on the shared
+  label column. The pages name GSPO without a formula; ``gspo_seam`` follows
+  the published sequence-level definition (READINGS["gspo"]).
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``
 (closed forms, a hand-worked example in ``tests/golden/``, torch library
@@ -60,8 +65,10 @@ RKL = 8
 GRPO = 16
 ENTROPY = 32
 FDCE = 64
+GSPO = 128
 ACCUMULATE = 1 << 16
 DISTILL_FLAGS = FKL | RKL | FDCE
+POLICY_FLAGS = GRPO | GSPO
 
 IGNORE_INDEX = -100
 
@@ -274,25 +281,107 @@ def loss_gradients_wrt_s(spec: Spec, vals: dict) -> dict:
 def _check_inputs(spec: Spec, labels, teacher, old_logprobs, advantages):
     if bin(spec.flags & DISTILL_FLAGS).count("1") > 1:
         raise ValueError("at most one distillation loss per plan")
-    if (spec.has(CE) or spec.has(GRPO)) and labels is None:
-        raise ValueError("CE and GRPO need labels")
+    if spec.has(GRPO) and spec.has(GSPO):
+        raise ValueError("at most one policy loss per plan")
+    if (spec.flags & (CE | POLICY_FLAGS)) and labels is None:
+        raise ValueError("CE, GRPO and GSPO need labels")
     if (spec.flags & DISTILL_FLAGS) and teacher is None:
         raise ValueError("distillation needs teacher logits")
-    if spec.has(GRPO) and (old_logprobs is None or advantages is None):
-        raise ValueError("GRPO needs old_logprobs and advantages")
+    if (spec.flags & POLICY_FLAGS) and (old_logprobs is None or advantages is None):
+        raise ValueError("GRPO and GSPO need old_logprobs and advantages")
+
+
+# ---------------------------------------------------------------------------
+# GSPO: the per-segment step between the forward and the backward
+# ---------------------------------------------------------------------------
+def segment_of_rows(offsets, n_rows: int) -> np.ndarray:
+    """Row -> segment index for contiguous segments [o_i, o_{i+1}).
+
+    ``offsets`` has S+1 entries, starts at 0, never decreases and ends at the
+    row count (READINGS["segments"]); an empty segment (o_i == o_{i+1}) owns
+    no row.
+    """
+    o = np.asarray(offsets, dtype=np.int64).reshape(-1)
+    if o.size < 2 or o[0] != 0 or o[-1] != n_rows or np.any(np.diff(o) < 0):
+        raise ValueError("segment offsets must run from 0 to n_rows without decreasing")
+    seg = np.empty(n_rows, dtype=np.int64)
+    for i in range(o.size - 1):
+        seg[o[i]:o[i + 1]] = i
+    return seg
+
+
+def gspo_seam(spec: Spec, logp, old_logprobs, advantages, valid, offsets) -> dict:
+    """Per-segment GSPO values and d(batch GSPO loss)/d(logp_t) per row.
+
+    For segment i with valid tokens T_i (n_i = |T_i| > 0), READINGS["gspo"]:
+      log s_i = (1/n_i) sum_{t in T_i} (logp_t - old_t)      (length-normalised
+                                                               sequence ratio)
+      A_i     = (1/n_i) sum_{t in T_i} A_t                   (READINGS["gspo_adv"])
+      loss_i  = -min(s_i A_i, clip(s_i, 1-eps, 1+eps) A_i)
+    and the batch loss is the mean of loss_i over the segments with n_i > 0.
+    Its derivative with respect to logp_t (t in T_i) is -act_i A_i s_i /
+    (n_i n_seg), act_i as for the per-token clip (READINGS["grpo_ties"]).
+    Segments with no valid token contribute nothing and are not counted.
+    """
+    logp = np.asarray(logp, dtype=np.float64).reshape(-1)
+    old = np.asarray(old_logprobs, dtype=np.float64).reshape(-1)
+    A = np.asarray(advantages, dtype=np.float64).reshape(-1)
+    valid = np.asarray(valid, dtype=bool).reshape(-1)
+    N = logp.size
+    seg = segment_of_rows(offsets, N)
+    S = len(offsets) - 1
+    eps = spec.eps
+    n_i = np.zeros(S, dtype=np.int64)
+    sum_d = np.zeros(S)
+    sum_a = np.zeros(S)
+    for t in range(N):
+        if valid[t]:
+            i = seg[t]
+            n_i[i] += 1
+            sum_d[i] += logp[t] - old[t]
+            sum_a[i] += A[t]
+    nonempty = n_i > 0
+    n_seg = int(nonempty.sum())
+    safe_n = np.where(nonempty, n_i, 1)
+    log_s = np.where(nonempty, sum_d / safe_n, 0.0)
+    ratio = np.exp(log_s)
+    adv = np.where(nonempty, sum_a / safe_n, 0.0)
+    loss = -np.minimum(ratio * adv, np.clip(ratio, 1.0 - eps, 1.0 + eps) * adv)
+    active = ~(((adv > 0) & (ratio > 1.0 + eps)) | ((adv < 0) & (ratio < 1.0 - eps)))
+    clipped = np.abs(ratio - 1.0) > eps
+    k3 = (ratio - 1.0) - log_s
+    dlogp = np.zeros(N)
+    if n_seg > 0:
+        for t in range(N):
+            i = seg[t]
+            if valid[t] and active[i]:
+                dlogp[t] = -adv[i] * ratio[i] / (n_i[i] * n_seg)
+    z = ~nonempty
+    return {
+        "segment": seg, "n_tokens": n_i, "nonempty": nonempty, "n_seg": n_seg,
+        "log_ratio": log_s, "ratio": ratio, "adv": adv,
+        "loss": np.where(z, 0.0, loss), "active": active,
+        "clipped": clipped & nonempty, "k3": np.where(z, 0.0, k3),
+        "dlogp": dlogp,
+    }
 
 
 def rows_forward_backward(spec: Spec, x, n: float, labels=None, mask=None,
                           teacher=None, old_logprobs=None, advantages=None,
-                          grad_in=None, want_grad=True):
+                          grad_in=None, want_grad=True, gspo_dlogp=None):
     """Per-row values and gradient rows for a subset of a batch.
 
     ``n`` is the batch-level divisor (valid rows of the whole batch, or the
     caller's divisor); it is an argument so that sampled rows of a large batch
-    can be checked one by one. Returns (vals, valid, bad, grad) where grad is
-    None when ``want_grad`` is False.
+    can be checked one by one. With GSPO, ``gspo_dlogp`` is the per-row
+    derivative of the batch GSPO loss with respect to logp_t from
+    ``gspo_seam`` (it depends on whole segments, so the caller computes it).
+    Returns (vals, valid, bad, grad) where grad is None when ``want_grad`` is
+    False.
     """
     _check_inputs(spec, labels, teacher, old_logprobs, advantages)
+    if spec.has(GSPO) and want_grad and gspo_dlogp is None:
+        raise ValueError("GSPO needs the per-row derivative from gspo_seam")
     x = np.asarray(x, dtype=np.float64)
     R, V = x.shape
     assert V == spec.V
@@ -308,7 +397,13 @@ def rows_forward_backward(spec: Spec, x, n: float, labels=None, mask=None,
             if weights[name] != 0.0:
                 g_s += weights[name] * gk
         scale = spec.grad_scale / n if n > 0 else 0.0
-        g_x = scale * transform_derivative(x, spec) * g_s
+        g_s *= scale
+        if spec.has(GSPO) and spec.w_grpo != 0.0:
+            # d logp_t / d s_j = onehot(y)_j - q_j; the seam's derivative
+            # already carries the segment means' own normalisation.
+            d = np.asarray(gspo_dlogp, dtype=np.float64).reshape(-1)
+            g_s += (spec.grad_scale * spec.w_grpo) * d[:, None] * (_onehot(vals["y"], V) - vals["q"])
+        g_x = transform_derivative(x, spec) * g_s
         g_x[~valid] = 0.0
         if grad_in is not None and spec.has(ACCUMULATE):
             base = np.asarray(grad_in, dtype=np.float64)
@@ -327,8 +422,14 @@ def batch_divisor(spec: Spec, n_valid: int) -> float:
 
 
 def scalars_from_rows(spec: Spec, vals: dict, valid: np.ndarray, bad: np.ndarray,
-                      n: float) -> np.ndarray:
-    """The 13 output slots: per-loss batch means, the weighted total, counts."""
+                      n: float, seam: dict | None = None) -> np.ndarray:
+    """The 13 output slots: per-loss batch means, the weighted total, counts.
+
+    With GSPO the policy slots hold segment means (READINGS["gspo_slots"]):
+    the loss, ratio, clip fraction, k3 of the sequence ratio and advantage
+    average over the nonempty segments of ``seam``; NEWLOGP stays a token
+    mean.
+    """
     out = np.zeros(len(SLOTS), dtype=np.float64)
     n_valid = int(valid.sum())
 
@@ -355,6 +456,16 @@ def scalars_from_rows(spec: Spec, vals: dict, valid: np.ndarray, bad: np.ndarray
             out[SLOT["CLIPFRAC"]] = float(np.sum(vals["clipped"][valid]) / n)
         out[SLOT["KL_OLD_NEW"]] = mean("k3")
         out[SLOT["ADV_MEAN"]] = mean("adv")
+    if spec.has(GSPO):
+        out[SLOT["NEWLOGP"]] = mean("logp")
+        ns = seam["n_seg"]
+        if ns > 0:
+            ne = seam["nonempty"]
+            out[SLOT["GRPO"]] = float(np.sum(seam["loss"][ne]) / ns)
+            out[SLOT["RATIO"]] = float(np.sum(seam["ratio"][ne]) / ns)
+            out[SLOT["CLIPFRAC"]] = float(np.sum(seam["clipped"][ne]) / ns)
+            out[SLOT["KL_OLD_NEW"]] = float(np.sum(seam["k3"][ne]) / ns)
+            out[SLOT["ADV_MEAN"]] = float(np.sum(seam["adv"][ne]) / ns)
     if spec.has(ENTROPY):
         out[SLOT["ENTROPY"]] = mean("entropy")
     # [#549 Approach] each loss stores its own scalar; the weighted total is
@@ -369,22 +480,33 @@ def scalars_from_rows(spec: Spec, vals: dict, valid: np.ndarray, bad: np.ndarray
 
 def forward_backward(spec: Spec, x, labels=None, mask=None, teacher=None,
                      old_logprobs=None, advantages=None, grad_in=None,
-                     want_grad=True):
-    """Whole-batch oracle: (scalars float64[13], grad float64[N, V] or None)."""
+                     want_grad=True, seq_offsets=None):
+    """Whole-batch oracle: (scalars float64[13], grad float64[N, V] or None).
+
+    GSPO needs ``seq_offsets`` (S+1 row offsets of contiguous segments).
+    """
     x = np.asarray(x, dtype=np.float64)
     valid, _ = row_validity(x.shape[0], spec.V, labels, mask)
     n = batch_divisor(spec, int(valid.sum()))
+    seam = None
+    if spec.has(GSPO):
+        if seq_offsets is None:
+            raise ValueError("GSPO needs segment offsets")
+        _check_inputs(spec, labels, teacher, old_logprobs, advantages)
+        logp = log_softmax_rows(transform(x, spec))[
+            np.arange(x.shape[0]), np.clip(np.asarray(labels, dtype=np.int64).reshape(-1), 0, spec.V - 1)]
+        seam = gspo_seam(spec, logp, old_logprobs, advantages, valid, seq_offsets)
     vals, valid, bad, grad = rows_forward_backward(
         spec, x, n, labels, mask, teacher, old_logprobs, advantages,
-        grad_in, want_grad)
-    return scalars_from_rows(spec, vals, valid, bad, n), grad
+        grad_in, want_grad, gspo_dlogp=None if seam is None else seam["dlogp"])
+    return scalars_from_rows(spec, vals, valid, bad, n, seam), grad
 
 
 def total_loss(spec: Spec, x, labels=None, mask=None, teacher=None,
-               old_logprobs=None, advantages=None) -> float:
+               old_logprobs=None, advantages=None, seq_offsets=None) -> float:
     """The scalar the combined gradient differentiates, times grad_scale."""
     sc, _ = forward_backward(spec, x, labels, mask, teacher, old_logprobs,
-                             advantages, want_grad=False)
+                             advantages, want_grad=False, seq_offsets=seq_offsets)
     return spec.grad_scale * sc[SLOT["TOTAL"]]
 
 
@@ -412,4 +534,9 @@ READINGS = {
     "masked_accumulate": "Masked rows: overwrite mode writes +0.0, accumulate mode leaves the buffer untouched.",
     "nan": "NaN and Inf inputs propagate; nothing is sanitised.",
     "newlogp_space": "new_logprobs live in the transformed (scaled, softcapped) space, the same softmax the losses use.",
+    "segments": "GSPO segments are contiguous row ranges given by S+1 offsets from 0 to n_rows; empty segments are allowed and own no row.",
+    "gspo": "GSPO: sequence ratio s_i = exp(mean over the segment's valid tokens of logp - old); loss_i = -min(s_i A_i, clip(s_i, 1-eps, 1+eps) A_i); batch loss = mean over segments with a valid token; same clip/tie rule as GRPO.",
+    "gspo_adv": "A segment's advantage is the mean of its valid tokens' advantages (the broadcast value when the caller repeats one per sequence).",
+    "gspo_slots": "With GSPO the policy slots are segment means (loss, ratio, clip fraction, k3 of the sequence ratio, advantage); NEWLOGP stays a token mean; GSPO ignores the caller divisor.",
+    "policy_exclusive": "GRPO and GSPO are two policy losses of one kind: a plan holds at most one.",
 }

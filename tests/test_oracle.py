@@ -192,7 +192,7 @@ def test_newlogp_vs_torch_log_softmax():
 # ---------------------------------------------------------------------------
 # Independent torch autograd of the total loss (pins every hand gradient)
 # ---------------------------------------------------------------------------
-def _torch_total(spec, x, y, mask, t, old, adv):
+def _torch_total(spec, x, y, mask, t, old, adv, offsets=None):
     """The weighted total, built from torch library pieces, differentiated by autograd."""
     xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
     k, c = spec.logit_scale, spec.softcap
@@ -226,6 +226,24 @@ def _torch_total(spec, x, y, mask, t, old, adv):
         A = torch.tensor(adv)[valid]
         obj = torch.minimum(r * A, torch.clamp(r, 1 - spec.eps, 1 + spec.eps) * A)
         total = total + spec.w_grpo * (-obj).sum() / n
+    if spec.flags & oracle.GSPO:
+        # sequence-level ratio: exp of the mean token log-ratio of each
+        # segment's valid tokens; the loss averages over nonempty segments
+        lq_all = torch.log_softmax(s, -1)
+        yc = torch.clamp(yv, 0, spec.V - 1)
+        lp = lq_all.gather(-1, yc[:, None])[:, 0]
+        objs = []
+        for i in range(len(offsets) - 1):
+            idx = [r for r in range(offsets[i], offsets[i + 1]) if bool(valid[r])]
+            if not idx:
+                continue
+            idx = torch.tensor(idx)
+            log_s = (lp[idx] - torch.tensor(old)[idx]).mean()
+            r = torch.exp(log_s)
+            A = torch.tensor(adv)[idx].mean()
+            objs.append(torch.minimum(r * A, torch.clamp(r, 1 - spec.eps, 1 + spec.eps) * A))
+        if objs:
+            total = total + spec.w_grpo * (-torch.stack(objs)).mean()
     (spec.grad_scale * total).backward()
     return xt.grad.numpy()
 
@@ -480,6 +498,149 @@ def test_all_rows_masked_gives_zeros():
 
 
 # ---------------------------------------------------------------------------
+# GSPO (sequence-level ratio, per-segment step between forward and backward)
+# ---------------------------------------------------------------------------
+GSPO_OFFSETS = [0, 3, 3, 7, 8, 13]     # an empty segment and a one-token one
+
+
+def _gspo_case(seed=11, N=13, V=29, softcap=0.0, flags=None, spread=0.3):
+    rng = _rng(seed)
+    t = rng.normal(0, 3.0, size=(N, V))
+    x = 0.7 * t + rng.normal(0, 1.5, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    y[4] = -100
+    mask = np.ones(N, dtype=np.uint8)
+    mask[min(9, N - 1)] = 0
+    flags = flags if flags is not None else (oracle.CE | oracle.ZLOSS | oracle.GSPO | oracle.ENTROPY)
+    spec = Spec(V=V, flags=flags, w_ce=0.6, w_z=0.2, w_distill=0.5, w_grpo=1.3,
+                grad_scale=0.5, temperature=1.5, eps=0.2, logit_scale=0.8, softcap=softcap)
+    vals = ho.row_values(spec, x, y)
+    old = vals["logp"] + rng.normal(0, spread, size=N)
+    # one advantage per segment, repeated over its tokens
+    adv = np.zeros(N)
+    for i in range(len(GSPO_OFFSETS) - 1):
+        adv[GSPO_OFFSETS[i]:GSPO_OFFSETS[i + 1]] = rng.normal()
+    return spec, x, y, mask, t, old, adv
+
+
+@pytest.mark.parametrize("softcap", [0.0, 4.0])
+@pytest.mark.parametrize("extra", [0, oracle.RKL, oracle.FKL])
+def test_gspo_gradient_vs_torch_autograd(softcap, extra):
+    spec, x, y, mask, t, old, adv = _gspo_case(softcap=softcap)
+    spec.flags |= extra
+    _, grad = oracle.forward_backward(spec, x, y, mask, t, old, adv, seq_offsets=GSPO_OFFSETS)
+    ref = _torch_total(spec, x, y, mask, t, old, adv, offsets=GSPO_OFFSETS)
+    np.testing.assert_allclose(grad, ref, atol=1e-15, rtol=1e-10)
+
+
+def test_gspo_one_token_segments_equal_grpo():
+    rng = _rng(12)
+    N, V = 11, 17
+    x = rng.normal(0, 2.0, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    y[3] = -100
+    mask = np.ones(N, dtype=np.uint8)
+    mask[7] = 0
+    base = dict(V=V, w_ce=0.4, w_z=0.1, w_grpo=1.0, grad_scale=0.7, eps=0.2)
+    sp_g = Spec(flags=oracle.CE | oracle.ZLOSS | oracle.GRPO, **base)
+    sp_s = Spec(flags=oracle.CE | oracle.ZLOSS | oracle.GSPO, **base)
+    old, adv = _grpo_inputs(rng, x, y, sp_g, spread=0.4)
+    sc_g, g_g = oracle.forward_backward(sp_g, x, y, mask, None, old, adv)
+    sc_s, g_s = oracle.forward_backward(sp_s, x, y, mask, None, old, adv, seq_offsets=np.arange(N + 1))
+    assert sc_g[SLOT["CLIPFRAC"]] > 0            # the case exercises the clip
+    np.testing.assert_allclose(sc_s, sc_g, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(g_s, g_g, rtol=1e-12, atol=1e-16)
+
+
+def test_gspo_ratio_one_closed_forms():
+    spec, x, y, mask, t, old, adv = _gspo_case(flags=oracle.GSPO)
+    spec.w_ce = 0.0
+    vals = ho.row_values(spec, x, y)
+    old = vals["logp"].copy()                     # every sequence ratio is 1
+    sc, grad = oracle.forward_backward(spec, x, y, mask, None, old, adv, seq_offsets=GSPO_OFFSETS)
+    valid, _ = ho.row_validity(len(y), spec.V, y, mask)
+    seg_adv, counts = [], []
+    for i in range(len(GSPO_OFFSETS) - 1):
+        rows = [r for r in range(GSPO_OFFSETS[i], GSPO_OFFSETS[i + 1]) if valid[r]]
+        if rows:
+            seg_adv.append(adv[rows[0]])
+            counts.append((rows, len(rows)))
+    n_seg = len(seg_adv)
+    assert n_seg == 4                             # the empty segment does not count
+    assert sc[SLOT["RATIO"]] == pytest.approx(1.0, abs=1e-15)
+    assert sc[SLOT["CLIPFRAC"]] == 0.0
+    assert sc[SLOT["KL_OLD_NEW"]] == pytest.approx(0.0, abs=1e-15)
+    assert sc[SLOT["GRPO"]] == pytest.approx(-np.mean(seg_adv), abs=1e-14)
+    assert sc[SLOT["ADV_MEAN"]] == pytest.approx(np.mean(seg_adv), abs=1e-14)
+    # gradient = -(A_i / (n_i n_seg)) (onehot(y) - q) times the chain factor k
+    q = vals["q"]
+    expect = np.zeros_like(x)
+    for (rows, n_i), A in zip(counts, seg_adv):
+        for r in rows:
+            oh = np.zeros(spec.V)
+            oh[y[r]] = 1.0
+            expect[r] = -spec.grad_scale * spec.w_grpo * A / (n_i * n_seg) * (oh - q[r]) * spec.logit_scale
+    np.testing.assert_allclose(grad, expect, atol=1e-16, rtol=1e-12)
+
+
+def test_gspo_sequence_ratio_and_clip_closed_forms():
+    spec, x, y, mask, t, old, adv = _gspo_case(flags=oracle.GSPO)
+    vals = ho.row_values(spec, x, y)
+    valid, _ = ho.row_validity(len(y), spec.V, y, mask)
+    # segment [0, 3): token log-ratios 0.1, 0.3, 0.5 -> s = e^0.3 > 1 + eps
+    old = vals["logp"].copy()
+    old[0:3] = vals["logp"][0:3] - np.array([0.1, 0.3, 0.5])
+    adv[0:3] = 2.0
+    seam = ho.gspo_seam(spec, vals["logp"], old, adv, valid, GSPO_OFFSETS)
+    assert seam["ratio"][0] == pytest.approx(math.exp(0.3), rel=1e-14)
+    assert seam["loss"][0] == pytest.approx(-(1.0 + spec.eps) * 2.0, rel=1e-14)
+    assert not seam["active"][0] and seam["clipped"][0]
+    _, grad = oracle.forward_backward(spec, x, y, mask, None, old, adv, seq_offsets=GSPO_OFFSETS)
+    assert np.all(grad[0:3] == 0.0)               # clipped with A > 0: no gradient
+    assert np.abs(grad[5:7]).max() > 0            # other segments still flow
+    # the same log-ratios with A < 0 flow through the unclipped term
+    adv[0:3] = -2.0
+    _, grad = oracle.forward_backward(spec, x, y, mask, None, old, adv, seq_offsets=GSPO_OFFSETS)
+    assert np.abs(grad[0:3]).max() > 0
+
+
+def test_gspo_finite_differences():
+    spec, x, y, mask, t, old, adv = _gspo_case(seed=13, N=8, V=7, spread=0.1,
+                                                flags=oracle.CE | oracle.GSPO | oracle.RKL)
+    offsets = [0, 2, 2, 5, 8]
+    mask[:] = 1
+    mask[3] = 0
+    y[4] = 1
+    _, grad = oracle.forward_backward(spec, x, y, mask, t, old, adv, seq_offsets=offsets)
+    h = 1e-6
+    fd = np.zeros_like(x)
+    for i in range(x.shape[0]):
+        for j in range(x.shape[1]):
+            xp = x.copy()
+            xp[i, j] += h
+            xm = x.copy()
+            xm[i, j] -= h
+            fp = oracle.total_loss(spec, xp, y, mask, t, old, adv, seq_offsets=offsets)
+            fm = oracle.total_loss(spec, xm, y, mask, t, old, adv, seq_offsets=offsets)
+            fd[i, j] = (fp - fm) / (2 * h)
+    np.testing.assert_allclose(grad, fd, atol=2e-8, rtol=0)
+    assert np.all(grad[3] == 0.0)
+
+
+def test_gspo_all_masked_and_bad_offsets():
+    spec, x, y, mask, t, old, adv = _gspo_case(flags=oracle.GSPO)
+    mask[:] = 0
+    sc, grad = oracle.forward_backward(spec, x, y, mask, None, old, adv, seq_offsets=GSPO_OFFSETS)
+    assert np.all(sc[:11] == 0.0) and np.all(grad == 0.0)
+    for bad in ([1, 13], [0, 12], [0, 5, 4, 13], [0]):
+        with pytest.raises(ValueError):
+            oracle.forward_backward(spec, x, y, None, None, old, adv, seq_offsets=bad)
+    with pytest.raises(ValueError):
+        oracle.forward_backward(Spec(V=spec.V, flags=oracle.GRPO | oracle.GSPO), x, y, None, None,
+                                old, adv, seq_offsets=GSPO_OFFSETS)
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each mutation of the oracle must be caught by a pin above
 # ---------------------------------------------------------------------------
 def _mutant_total_grad_fails(monkeypatch, target, replacement):
@@ -536,3 +697,35 @@ def test_planted_mistakes_are_caught(monkeypatch):
     with pytest.raises(AssertionError):
         test_finite_differences_clipped_grpo_tokens()
     monkeypatch.setattr(ho, "row_values", orig_values)
+
+
+def test_gspo_planted_mistakes_are_caught(monkeypatch):
+    orig = ho.gspo_seam
+
+    def per_token_mean_ratio(spec, logp, old, A, valid, offsets):
+        # mean of the token ratios instead of the exponential of the mean log-ratio
+        out = orig(spec, logp, old, A, valid, offsets)
+        seg = out["segment"]
+        r_tok = np.exp(np.asarray(logp) - np.asarray(old))
+        for i in np.nonzero(out["nonempty"])[0]:
+            rows = (seg == i) & np.asarray(valid)
+            r = r_tok[rows].mean()
+            d = -out["adv"][i] * r / (rows.sum() * out["n_seg"]) if out["active"][i] else 0.0
+            out["dlogp"][rows] = d
+        return out
+
+    def no_length_norm(spec, logp, old, A, valid, offsets):
+        out = orig(spec, logp, old, A, valid, offsets)
+        out["dlogp"] = out["dlogp"] * np.take(out["n_tokens"], out["segment"])
+        return out
+
+    def token_count_divisor(spec, logp, old, A, valid, offsets):
+        out = orig(spec, logp, old, A, valid, offsets)
+        out["dlogp"] = out["dlogp"] * out["n_seg"] / max(int(np.asarray(valid).sum()), 1)
+        return out
+
+    for mutant in (per_token_mean_ratio, no_length_norm, token_count_divisor):
+        monkeypatch.setattr(ho, "gspo_seam", mutant)
+        with pytest.raises(AssertionError):
+            test_gspo_gradient_vs_torch_autograd(0.0, 0)
+    monkeypatch.setattr(ho, "gspo_seam", orig)
