@@ -27,7 +27,9 @@ import workloads  # noqa: E402
 METRIC = "tokens/s + achieved HBM GB/s (% peak), CE+z+GRPO+entropy, V=151936 bf16, 1 GPU"
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, vendor figure
 FUSED_KERNEL = "fused_kernel"
-LOSS_NAMES = {1: "CE", 2: "z", 4: "FKL", 8: "RKL", 64: "FDCE", 16: "GRPO", 32: "entropy"}
+# with GSPO the timed bracket holds the forward, the segment step and the reloading backward
+GSPO_KERNELS = "fused_kernel (forward) + seam_kernel + grad_kernel"
+LOSS_NAMES = {1: "CE", 2: "z", 4: "FKL", 8: "RKL", 64: "FDCE", 16: "GRPO", 128: "GSPO", 32: "entropy"}
 
 
 def log(msg):
@@ -77,13 +79,17 @@ def cpu_baseline(w, budget_s: float, threads: int):
                  teacher=inp["teacher"].double().numpy() if inp["teacher"] is not None else None,
                  advantages=inp["advantages"].double().numpy() if inp["advantages"] is not None else None,
                  grad_in=inp["grad_init"].double().numpy() if inp["grad_init"] is not None else None)
-        if w.flags & oracle.GRPO:
+        if w.flags & (oracle.GRPO | oracle.GSPO):
             d["old_logprobs"] = oracle.row_values(spec, x, y)["logp"] + inp["old_noise"].double().numpy()
         return x, d
 
     def task(args):
         x, d = args
-        oracle.rows_forward_backward(spec, x, float(w.N), **d)
+        if w.flags & oracle.GSPO:
+            # the rows of one task form one segment (GSPO's coefficients need whole segments)
+            oracle.forward_backward(spec, x, seq_offsets=[0, x.shape[0]], **d)
+        else:
+            oracle.rows_forward_backward(spec, x, float(w.N), **d)
 
     def split(x, d, k):
         out = []
@@ -163,7 +169,7 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     log(f"generating {w.name}: N={w.N} V={w.V} {w.dtype}")
     inp = workloads.generate(w, dev)
-    if w.flags & workloads.GRPO:
+    if w.flags & (workloads.GRPO | workloads.GSPO):
         # old = label log-prob of the stored logits (fp32, torch) + noise: input synthesis
         N = w.N
         old = torch.empty(N, dtype=torch.float32, device=dev)
@@ -189,7 +195,8 @@ def main(argv=None):
 
     def step(p=plan, g=grad):
         return p(inp["logits"], labels=labels, mask=inp["mask"], teacher=inp["teacher"],
-                 old_logprobs=inp.get("old_logprobs"), advantages=inp["advantages"], grad=g)
+                 old_logprobs=inp.get("old_logprobs"), advantages=inp["advantages"], grad=g,
+                 seq_offsets=inp["seq_offsets"])
 
     # Context measurements first (they also bring the device to its working
     # clocks before the fused warm-up and timed steps).
@@ -216,7 +223,7 @@ def main(argv=None):
             if not (w.flags & bit):
                 continue
             kw = plan_kwargs(w)
-            keep = {1: "ce", 2: "z", 4: "distill", 8: "distill", 64: "distill", 16: "grpo"}.get(bit)
+            keep = {1: "ce", 2: "z", 4: "distill", 8: "distill", 64: "distill", 16: "grpo", 128: "grpo"}.get(bit)
             for key in ("ce", "z", "distill", "grpo"):
                 if key != keep:
                     kw[key] = 0.0
@@ -279,7 +286,7 @@ def main(argv=None):
     traffic = stored_traffic(w, src_hash)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                "kernel": FUSED_KERNEL, "kernel_ms_avg": round(kernel_avg, 5),
+                "kernel": GSPO_KERNELS if w.flags & workloads.GSPO else FUSED_KERNEL, "kernel_ms_avg": round(kernel_avg, 5),
                 "algorithmic_bytes_per_launch": algo_bytes}
 
     if separate is not None:

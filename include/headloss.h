@@ -67,6 +67,11 @@ enum {
                               against the teacher distribution, -sum p log q
                               (#549 Loss coverage: from-distribution
                               cross-entropy); gradient as HL_FKL            */
+    HL_GSPO = 1u << 7,     /* GSPO: the clipped objective on the sequence-
+                              level ratio s_i = exp(mean over segment i's
+                              valid tokens of logp - old), averaged over
+                              segments; needs hl_forward_backward_segments.
+                              At most one of HL_GRPO, HL_GSPO per plan.     */
     HL_ACCUMULATE = 1u << 16 /* mode bit: add into grad_out instead of
                                 overwriting it (#558 Validation: gradient
                                 accumulation)                                */
@@ -80,15 +85,19 @@ enum {
 typedef struct {
     float ce;         /* weight of HL_CE                                    */
     float z;          /* weight of HL_ZLOSS                                 */
-    float distill;    /* weight of HL_FKL / HL_RKL                          */
-    float grpo;       /* weight of HL_GRPO                                  */
+    float distill;    /* weight of HL_FKL / HL_RKL / HL_FDCE                */
+    float grpo;       /* weight of HL_GRPO or HL_GSPO                       */
     float grad_scale; /* extra factor on the gradient only (G)              */
     float divisor;    /* > 0: divide sums by this; <= 0: by the number of
                          valid rows of the call                             */
 } hl_weights;
 
 /* Output slots of scalars_out (device float[HL_NUM_SCALARS]). Slots of
- * losses that are not enabled are written as 0. */
+ * losses that are not enabled are written as 0. With HL_GSPO the policy slots
+ * GRPO (the GSPO loss), RATIO, CLIPFRAC, KL_OLD_NEW and ADV_MEAN are means
+ * over the segments that hold a valid token, of the segment's loss, sequence
+ * ratio s_i, clipped flag |s_i - 1| > eps, (s_i - 1) - log s_i and advantage;
+ * NEWLOGP stays a mean over valid tokens. */
 enum {
     HL_S_CE = 0, HL_S_Z, HL_S_DISTILL, HL_S_GRPO, HL_S_NEWLOGP, HL_S_RATIO,
     HL_S_CLIPFRAC, HL_S_KL_OLD_NEW, HL_S_ADV_MEAN, HL_S_ENTROPY, HL_S_TOTAL,
@@ -118,13 +127,14 @@ typedef struct hl_plan_s* hl_plan_t;
  *   weights      host pointer; all fields finite.
  *   temperature  divides the teacher logits (distillation only), > 0
  *                (#549 Bundled fix: the temperature is honoured).
- *   eps          GRPO clip range, 0 < eps < 1 (GRPO only).
+ *   eps          GRPO / GSPO clip range, 0 < eps < 1 (policy losses only).
  *   logit_scale  student logits are multiplied by it, finite and > 0; one
  *                plan = one scale (#549 Approach: one softmax = one scale).
  *   softcap      0 = off; > 0: s = softcap * tanh(logit_scale * x / softcap).
  * Makes no HIP call. Errors: HL_ERR_INVALID_ARG (V < 1, unknown flag bits,
- * no loss flag, two distillation flags, temperature <= 0 with distillation,
- * eps outside (0,1) with GRPO, bad scale or softcap, non-finite weight),
+ * no loss flag, two distillation flags, HL_GRPO with HL_GSPO, temperature
+ * <= 0 with distillation, eps outside (0,1) with a policy loss, bad scale or
+ * softcap, non-finite weight),
  * HL_ERR_UNSUPPORTED (V too long for any kernel variant).
  */
 hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags,
@@ -141,9 +151,9 @@ size_t hl_workspace_bytes(hl_plan_t plan, int64_t n_rows);
 
 /* Give the plan caller-owned device workspace (256-byte aligned, at least
  * hl_workspace_bytes(plan, n_rows) for every later call). Replaces any
- * workspace the library allocated. The library zeroes it before returning
- * (a blocking memset on the default stream). Errors: HL_ERR_INVALID_ARG (NULL
- * plan or pointer, misaligned pointer), HL_ERR_HIP. */
+ * workspace the library allocated. Makes no HIP call: the next call clears
+ * whatever part of the workspace must start at zero, on its own stream.
+ * Errors: HL_ERR_INVALID_ARG (NULL plan or pointer, misaligned pointer). */
 hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t bytes);
 
 /*
@@ -153,7 +163,7 @@ hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t byte
  *   logits          device [N, V] row-major contiguous, plan dtype, base
  *                   16-byte aligned. Raw student logits.
  *   labels          device int64[N] or NULL; -100 = ignored token. Needed by
- *                   HL_CE and HL_GRPO. An unmasked label outside [0, V) that
+ *                   HL_CE, HL_GRPO and HL_GSPO. An unmasked label outside [0, V) that
  *                   is not -100 masks the row and counts in N_BADLABEL.
  *   mask            device uint8[N] or NULL; 0 = masked token. Masking
  *                   applies to every loss and metric.
@@ -185,9 +195,45 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
                               const float* advantages, void* grad_out,
                               float* scalars_out, hipStream_t stream);
 
+/*
+ * hl_forward_backward_segments - hl_forward_backward with sequence segments,
+ * required by HL_GSPO (and accepted, then ignored, by every other plan).
+ * The GSPO case of #558 Design: a forward pass computes every row's softmax
+ * statistics, a per-segment step turns them into sequence ratios and a
+ * per-token label-column coefficient, and a backward that reloads the logits
+ * writes the combined gradient. The logits (and teacher) are therefore read
+ * twice.
+ *   seq_offsets  device int32[n_segments + 1]: segment i is rows
+ *                [seq_offsets[i], seq_offsets[i+1]); the offsets start at 0,
+ *                never decrease and end at n_rows (empty segments allowed).
+ *                Needed by HL_GSPO. Checked on the device: malformed offsets
+ *                make every float scalar and the gradient NaN.
+ *   n_segments   1 <= n_segments <= n_rows when n_rows > 0 (0 allowed when
+ *                n_rows == 0).
+ *   old_logprobs, advantages: per token, as for HL_GRPO; a segment's
+ *                advantage is the mean over its valid tokens.
+ * The GSPO gradient of a valid token t in segment i is
+ *   grad_scale * weights.grpo * act_i * A_i * s_i / (n_i * n_seg)
+ *   * ds/dx * (softmax - onehot(label)),
+ * with n_i the segment's valid tokens, n_seg the segments holding a valid
+ * token, act_i = 0 when the clip is strictly active in the advantage's
+ * direction (weights.divisor does not apply to GSPO).
+ * Other arguments, errors and asynchrony as hl_forward_backward, plus
+ * HL_ERR_INVALID_ARG (n_segments out of range) and HL_ERR_MISSING_INPUT
+ * (HL_GSPO without seq_offsets). hl_forward_backward on an HL_GSPO plan
+ * returns HL_ERR_MISSING_INPUT.
+ */
+hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const void* logits,
+                                       const int64_t* labels, const uint8_t* mask,
+                                       const void* teacher_logits, const float* old_logprobs,
+                                       const float* advantages, const int32_t* seq_offsets,
+                                       int64_t n_segments, void* grad_out,
+                                       float* scalars_out, hipStream_t stream);
+
 /* Device pointer to the per-row values of the plan's last call: float
  * [n_rows, HL_NUM_ROW_COLS] inside the workspace (masked rows are all 0,
- * HL_R_VALID is 1 for counted rows). Valid until the next call with the plan
+ * HL_R_VALID is 1 for counted rows; with HL_GSPO the policy columns hold the
+ * row's segment values). Valid until the next call with the plan
  * or a workspace change. These are the per-token values the batch means of
  * #549 Loss coverage are taken over (new_logprobs, entropy, ratio, ...).
  * Returns NULL when the plan has no workspace yet. */
@@ -214,7 +260,8 @@ hl_status hl_plan_set_variant(hl_plan_t plan, int chunks, int block);
 hl_status hl_plan_describe(hl_plan_t plan, int* chunks, int* block, int* vec_per_thread);
 
 /* Record the two events (hipEvent_t, may be NULL to stop) immediately before
- * and after the fused kernel of every later call, on the call's stream, so a
+ * and after the fused kernel of every later call (with HL_GSPO: before the
+ * forward kernel and after the gradient kernel), on the call's stream, so a
  * profiler can time the dominant kernel alone. */
 hl_status hl_plan_set_timing_events(hl_plan_t plan, hipEvent_t before, hipEvent_t after);
 

@@ -35,6 +35,7 @@ RKL = 1 << 3
 GRPO = 1 << 4
 ENTROPY = 1 << 5
 FDCE = 1 << 6
+GSPO = 1 << 7
 ACCUMULATE = 1 << 16
 
 SLOTS = ("CE", "Z", "DISTILL", "GRPO", "NEWLOGP", "RATIO", "CLIPFRAC",
@@ -98,6 +99,8 @@ def load_library(path: str | None = None):
     lib.hl_plan_set_workspace.restype = ctypes.c_int
     lib.hl_forward_backward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.hl_forward_backward.restype = ctypes.c_int
+    lib.hl_forward_backward_segments.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp]
+    lib.hl_forward_backward_segments.restype = ctypes.c_int
     lib.hl_row_values.argtypes = [vp]
     lib.hl_row_values.restype = vp
     lib.hl_plan_set_chunks.argtypes = [vp, ctypes.c_int]
@@ -145,8 +148,9 @@ def _dtype_code(dtype) -> int:
 class Plan:
     """A validated loss set (``hl_plan``) bound to one vocabulary size.
 
-    Calling the plan runs ``hl_forward_backward`` on the current stream of
-    the logits' device and returns the device float32[13] scalar tensor.
+    Calling the plan runs ``hl_forward_backward`` (``hl_forward_backward_segments``
+    when ``seq_offsets`` is given) on the current stream of the logits' device
+    and returns the device float32[13] scalar tensor.
     """
 
     def __init__(self, V: int, dtype, flags: int, *, ce: float = 1.0, z: float = 0.0,
@@ -220,7 +224,7 @@ class Plan:
         return ctypes.c_void_p(t.data_ptr())
 
     def __call__(self, logits, labels=None, mask=None, teacher=None, old_logprobs=None,
-                 advantages=None, grad=None, scalars=None, stream=None):
+                 advantages=None, grad=None, scalars=None, stream=None, seq_offsets=None):
         torch = _torch()
         if logits.dim() != 2 or logits.shape[1] != self.V:
             raise ValueError(f"logits must be [N, {self.V}], got {tuple(logits.shape)}")
@@ -244,8 +248,17 @@ class Plan:
         self._ensure_workspace(n, dev)
         if stream is None:
             stream = torch.cuda.current_stream(dev)
-        st = self._lib.hl_forward_backward(self._h, n, *args, sp, ctypes.c_void_p(stream.cuda_stream))
-        _check("hl_forward_backward", st)
+        if seq_offsets is None:
+            st = self._lib.hl_forward_backward(self._h, n, *args, sp, ctypes.c_void_p(stream.cuda_stream))
+            _check("hl_forward_backward", st)
+        else:
+            if seq_offsets.dim() != 1 or seq_offsets.numel() < 1:
+                raise ValueError("seq_offsets must be a 1-D int32 tensor of n_segments + 1 offsets")
+            op = self._ptr(seq_offsets, "seq_offsets", torch.int32)
+            st = self._lib.hl_forward_backward_segments(
+                self._h, n, *args[:6], op, seq_offsets.numel() - 1, args[6], sp,
+                ctypes.c_void_p(stream.cuda_stream))
+            _check("hl_forward_backward_segments", st)
         self._last_rows = n
         return scalars
 

@@ -40,6 +40,82 @@ __global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
         p.ctrl[CTRL_EPOCH] = (p.fresh || next == 0u) ? 1u : next;
         p.ctrl[CTRL_ERROR] = 0u;
         p.ctrl[CTRL_DONE] = 0u;
+        p.ctrl[CTRL_NSEG] = 0u;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// seam_kernel (GSPO): one wave per segment [o_i, o_{i+1}). From the final row
+// records it forms each valid token's log-ratio logp_t - old_t in fp64, sums
+// them with the advantages in a fixed order (lane-strided, then an xor
+// butterfly, which leaves the same bits in every lane), and derives the
+// sequence ratio s_i = exp(mean log-ratio), the segment advantage (mean of
+// its tokens' advantages), the clipped objective and the per-token
+// coefficient act * A_i * s_i / n_i that the load-mode backward adds to the
+// label column. Malformed offsets raise CTRL_ERROR (the scalars and the
+// gradient then come out NaN); every access stays inside [0, n_rows).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSeamBlock) void seam_kernel(const SeamParams p) {
+    constexpr double LN2 = 0.69314718055994530942;
+    const int lane = threadIdx.x & 63;
+    const int64_t i = (int64_t)blockIdx.x * (kSeamBlock / 64) + (threadIdx.x >> 6);
+    if (i >= p.n_segments) return;
+    const int64_t o0 = p.offsets[i], o1 = p.offsets[i + 1];
+    const bool ok = o0 >= 0 && o1 >= o0 && o1 <= p.n_rows && (i != 0 || o0 == 0) &&
+                    (i != p.n_segments - 1 || o1 == p.n_rows);
+    if (!ok) {
+        if (lane == 0) __hip_atomic_store(&p.ctrl[CTRL_ERROR], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    double sd = 0.0, sa = 0.0;
+    uint32_t cnt = 0;
+    for (int64_t t = o0 + lane; t < o1; t += 64) {
+        const float* rec = p.row_rec + t * REC;
+        if (rec[R_VALID] != 0.f) {
+            const double lse = ((double)rec[R_M] + log2((double)rec[R_Z])) * LN2;
+            const double xy = rec[R_XY];
+            const double sy = p.cap > 0.f ? (double)p.cap * tanh((double)p.k * xy / (double)p.cap)
+                                          : (double)p.k * xy;
+            sd += (sy - lse) - (double)p.old_logprobs[t];
+            sa += (double)p.advantages[t];
+            ++cnt;
+        }
+    }
+    for (int m = 1; m < 64; m <<= 1) {
+        sd = __dadd_rn(sd, __shfl_xor(sd, m, 64));
+        sa = __dadd_rn(sa, __shfl_xor(sa, m, 64));
+        cnt += __shfl_xor(cnt, m, 64);
+    }
+    double loss = 0.0, ratio = 0.0, clip = 0.0, k3 = 0.0, adv = 0.0, deriv = 0.0;
+    if (cnt > 0u) {
+        const double ls = sd / (double)cnt;
+        const double eps = p.eps;
+        ratio = exp(ls);
+        adv = sa / (double)cnt;
+        const double rc = ratio < 1.0 - eps ? 1.0 - eps : (ratio > 1.0 + eps ? 1.0 + eps : ratio);
+        const double un = ratio * adv, cl = rc * adv;
+        loss = -(un < cl ? un : cl);
+        const bool active = !((adv > 0.0 && ratio > 1.0 + eps) || (adv < 0.0 && ratio < 1.0 - eps));
+        clip = fabs(ratio - 1.0) > eps ? 1.0 : 0.0;
+        k3 = expm1(ls) - ls;
+        deriv = active ? adv * ratio / (double)cnt : 0.0;
+    }
+    if (lane == 0) {
+        double* sr = p.seg_rec + i * SEGREC;
+        sr[SG_LOSS] = loss;
+        sr[SG_RATIO] = ratio;
+        sr[SG_CLIP] = clip;
+        sr[SG_K3] = k3;
+        sr[SG_ADV] = adv;
+        sr[SG_NONEMPTY] = cnt > 0u ? 1.0 : 0.0;
+        sr[SG_DERIV] = deriv;
+        sr[SG_COUNT] = (double)cnt;
+        if (cnt > 0u) atomicAdd(&p.ctrl[CTRL_NSEG], 1u);
+    }
+    const float dc = (float)deriv;
+    for (int64_t t = o0 + lane; t < o1; t += 64) {
+        p.row_coef[t] = p.row_rec[t * REC + R_VALID] != 0.f ? dc : 0.f;
+        p.seg_of_row[t] = (int32_t)i;
     }
 }
 
@@ -102,11 +178,38 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
                     v[RC_ADV] = adv;
                 }
             }
+            if (f & F_GSPO) {
+                // per-token view of the token's segment
+                const int64_t sid = p.seg_of_row[r];
+                const bool in = sid >= 0 && sid < p.n_segments;
+                const double* sr = p.seg_rec + (in ? sid : 0) * SEGREC;
+                const double qnan = __builtin_nan("");
+                v[RC_GRPO] = in ? sr[SG_LOSS] : qnan;
+                v[RC_RATIO] = in ? sr[SG_RATIO] : qnan;
+                v[RC_CLIP] = in ? sr[SG_CLIP] : qnan;
+                v[RC_K3] = in ? sr[SG_K3] : qnan;
+                v[RC_ADV] = in ? sr[SG_ADV] : qnan;
+            }
             v[RC_VALID] = 1.0;
         }
         float* out = p.rows + r * NCOL;
 #pragma unroll
         for (int c = 0; c < NCOL; ++c) out[c] = (float)v[c];
+    }
+    if (f & F_GSPO) {
+        // the policy columns are summed over segments, not rows: thread r
+        // contributes segment r (there are never more segments than rows)
+        v[RC_GRPO] = v[RC_RATIO] = v[RC_CLIP] = v[RC_K3] = v[RC_ADV] = 0.0;
+        if (r < p.n_segments) {
+            const double* sr = p.seg_rec + r * SEGREC;
+            if (sr[SG_NONEMPTY] != 0.0) {
+                v[RC_GRPO] = sr[SG_LOSS];
+                v[RC_RATIO] = sr[SG_RATIO];
+                v[RC_CLIP] = sr[SG_CLIP];
+                v[RC_K3] = sr[SG_K3];
+                v[RC_ADV] = sr[SG_ADV];
+            }
+        }
     }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
@@ -180,6 +283,19 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
             out[7] = (float)(sum[RC_K3] * inv);
             out[8] = (float)(sum[RC_ADV] * inv);
         }
+        if (f & F_GSPO) {
+            out[4] = (float)(sum[RC_LOGP] * inv);
+            const uint32_t n_seg = p.ctrl[CTRL_NSEG];
+            if (n_seg > 0u) {
+                const double is = 1.0 / (double)n_seg;
+                grpo = sum[RC_GRPO] * is;
+                out[3] = (float)grpo;
+                out[5] = (float)(sum[RC_RATIO] * is);
+                out[6] = (float)(sum[RC_CLIP] * is);
+                out[7] = (float)(sum[RC_K3] * is);
+                out[8] = (float)(sum[RC_ADV] * is);
+            }
+        }
         if (f & F_ENT) out[9] = (float)(sum[RC_ENT] * inv);
         out[10] = (float)((double)p.w_ce * ce + (double)p.w_z * z + (double)p.w_d * kl +
                           (double)p.w_g * grpo);
@@ -187,7 +303,8 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
     out[11] = (float)n_valid;
     out[12] = (float)p.ctrl[CTRL_NBAD];
     if (p.ctrl[CTRL_ERROR] != 0u) {
-        // a split-vocab row never saw all of its chunks: nothing is trustworthy
+        // a split-vocab row never saw all of its chunks, or the segment
+        // offsets were malformed: nothing is trustworthy
         for (int i = 0; i < 11; ++i) out[i] = __builtin_nanf("");
     }
     for (int i = 0; i < NSCALARS; ++i) p.scalars[i] = out[i];
@@ -201,6 +318,14 @@ hipError_t launch_count(const CountParams& p, hipStream_t s) {
         groups = groups < 1 ? 1 : (groups > 1024 ? 1024 : groups);
     }
     hipLaunchKernelGGL(count_kernel, dim3((unsigned)groups), dim3(1024), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_seam(const SeamParams& p, hipStream_t s) {
+    (void)hipGetLastError();
+    constexpr int per = kSeamBlock / 64;
+    const int64_t groups = (p.n_segments + per - 1) / per;
+    hipLaunchKernelGGL(seam_kernel, dim3((unsigned)groups), dim3(kSeamBlock), 0, s, p);
     return hipGetLastError();
 }
 

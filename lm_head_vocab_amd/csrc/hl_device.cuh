@@ -12,6 +12,9 @@
 //                  registers it already holds;
 //   reduce_kernel  fixed-order fp64 sum of the per-row values into the batch
 //                  scalars.
+// With GSPO the fused kernel runs forward-only, a segment kernel turns the
+// row statistics into per-segment ratios and per-row coefficients, and
+// grad_kernel reloads each row to write the gradient.
 //
 // The gradient is written in the two-coefficient form of Fast-LLM PR #558
 // (Triton kernel for the monolithic loss, section Design): prob_coeff times
@@ -300,6 +303,93 @@ __device__ __forceinline__ void row_status(const int64_t* labels, const uint8_t*
 }
 
 // ---------------------------------------------------------------------------
+// Per-row gradient coefficients and the per-element gradient
+// ---------------------------------------------------------------------------
+// The gradient of the weighted loss with respect to the raw logit x_j is
+//   G k / n * c_j * (P q_j - L [j == y] - w_fkl p_j + w_rkl q_j (lq_j - lp_j - RKL))
+// with P = w_ce + 2 w_z lse + w_g a + w_fkl, L = w_ce + w_g a, a = act * A * r,
+// c_j = 1 (or 1 - tanh^2 with softcap). Fast-LLM PR #558 (Triton kernel for
+// the monolithic loss), section Design: every loss only adds to the
+// probability coefficient and the label-column coefficient.
+struct Coefs {
+    float B2;      // log2-domain student log-partition
+    float Bt2;     // log2-domain teacher log-partition
+    float alpha;   // probability coefficient, times G k / n
+    float beta;    // label-column coefficient, times G k / n
+    float gam;     // forward-KL teacher coefficient, times G k / n
+    float rho2;    // reverse-KL log-ratio coefficient (log2 domain)
+    float c0;      // reverse-KL probability coefficient
+};
+
+// All data registers are live where the fused kernel calls this, so only
+// single-instruction hardware log2 / exp2 / rcp are used; the reported
+// per-row values are recomputed in fp64 by the reduction from the same record.
+template <int TMODE, bool SOFTCAP>
+__device__ __forceinline__ Coefs row_coefs(const FusedParams& p, const Rec& r, int64_t y, float xy,
+                                           float old, float adv) {
+    const uint32_t f = p.flags;
+    const float l2Z = __builtin_amdgcn_logf(r.Z);
+    Coefs k;
+    k.B2 = r.M + l2Z;
+    const float lse = k.B2 * kLn2f;
+    k.Bt2 = 0.f;
+    float kl = 0.f;
+    if (TMODE != TM_NONE) {
+        const float l2Zt = __builtin_amdgcn_logf(r.Zt);
+        k.Bt2 = r.Mt + l2Zt;
+        if (TMODE == TM_RKL) kl = kLn2f * (r.SX * __builtin_amdgcn_rcpf(r.Z) - l2Z + l2Zt);
+    }
+    float a_g = 0.f;
+    if ((f & F_GRPO) && y >= 0) {
+        const float sy = SOFTCAP ? p.cap * hl_tanh(xy * p.kc) : p.k * xy;
+        const float d = (sy - lse) - old;
+        const float ratio = fast_exp2(d * kLog2e);
+        const bool active = !((adv > 0.f && ratio > 1.f + p.eps) || (adv < 0.f && ratio < 1.f - p.eps));
+        a_g = active ? adv * ratio : 0.f;
+    }
+    const uint32_t n_valid = p.ctrl[CTRL_NVALID];
+    const float n = p.divisor > 0.f ? p.divisor : (float)n_valid;
+    const float scale = p.grad_scale * p.k / n;
+    float P = 0.f, L = 0.f, wd = 0.f;
+    if ((f & F_CE) && p.w_ce != 0.f) { P += p.w_ce; L += p.w_ce; }
+    if ((f & F_Z) && p.w_z != 0.f) P += 2.f * p.w_z * lse;
+    if ((f & F_GRPO) && p.w_g != 0.f) { P += p.w_g * a_g; L += p.w_g * a_g; }
+    if ((f & F_DISTILL) && p.w_d != 0.f) wd = p.w_d;
+    if (fkl_like(TMODE)) P += wd;
+    k.alpha = scale * P;
+    k.beta = scale * L;
+    k.gam = scale * wd;
+    k.rho2 = scale * wd * kLn2f;
+    k.c0 = scale * (P - wd * kl);
+    return k;
+}
+
+// Gradient of one element; lab = the label-column coefficient at the label, else 0.
+template <int TMODE, bool SOFTCAP>
+__device__ __forceinline__ float grad_one(const FusedParams& p, const Coefs& k, float x, float t, float lab) {
+    float aq, cf = 1.0f;
+    if (SOFTCAP) {
+        const float th = hl_tanh(x * p.kc);
+        aq = fmaf(p.cap * th, kLog2e, -k.B2);
+        cf = fmaf(-th, th, 1.0f);
+    } else {
+        aq = fmaf(x, p.K1, -k.B2);
+    }
+    const float q = fast_exp2(aq);
+    float g;
+    if (TMODE == TM_NONE) {
+        g = fmaf(k.alpha, q, -lab);
+    } else if (fkl_like(TMODE)) {
+        const float pt = fast_exp2(fmaf(t, p.K2, -k.Bt2));
+        g = fmaf(k.alpha, q, fmaf(-k.gam, pt, -lab));
+    } else {
+        const float up = fmaf(t, p.K2, -k.Bt2);
+        g = fmaf(q, fmaf(k.rho2, aq - up, k.c0), -lab);
+    }
+    return SOFTCAP ? cf * g : g;
+}
+
+// ---------------------------------------------------------------------------
 // fused_kernel
 // ---------------------------------------------------------------------------
 // Bounded wait for the sibling chunks of a row (split-vocab variant only).
@@ -574,67 +664,11 @@ void fused_kernel(const FusedParams p) {
     if (p.grad == nullptr) return;
 
     // ---- gradient coefficients (fp32, every thread) ----
-    // All data registers are live here, so only single-instruction hardware
-    // log2 / exp2 / rcp are used; the reported per-row values are recomputed
-    // in fp64 by the reduction kernel from the same record.
-    const uint32_t f = p.flags;
-    const float l2Z = __builtin_amdgcn_logf(r.Z);
-    const float B2 = r.M + l2Z;                        // log2-domain lse
-    const float lse = B2 * kLn2f;
-    float Bt2 = 0.f, kl = 0.f;
-    if (TMODE != TM_NONE) {
-        const float l2Zt = __builtin_amdgcn_logf(r.Zt);
-        Bt2 = r.Mt + l2Zt;
-        if (TMODE == TM_RKL) kl = kLn2f * (r.SX * __builtin_amdgcn_rcpf(r.Z) - l2Z + l2Zt);
-    }
-    float a_g = 0.f;
-    if ((f & F_GRPO) && y >= 0) {
-        const float xy = s_row[0];
-        const float sy = SOFTCAP ? p.cap * hl_tanh(xy * p.kc) : p.k * xy;
-        const float d = (sy - lse) - s_row[1];
-        const float ratio = fast_exp2(d * kLog2e);
-        const float adv = s_row[2];
-        const bool active = !((adv > 0.f && ratio > 1.f + p.eps) || (adv < 0.f && ratio < 1.f - p.eps));
-        a_g = active ? adv * ratio : 0.f;
-    }
-    const uint32_t n_valid = p.ctrl[CTRL_NVALID];
-    const float n = p.divisor > 0.f ? p.divisor : (float)n_valid;
-    const float scale = p.grad_scale * p.k / n;
-    float P = 0.f, L = 0.f, wd = 0.f;
-    if ((f & F_CE) && p.w_ce != 0.f) { P += p.w_ce; L += p.w_ce; }
-    if ((f & F_Z) && p.w_z != 0.f) P += 2.f * p.w_z * lse;
-    if ((f & F_GRPO) && p.w_g != 0.f) { P += p.w_g * a_g; L += p.w_g * a_g; }
-    if ((f & F_DISTILL) && p.w_d != 0.f) wd = p.w_d;
-    if (fkl_like(TMODE)) P += wd;
-    const float alpha = scale * P;             // prob_coeff (times G k / n)
-    const float beta = scale * L;              // label_coeff
-    const float gam = scale * wd;              // forward-KL teacher coefficient
-    const float rho2 = scale * wd * kLn2f;
-    const float c0 = scale * (P - wd * kl);
-
-    // grad for one element; lab = label_coeff at the label column, else 0
+    const Coefs kf = row_coefs<TMODE, SOFTCAP>(p, r, y, s_row[0], s_row[1], s_row[2]);
     auto grad_elem = [&](float x, float t, float lab) -> float {
-        float aq, cf = 1.0f;
-        if (SOFTCAP) {
-            const float th = hl_tanh(x * p.kc);
-            aq = fmaf(p.cap * th, kLog2e, -B2);
-            cf = fmaf(-th, th, 1.0f);
-        } else {
-            aq = fmaf(x, p.K1, -B2);
-        }
-        const float q = fast_exp2(aq);
-        float g;
-        if (TMODE == TM_NONE) {
-            g = fmaf(alpha, q, -lab);
-        } else if (fkl_like(TMODE)) {
-            const float pt = fast_exp2(fmaf(t, p.K2, -Bt2));
-            g = fmaf(alpha, q, fmaf(-gam, pt, -lab));
-        } else {
-            const float up = fmaf(t, p.K2, -Bt2);
-            g = fmaf(q, fmaf(rho2, aq - up, c0), -lab);
-        }
-        return SOFTCAP ? cf * g : g;
+        return grad_one<TMODE, SOFTCAP>(p, kf, x, t, lab);
     };
+    const float beta = kf.beta;
 
     // label position relative to this chunk's body vectors (-1: not here)
     int yv = -1;
@@ -676,6 +710,127 @@ template <typename T, int BLOCK, int NVEC, int TMODE, bool SOFTCAP>
 hipError_t launch_fused(const FusedParams& p, dim3 grid, hipStream_t s) {
     (void)hipGetLastError();   // drop an error left by an earlier, unrelated call
     hipLaunchKernelGGL((fused_kernel<T, BLOCK, NVEC, TMODE, SOFTCAP>), grid, dim3(BLOCK), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// grad_kernel: the load-mode backward. One workgroup per row reloads the row
+// (and the teacher row) after the softmax statistics are final, and writes the
+// gradient with the same coefficients as the fused kernel plus a per-row
+// label-column coefficient from the GSPO segment step. Fast-LLM PR #558, section
+// Design: with GSPO present, a per-segment step runs between the forward and
+// a load-mode backward and hands it a per-token coefficient that superposes
+// with the in-kernel losses.
+// ---------------------------------------------------------------------------
+template <typename T, int TMODE, bool SOFTCAP>
+__global__ __launch_bounds__(kGradBlock) void grad_kernel(const FusedParams p) {
+    constexpr int VEC = T::VEC;
+    constexpr int ES = T::ESIZE;
+    constexpr int U = 4;                      // vectors in flight per thread and tensor
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+
+    bool valid, bad;
+    int64_t y;
+    row_status(p.labels, p.mask, row, p.V, valid, bad, y);
+
+    const int64_t V = p.V;
+    const int64_t rowoff = row * V;
+    const int mis = (int)((rowoff * ES) & 15);
+    int head = mis ? (16 - mis) / ES : 0;
+    if (head > V) head = (int)V;
+    const int64_t nbv = (V - head) / VEC;
+    const int tail = (int)(V - head - nbv * VEC);
+    const int n_extra = head + tail;
+    const char* xrow = static_cast<const char*>(p.logits) + rowoff * ES;
+    const char* trow = static_cast<const char*>(p.teacher) + rowoff * ES;
+    char* grow = static_cast<char*>(p.grad) + rowoff * ES;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(xrow + (int64_t)head * ES);
+    const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)head * ES);
+    u32x4* gv = reinterpret_cast<u32x4*>(grow + (int64_t)head * ES);
+
+    if (!valid) {
+        if (!p.accumulate) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            for (int64_t i = tid; i < nbv; i += kGradBlock) st_stream(gv + i, z);
+            for (int e = tid; e < n_extra; e += kGradBlock) {
+                const int64_t ei = e < head ? e : head + nbv * VEC + (e - head);
+                T::store1(grow, ei, 0.0f);
+            }
+        }
+        return;
+    }
+
+    const float* rec = p.row_rec + row * REC;
+    Rec r;
+    r.M = rec[R_M]; r.Z = rec[R_Z]; r.S = rec[R_S];
+    r.Mt = rec[R_MT]; r.Zt = rec[R_ZT]; r.SX = rec[R_SX]; r.St = rec[R_ST];
+    const float old = p.old_logprobs ? p.old_logprobs[row] : 0.f;
+    const float adv = p.advantages ? p.advantages[row] : 0.f;
+    Coefs k = row_coefs<TMODE, SOFTCAP>(p, r, y, rec[R_XY], old, adv);
+    if (p.row_coef != nullptr && p.w_g != 0.f) {
+        // GSPO: d(loss)/d(logp_t) = -coef_t / n_seg; d logp_t / d s_j = [j == y] - q_j
+        const uint32_t n_seg = p.ctrl[CTRL_NSEG];
+        const float e = n_seg > 0u ? p.grad_scale * p.k * p.w_g * p.row_coef[row] / (float)n_seg : 0.f;
+        k.alpha += e;
+        k.beta += e;
+        k.c0 += e;
+    }
+    if (p.ctrl[CTRL_ERROR] != 0u) {
+        // statistics or segments are not trustworthy: make the gradient say so
+        k.alpha = k.beta = k.c0 = __builtin_nanf("");
+    }
+
+    int64_t yv = -1;
+    int ly = 0;
+    if (y >= head && y < head + nbv * VEC) {
+        yv = (y - head) / VEC;
+        ly = (int)((y - head) % VEC);
+    }
+
+    for (int64_t base = 0; base < nbv; base += (int64_t)kGradBlock * U) {
+        u32x4 xs[U], ts[TMODE != TM_NONE ? U : 1], gs[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + u * kGradBlock + tid;
+            if (i < nbv) {
+                xs[u] = ld_stream(xv + i);
+                if (TMODE != TM_NONE) ts[u] = ld_stream(tv + i);
+                if (p.accumulate) gs[u] = ld_stream(gv + i);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + u * kGradBlock + tid;
+            if (i < nbv) {
+                float g[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    g[e] = grad_one<TMODE, SOFTCAP>(p, k, T::get(xs[u], e),
+                                                    TMODE != TM_NONE ? T::get(ts[u], e) : 0.f,
+                                                    (i == yv && e == ly) ? k.beta : 0.f);
+                if (p.accumulate) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) g[e] = T::get(gs[u], e) + g[e];
+                }
+                st_stream(gv + i, T::pack(g));
+            }
+        }
+    }
+    for (int e = tid; e < n_extra; e += kGradBlock) {
+        const int64_t ei = e < head ? e : head + nbv * VEC + (e - head);
+        const float x = T::load1(xrow, ei);
+        const float t = TMODE != TM_NONE ? T::load1(trow, ei) : 0.f;
+        float g = grad_one<TMODE, SOFTCAP>(p, k, x, t, ei == y ? k.beta : 0.f);
+        if (p.accumulate) g = T::load1(grow, ei) + g;
+        T::store1(grow, ei, g);
+    }
+}
+
+template <typename T, int TMODE, bool SOFTCAP>
+hipError_t launch_grad(const FusedParams& p, hipStream_t s) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((grad_kernel<T, TMODE, SOFTCAP>), dim3((unsigned)p.n_rows), dim3(kGradBlock), 0, s, p);
     return hipGetLastError();
 }
 

@@ -1,0 +1,16 @@
+// Load-mode gradient kernel instances for bf16 logits (every teacher mode, softcap on/off).
+#include "hl_device.cuh"
+
+namespace hl {
+
+GradLauncher get_grad_bf16(int tmode, bool softcap) {
+    switch (tmode) {
+        case TM_NONE: return softcap ? &launch_grad<BF16T, TM_NONE, true> : &launch_grad<BF16T, TM_NONE, false>;
+        case TM_FKL: return softcap ? &launch_grad<BF16T, TM_FKL, true> : &launch_grad<BF16T, TM_FKL, false>;
+        case TM_RKL: return softcap ? &launch_grad<BF16T, TM_RKL, true> : &launch_grad<BF16T, TM_RKL, false>;
+        case TM_FDCE: return softcap ? &launch_grad<BF16T, TM_FDCE, true> : &launch_grad<BF16T, TM_FDCE, false>;
+        default: return nullptr;
+    }
+}
+
+}  // namespace hl

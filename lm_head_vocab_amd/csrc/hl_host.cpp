@@ -26,6 +26,7 @@ struct hl_plan_s {
     int forced_block;
     Geometry geo;
     FusedLauncher fused;
+    GradLauncher grad;   // load-mode backward (GSPO plans)
     void* ws;
     size_t ws_bytes;
     bool ws_owned;
@@ -46,7 +47,8 @@ hl_status hip_fail(const char* where, hipError_t e) {
 }
 
 constexpr uint32_t kDistillBits = HL_FKL | HL_RKL | HL_FDCE;
-constexpr uint32_t kLossBits = HL_CE | HL_ZLOSS | kDistillBits | HL_GRPO | HL_ENTROPY;
+constexpr uint32_t kPolicyBits = HL_GRPO | HL_GSPO;
+constexpr uint32_t kLossBits = HL_CE | HL_ZLOSS | kDistillBits | kPolicyBits | HL_ENTROPY;
 constexpr uint32_t kKnownBits = kLossBits | HL_ACCUMULATE;
 constexpr int kTwoPerCuNvec = 10;         // 64 VGPRs at 1024 threads: two workgroups per CU
 constexpr int kTwoPerCuNvecSoftcap = 8;   // the softcap instances need a few more registers
@@ -54,9 +56,13 @@ constexpr int kTwoPerCuNvecSoftcap = 8;   // the softcap instances need a few mo
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-    size_t ctrl, chunk_rec, row_rec, rows, partials, total;
+    size_t ctrl, chunk_rec, row_rec, rows, partials, row_coef, seg_of_row, seg_rec, total;
 };
 
+// Workspace regions, in order: control words, split-vocab exchange words,
+// per-row softmax records, per-row values, reduction partials, and for GSPO
+// the per-row coefficient, the row -> segment map and the segment records
+// (sized for the most segments a call may pass, n_rows).
 Layout layout_for(const hl_plan_s* p, int64_t n) {
     Layout L;
     const size_t N = n > 0 ? (size_t)n : 0;
@@ -67,7 +73,11 @@ Layout layout_for(const hl_plan_s* p, int64_t n) {
     L.rows = L.row_rec + align256(N * REC * sizeof(float));
     L.partials = L.rows + align256(N * NCOL * sizeof(float));
     const size_t groups = N > 0 ? (N + kReduceBlock - 1) / kReduceBlock : 1;
-    L.total = L.partials + align256(groups * NSUM * sizeof(double));
+    L.row_coef = L.partials + align256(groups * NSUM * sizeof(double));
+    const bool gspo = (p->flags & HL_GSPO) != 0u;
+    L.seg_of_row = L.row_coef + (gspo ? align256(N * sizeof(float)) : 0);
+    L.seg_rec = L.seg_of_row + (gspo ? align256(N * sizeof(int32_t)) : 0);
+    L.total = L.seg_rec + (gspo ? align256(N * SEGREC * sizeof(double)) : 0);
     return L;
 }
 
@@ -162,6 +172,12 @@ hl_status choose(hl_plan_s* p) {
         p->geo = g;
     }
     p->fused = lookup(p->dtype, p->tmode, p->geo.block, p->geo.nvec, p->softcap > 0.f);
+    if (p->flags & HL_GSPO) {
+        const bool sc = p->softcap > 0.f;
+        p->grad = p->dtype == HL_F32 ? get_grad_f32(p->tmode, sc)
+                : p->dtype == HL_F16 ? get_grad_f16(p->tmode, sc) : get_grad_bf16(p->tmode, sc);
+        if (p->grad == nullptr) return HL_ERR_UNSUPPORTED;
+    }
     return p->fused ? HL_OK : HL_ERR_UNSUPPORTED;
 }
 
@@ -200,7 +216,8 @@ hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags
     if (dbits & (dbits - 1u)) return HL_ERR_INVALID_ARG;   // at most one distillation loss
     const bool distill = dbits != 0u;
     if (distill && !(finite(temperature) && temperature > 0.f)) return HL_ERR_INVALID_ARG;
-    if ((loss_flags & HL_GRPO) && !(finite(eps) && eps > 0.f && eps < 1.f)) return HL_ERR_INVALID_ARG;
+    if ((loss_flags & kPolicyBits) == kPolicyBits) return HL_ERR_INVALID_ARG;   // one policy loss
+    if ((loss_flags & kPolicyBits) && !(finite(eps) && eps > 0.f && eps < 1.f)) return HL_ERR_INVALID_ARG;
     if (!(finite(logit_scale) && logit_scale > 0.f)) return HL_ERR_INVALID_ARG;
     if (!(finite(softcap) && softcap >= 0.f)) return HL_ERR_INVALID_ARG;
     const hl_weights& w = *weights;
@@ -320,13 +337,28 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
                               const void* teacher_logits, const float* old_logprobs,
                               const float* advantages, void* grad_out,
                               float* scalars_out, hipStream_t stream) {
+    return hl_forward_backward_segments(plan, n_rows, logits, labels, mask, teacher_logits, old_logprobs,
+                                        advantages, nullptr, 0, grad_out, scalars_out, stream);
+}
+
+hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const void* logits,
+                                       const int64_t* labels, const uint8_t* mask,
+                                       const void* teacher_logits, const float* old_logprobs,
+                                       const float* advantages, const int32_t* seq_offsets,
+                                       int64_t n_segments, void* grad_out,
+                                       float* scalars_out, hipStream_t stream) {
     if (plan == nullptr || n_rows < 0 || scalars_out == nullptr) return HL_ERR_INVALID_ARG;
     if (n_rows > 0 && logits == nullptr) return HL_ERR_INVALID_ARG;
     const uint32_t f = plan->flags;
+    const bool gspo = (f & HL_GSPO) != 0u;
+    if (gspo) {
+        if (n_rows > 0 && seq_offsets == nullptr) return HL_ERR_MISSING_INPUT;
+        if (n_segments < 0 || n_segments > n_rows || (n_rows > 0 && n_segments < 1)) return HL_ERR_INVALID_ARG;
+    }
     if (n_rows > 0) {
-        if ((f & (HL_CE | HL_GRPO)) && labels == nullptr) return HL_ERR_MISSING_INPUT;
+        if ((f & (HL_CE | kPolicyBits)) && labels == nullptr) return HL_ERR_MISSING_INPUT;
         if ((f & kDistillBits) && teacher_logits == nullptr) return HL_ERR_MISSING_INPUT;
-        if ((f & HL_GRPO) && (old_logprobs == nullptr || advantages == nullptr)) return HL_ERR_MISSING_INPUT;
+        if ((f & kPolicyBits) && (old_logprobs == nullptr || advantages == nullptr)) return HL_ERR_MISSING_INPUT;
         if (!aligned16(logits)) return HL_ERR_INVALID_ARG;
         if (plan->tmode != TM_NONE && !aligned16(teacher_logits)) return HL_ERR_INVALID_ARG;
         if (grad_out != nullptr && !aligned16(grad_out)) return HL_ERR_INVALID_ARG;
@@ -383,8 +415,11 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
         fp.mask = mask;
         fp.old_logprobs = (f & HL_GRPO) ? old_logprobs : nullptr;
         fp.advantages = (f & HL_GRPO) ? advantages : nullptr;
-        fp.grad = grad_out;
+        // GSPO: the fused kernel only computes the row statistics; the
+        // gradient waits for the segment step
+        fp.grad = gspo ? nullptr : grad_out;
         fp.row_rec = row_rec;
+        fp.row_coef = nullptr;
         fp.chunk_words = chunk_words;
         fp.ctrl = ctrl;
         fp.n_rows = n_rows;
@@ -412,6 +447,30 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
             return hip_fail("hipEventRecord(before)", e);
         e = plan->fused(fp, grid, stream);
         if (e != hipSuccess) return hip_fail("fused kernel launch", e);
+        if (gspo) {
+            SeamParams sp;
+            sp.row_rec = row_rec;
+            sp.old_logprobs = old_logprobs;
+            sp.advantages = advantages;
+            sp.offsets = seq_offsets;
+            sp.seg_rec = reinterpret_cast<double*>(ws + L.seg_rec);
+            sp.row_coef = reinterpret_cast<float*>(ws + L.row_coef);
+            sp.seg_of_row = reinterpret_cast<int32_t*>(ws + L.seg_of_row);
+            sp.ctrl = ctrl;
+            sp.n_rows = n_rows;
+            sp.n_segments = n_segments;
+            sp.k = plan->logit_scale;
+            sp.cap = plan->softcap;
+            sp.eps = plan->eps;
+            e = launch_seam(sp, stream);
+            if (e != hipSuccess) return hip_fail("segment kernel launch", e);
+            if (grad_out != nullptr) {
+                fp.grad = grad_out;
+                fp.row_coef = sp.row_coef;
+                e = plan->grad(fp, stream);
+                if (e != hipSuccess) return hip_fail("gradient kernel launch", e);
+            }
+        }
         if (plan->ev_after && (e = hipEventRecord(plan->ev_after, stream)) != hipSuccess)
             return hip_fail("hipEventRecord(after)", e);
     }
@@ -422,6 +481,9 @@ hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits
     rp.labels = labels;
     rp.old_logprobs = (f & HL_GRPO) ? old_logprobs : nullptr;
     rp.advantages = (f & HL_GRPO) ? advantages : nullptr;
+    rp.seg_rec = gspo ? reinterpret_cast<const double*>(ws + L.seg_rec) : nullptr;
+    rp.seg_of_row = gspo ? reinterpret_cast<const int32_t*>(ws + L.seg_of_row) : nullptr;
+    rp.n_segments = gspo ? n_segments : 0;
     rp.rows = rows;
     rp.ctrl = ctrl;
     rp.k = plan->logit_scale;

@@ -15,7 +15,7 @@ constexpr bool fkl_like(int t) { return t == TM_FKL || t == TM_FDCE; }
 // Loss bits (same values as the public HL_* flags).
 enum : uint32_t {
     F_CE = 1u << 0, F_Z = 1u << 1, F_FKL = 1u << 2, F_RKL = 1u << 3,
-    F_GRPO = 1u << 4, F_ENT = 1u << 5, F_FDCE = 1u << 6, F_ACC = 1u << 16,
+    F_GRPO = 1u << 4, F_ENT = 1u << 5, F_FDCE = 1u << 6, F_GSPO = 1u << 7, F_ACC = 1u << 16,
     F_DISTILL = F_FKL | F_RKL | F_FDCE,
 };
 
@@ -35,8 +35,18 @@ constexpr int NSCALARS = 13;
 // and a valid flag.
 enum RecField : int { R_M = 0, R_Z, R_S, R_MT, R_ZT, R_SX, R_ST, R_XY, R_VALID, R_PAD, REC };
 
-// Control words at the start of the workspace.
-enum Ctrl : int { CTRL_NVALID = 0, CTRL_NBAD = 1, CTRL_EPOCH = 2, CTRL_ERROR = 3, CTRL_DONE = 4, NCTRL = 64 };
+// Control words at the start of the workspace. CTRL_NSEG counts the GSPO
+// segments that hold a valid row. CTRL_ERROR: 1 = a split-vocab row never saw
+// all of its chunks, 2 = malformed segment offsets.
+enum Ctrl : int {
+    CTRL_NVALID = 0, CTRL_NBAD = 1, CTRL_EPOCH = 2, CTRL_ERROR = 3, CTRL_DONE = 4, CTRL_NSEG = 5,
+    NCTRL = 64
+};
+
+// Per-segment GSPO record (fp64): loss, sequence ratio, clipped flag, k3 of
+// the ratio, segment advantage, nonempty flag, the per-token coefficient
+// act * A * s / n_i, and the valid-token count n_i.
+enum SegField : int { SG_LOSS = 0, SG_RATIO, SG_CLIP, SG_K3, SG_ADV, SG_NONEMPTY, SG_DERIV, SG_COUNT, SEGREC };
 
 // Split-vocab exchange: each chunk publishes its 7 statistics as 64-bit words
 // (float bits low, call epoch high); at most kMaxChunks chunks per row.
@@ -61,6 +71,7 @@ struct FusedParams {
     float* row_rec;           // [N, REC]
     uint64_t* chunk_words;    // [N, C, XWORDS]
     uint32_t* ctrl;           // [NCTRL]
+    const float* row_coef;    // [N] GSPO label-column coefficient per row (gradient kernel only)
     int64_t n_rows;
     int64_t V;
     int chunks;
@@ -99,6 +110,9 @@ struct ReduceParams {
     const int64_t* labels;
     const float* old_logprobs;
     const float* advantages;
+    const double* seg_rec;    // [S, SEGREC] (GSPO only)
+    const int32_t* seg_of_row;// [N] (GSPO only)
+    int64_t n_segments;
     uint32_t* ctrl;
     float* rows;              // [N, NCOL] per-row values (written)
     float* scalars;
@@ -109,7 +123,26 @@ struct ReduceParams {
     float divisor;
 };
 
+constexpr int kSeamBlock = 256;     // one wave per segment, 4 segments per workgroup
+
+struct SeamParams {
+    const float* row_rec;     // [N, REC] from the forward pass
+    const float* old_logprobs;
+    const float* advantages;
+    const int32_t* offsets;   // [S + 1]
+    double* seg_rec;          // [S, SEGREC] (written)
+    float* row_coef;          // [N] (written)
+    int32_t* seg_of_row;      // [N] (written)
+    uint32_t* ctrl;
+    int64_t n_rows;
+    int64_t n_segments;
+    float k, cap, eps;
+};
+
+constexpr int kGradBlock = 512;     // threads per row in the load-mode gradient kernel
+
 typedef hipError_t (*FusedLauncher)(const FusedParams&, dim3 grid, hipStream_t);
+typedef hipError_t (*GradLauncher)(const FusedParams&, hipStream_t);
 
 // One getter per (dtype, teacher mode) translation unit; nullptr when the
 // requested (block, nvec, softcap) instance does not exist.
@@ -126,8 +159,14 @@ FusedLauncher get_fused_f32_fdce(int block, int nvec, bool softcap);
 FusedLauncher get_fused_bf16_fdce(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f16_fdce(int block, int nvec, bool softcap);
 
+// Load-mode gradient kernels, one getter per dtype: nullptr for an unknown mode.
+GradLauncher get_grad_f32(int tmode, bool softcap);
+GradLauncher get_grad_bf16(int tmode, bool softcap);
+GradLauncher get_grad_f16(int tmode, bool softcap);
+
 hipError_t launch_count(const CountParams& p, hipStream_t s);  // grid grows when p.fresh
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
+hipError_t launch_seam(const SeamParams& p, hipStream_t s);
 
 // Vector counts that have a kernel instance, per block size.
 constexpr int kSmallBlock = 256;

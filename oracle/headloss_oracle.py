@@ -310,7 +310,8 @@ def segment_of_rows(offsets, n_rows: int) -> np.ndarray:
     return seg
 
 
-def gspo_seam(spec: Spec, logp, old_logprobs, advantages, valid, offsets) -> dict:
+def gspo_seam(spec: Spec, logp, old_logprobs, advantages, valid, offsets,
+              n_seg_total: int | None = None) -> dict:
     """Per-segment GSPO values and d(batch GSPO loss)/d(logp_t) per row.
 
     For segment i with valid tokens T_i (n_i = |T_i| > 0), READINGS["gspo"]:
@@ -322,6 +323,8 @@ def gspo_seam(spec: Spec, logp, old_logprobs, advantages, valid, offsets) -> dic
     Its derivative with respect to logp_t (t in T_i) is -act_i A_i s_i /
     (n_i n_seg), act_i as for the per-token clip (READINGS["grpo_ties"]).
     Segments with no valid token contribute nothing and are not counted.
+    ``n_seg_total`` replaces n_seg when the rows given are only some whole
+    segments of a larger batch (sampled checks of large batches).
     """
     logp = np.asarray(logp, dtype=np.float64).reshape(-1)
     old = np.asarray(old_logprobs, dtype=np.float64).reshape(-1)
@@ -341,7 +344,7 @@ def gspo_seam(spec: Spec, logp, old_logprobs, advantages, valid, offsets) -> dic
             sum_d[i] += logp[t] - old[t]
             sum_a[i] += A[t]
     nonempty = n_i > 0
-    n_seg = int(nonempty.sum())
+    n_seg = int(nonempty.sum()) if n_seg_total is None else int(n_seg_total)
     safe_n = np.where(nonempty, n_i, 1)
     log_s = np.where(nonempty, sum_d / safe_n, 0.0)
     ratio = np.exp(log_s)

@@ -25,8 +25,8 @@ def _plan(V=1000, dtype=hl.HL_BF16, flags=hl.CE, w=None, tau=1.0, eps=0.2, scale
 
 def test_every_declared_symbol_is_exported():
     names = hl.exported_functions_in_header()
-    assert {"hl_plan", "hl_forward_backward", "hl_plan_destroy", "hl_workspace_bytes",
-            "hl_plan_set_workspace", "hl_status_str"} <= set(names)
+    assert {"hl_plan", "hl_forward_backward", "hl_forward_backward_segments", "hl_plan_destroy",
+            "hl_workspace_bytes", "hl_plan_set_workspace", "hl_status_str"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -54,6 +54,9 @@ def test_status_strings():
     (dict(flags=hl.GRPO, eps=0.0), hl.HL_ERR_INVALID_ARG),
     (dict(flags=hl.GRPO, eps=1.0), hl.HL_ERR_INVALID_ARG),
     (dict(flags=hl.GRPO, eps=math.nan), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.GSPO, eps=0.0), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.GSPO, eps=1.5), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.GRPO | hl.GSPO), hl.HL_ERR_INVALID_ARG),
     (dict(scale=0.0), hl.HL_ERR_INVALID_ARG),
     (dict(scale=-1.0), hl.HL_ERR_INVALID_ARG),
     (dict(scale=math.inf), hl.HL_ERR_INVALID_ARG),
@@ -159,6 +162,29 @@ def test_forward_backward_host_checks_enqueue_nothing():
     assert fb(h, 4, fake, fake, None, fake, fake, fake, fake, fake, None) == hl.HL_ERR_WORKSPACE
     lib.hl_plan_destroy(h)
     lib.hl_plan_destroy(None)
+
+
+def test_segment_call_host_checks_enqueue_nothing():
+    st, h = _plan(V=64, flags=hl.CE | hl.GSPO | hl.RKL, w=Weights(1, 0, 1, 1, 1, 0))
+    assert st == 0
+    fake = VP(4096)
+    fs = lib.hl_forward_backward_segments
+    fb = lib.hl_forward_backward
+    # a GSPO plan needs segments: the plain entry point cannot serve it
+    assert fb(h, 4, fake, fake, None, fake, fake, fake, fake, fake, None) == hl.HL_ERR_MISSING_INPUT
+    assert fs(h, 4, fake, fake, None, fake, fake, fake, None, 2, fake, fake, None) == hl.HL_ERR_MISSING_INPUT
+    for n_seg in (0, 5, -1):   # 1 <= n_segments <= n_rows
+        assert fs(h, 4, fake, fake, None, fake, fake, fake, fake, n_seg, fake, fake, None) == hl.HL_ERR_INVALID_ARG
+    assert fs(h, 4, fake, fake, None, None, fake, fake, fake, 2, fake, fake, None) == hl.HL_ERR_MISSING_INPUT
+    assert fs(h, 4, fake, fake, None, fake, None, fake, fake, 2, fake, fake, None) == hl.HL_ERR_MISSING_INPUT
+    assert fs(h, 4, fake, fake, None, fake, fake, None, fake, 2, fake, fake, None) == hl.HL_ERR_MISSING_INPUT
+    assert lib.hl_plan_set_workspace(h, fake, 8) == hl.HL_OK
+    assert fs(h, 4, fake, fake, None, fake, fake, fake, fake, 2, fake, fake, None) == hl.HL_ERR_WORKSPACE
+    # the GSPO regions grow the workspace with the row count
+    st2, h2 = _plan(V=64, flags=hl.CE | hl.GRPO, w=Weights(1, 0, 1, 1, 1, 0))
+    assert lib.hl_workspace_bytes(h, 1000) > lib.hl_workspace_bytes(h2, 1000)
+    lib.hl_plan_destroy(h)
+    lib.hl_plan_destroy(h2)
 
 
 def test_binding_marshalling_errors_without_gpu():

@@ -5,6 +5,9 @@ label mixes, masking rates, per-sequence advantages, teacher correlation) of
 the five benchmark configurations, drawn with torch generators so that the
 same seed gives the same tensors on the GPU and on the host.
 
+Segments (GSPO) are contiguous row ranges given by int32 offsets; the
+benchmark segments are the workload's sequences.
+
 This module holds none of the loss arithmetic. GRPO needs old log-probs near
 the current policy's label log-prob; the generator draws only the noise
 (``old_noise``) and the caller adds the label log-prob it computes itself
@@ -20,7 +23,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-CE, ZLOSS, FKL, RKL, GRPO, ENTROPY, FDCE, ACCUMULATE = 1, 2, 4, 8, 16, 32, 64, 1 << 16
+CE, ZLOSS, FKL, RKL, GRPO, ENTROPY, FDCE, GSPO, ACCUMULATE = 1, 2, 4, 8, 16, 32, 64, 128, 1 << 16
 
 
 @dataclass(frozen=True)
@@ -82,6 +85,11 @@ WORKLOADS = {
         description="GRPO (eps 0.2) + z-loss (0.01) + entropy + ratio/clamp stats; 32 x 512 tokens; "
                     "logits ~ N(0, 2.5^2); uniform labels; old = label logprob + N(0, 0.05^2); "
                     "advantage per sequence ~ N(0, 1); 5% of tokens masked by the mask byte"),
+    "gspo_z_ent_bf16": Workload(
+        "gspo_z_ent_bf16", N=16384, V=151936, dtype="bf16", flags=GSPO | ZLOSS | ENTROPY,
+        weights=dict(ce=0.0, z=0.01, grpo=1.0), eps=0.002, seq_len=512, old_noise_std=0.05,
+        description="the GRPO inputs (32 x 512 tokens) with GSPO over the 32 sequences; eps 0.002 "
+                    "(a sequence ratio moves by about 0.05 / sqrt(512), so some sequences clip)"),
     "all_combined_bf16": Workload(
         "all_combined_bf16", N=32768, V=256000, dtype="bf16",
         flags=CE | ZLOSS | RKL | GRPO | ENTROPY | ACCUMULATE,
@@ -102,7 +110,8 @@ HEADLINE = "grpo_z_ent_bf16"
 
 def seed_for(name: str, subcase: int = 0) -> int:
     order = ["ce_z_tiny_f32", "ce_z_bf16", "ce_fkl_bf16", "grpo_z_ent_bf16", "all_combined_bf16"]
-    base = {"ce_rkl_bf16": "ce_fkl_bf16", "ce_fdce_bf16": "ce_fkl_bf16", "ce_z_f16": "ce_z_bf16"}.get(name, name)
+    base = {"ce_rkl_bf16": "ce_fkl_bf16", "ce_fdce_bf16": "ce_fkl_bf16", "ce_z_f16": "ce_z_bf16",
+            "gspo_z_ent_bf16": "grpo_z_ent_bf16"}.get(name, name)
     return 1000 * (order.index(base) + 1) + subcase
 
 
@@ -116,9 +125,9 @@ def generate(w: Workload | str, device="cpu", seed: int | None = None, n_rows: i
              chunk_rows: int = 1024) -> dict:
     """Draw one batch of inputs for workload ``w`` (``n_rows`` overrides N).
 
-    Returns a dict with logits, labels, mask, teacher, advantages, old_noise
-    and grad_init (None where the workload has no such input). Float tensors
-    are drawn in fp32 and cast once to the workload dtype.
+    Returns a dict with logits, labels, mask, teacher, advantages, old_noise,
+    grad_init and seq_offsets (None where the workload has no such input).
+    Float tensors are drawn in fp32 and cast once to the workload dtype.
     """
     if isinstance(w, str):
         w = WORKLOADS[w]
@@ -129,7 +138,7 @@ def generate(w: Workload | str, device="cpu", seed: int | None = None, n_rows: i
     V = w.V
     dt = w.torch_dtype
     out = {"logits": None, "labels": None, "mask": None, "teacher": None,
-           "advantages": None, "old_noise": None, "grad_init": None}
+           "advantages": None, "old_noise": None, "grad_init": None, "seq_offsets": None}
 
     def rows_normal(std):
         t = torch.empty((N, V), dtype=dt, device=device)
@@ -175,7 +184,7 @@ def generate(w: Workload | str, device="cpu", seed: int | None = None, n_rows: i
         # argmax of the stored teacher row (first maximal index on ties)
         amax = torch.argmax(t.float(), dim=1)
         out["labels"] = torch.where(bernoulli(N, 0.6), amax, uniform_labels(N))
-    elif w.name == "grpo_z_ent_bf16":
+    elif w.name in ("grpo_z_ent_bf16", "gspo_z_ent_bf16"):
         out["logits"] = rows_normal(2.5)
         out["labels"] = uniform_labels(N)
         out["mask"] = (~bernoulli(N, 0.05)).to(torch.uint8)
@@ -203,7 +212,30 @@ def generate(w: Workload | str, device="cpu", seed: int | None = None, n_rows: i
         out["grad_init"] = rows_normal(ALL_COMBINED_GRAD_SIGMA)
     else:
         raise KeyError(w.name)
+    if w.flags & GSPO:
+        starts = torch.arange(0, N, w.seq_len, device=device)
+        out["seq_offsets"] = torch.cat([starts, torch.tensor([N], device=device)]).to(torch.int32)
     return out
+
+
+def segment_offsets(N: int, seed: int, max_len: int = 8, empty_frac: float = 0.1,
+                    device="cpu") -> torch.Tensor:
+    """Seeded contiguous segments covering N rows: int32 offsets [S + 1] from 0
+    to N with lengths in [1, max_len], some empty segments mixed in, and never
+    more segments than rows."""
+    g = _gen(torch.device("cpu"), seed)
+    offs = [0]
+    while offs[-1] < N:
+        if len(offs) - 1 < N - 1 and torch.rand((1,), generator=g).item() < empty_frac:
+            offs.append(offs[-1])
+        ln = int(torch.randint(1, max_len + 1, (1,), generator=g).item())
+        offs.append(min(N, offs[-1] + ln))
+    while len(offs) - 1 > max(N, 1):        # drop empty segments beyond the row count
+        for i in range(1, len(offs)):
+            if offs[i] == offs[i - 1]:
+                del offs[i]
+                break
+    return torch.tensor(offs, dtype=torch.int32, device=device)
 
 
 def algorithmic_bytes(w: Workload, n_valid_rows: int, n_rows: int | None = None,
@@ -221,10 +253,13 @@ def algorithmic_bytes(w: Workload, n_valid_rows: int, n_rows: int | None = None,
             b += n_valid_rows * 2 * row
         else:
             b += N * row
+    if w.flags & GSPO:
+        # the backward reloads every valid row once the segment ratios are known
+        b += n_valid_rows * tensors_read * row
     side = 8  # labels
-    if w.name == "grpo_z_ent_bf16":
+    if w.name in ("grpo_z_ent_bf16", "gspo_z_ent_bf16"):
         side += 1  # mask byte
-    if w.flags & GRPO:
+    if w.flags & (GRPO | GSPO):
         side += 8  # old_logprobs + advantages
     return b + N * side
 
