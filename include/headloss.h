@@ -232,8 +232,8 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
 
 /* Device pointer to the per-row values of the plan's last call: float
  * [n_rows, HL_NUM_ROW_COLS] inside the workspace (masked rows are all 0,
- * HL_R_VALID is 1 for counted rows; with HL_GSPO the policy columns hold the
- * row's segment values). Valid until the next call with the plan
+ * HL_R_VALID is 1 for counted rows; HL_R_ENTROPY is 0 unless HL_ENTROPY is
+ * requested; with HL_GSPO the policy columns hold the row's segment values). Valid until the next call with the plan
  * or a workspace change. These are the per-token values the batch means of
  * #549 Loss coverage are taken over (new_logprobs, entropy, ratio, ...).
  * Returns NULL when the plan has no workspace yet. */

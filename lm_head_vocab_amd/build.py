@@ -3,7 +3,10 @@
 Usage: python -m lm_head_vocab_amd.build  [-j JOBS]
 
 Every call recompiles every source (no stale objects), in parallel, then
-links the shared library next to this file.
+links the shared library next to this file. Each kernel's resource report is
+checked: a kernel that spills vector registers or uses private (scratch)
+memory fails the build, since the kernels are designed to keep their row slices in
+registers and a spill would silently move them to memory.
 """
 
 from __future__ import annotations
@@ -11,6 +14,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -40,13 +44,32 @@ def sources():
     return out
 
 
+def resource_problems(remarks: str) -> list[str]:
+    """Kernels whose resource report shows VGPR spills or scratch use. (SGPR
+    spills go to VGPR lanes, not to memory, and are allowed.)"""
+    bad = []
+    name = None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill): (\d+)", line)
+        if m and name and int(m.group(2)) > 0:
+            bad.append(f"{name}: {m.group(1)} = {m.group(2)}")
+    return bad
+
+
 def _compile(src: str) -> tuple[str, float]:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     t0 = time.time()
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    bad = resource_problems(res.stderr)
+    if bad:
+        raise RuntimeError(f"{os.path.basename(src)}: kernels spill or use scratch memory:\n  " + "\n  ".join(bad))
     return obj, time.time() - t0
 
 

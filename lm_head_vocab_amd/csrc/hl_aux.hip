@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
             const double l2Z = log2(Z);
             const double lse = ((double)rec[R_M] + l2Z) * LN2;
             v[RC_Z] = lse * lse;
-            v[RC_ENT] = LN2 * (l2Z - (double)rec[R_S] / Z);
+            if (f & F_ENT) v[RC_ENT] = LN2 * (l2Z - (double)rec[R_S] / Z);   // S is formed only then
             if (f & F_DISTILL) {
                 const double Zt = rec[R_ZT];
                 const double l2Zt = log2(Zt);

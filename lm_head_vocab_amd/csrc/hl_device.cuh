@@ -23,6 +23,8 @@
 // head-loss kernel (torch.compile)", section Approach).
 #pragma once
 
+#include <type_traits>
+
 #include "hl_internal.h"
 
 namespace hl {
@@ -395,6 +397,7 @@ __device__ __forceinline__ float grad_one(const FusedParams& p, const Coefs& k, 
 // Bounded wait for the sibling chunks of a row (split-vocab variant only).
 constexpr uint32_t kSpinLimit = 1u << 20;
 
+
 // Waves per SIMD the register allocation must allow (the second
 // __launch_bounds__ argument): student-only slices of at most 10 vectors per
 // thread (8 with softcap) are held to 64 VGPRs, i.e. 8 waves per SIMD, so that
@@ -508,31 +511,39 @@ void fused_kernel(const FusedParams p) {
         if (TMODE != TM_NONE) te = T::load1(trow, eidx);
     }
 
-    // ---- pass 1a: max of the raw logits (the transform is increasing) ----
+    // ---- pass 1: sums relative to a provisional wave shift, log2 domain ----
+    // The shift is the wave's maximum over its first vector, not the row
+    // maximum: any shift gives the same statistics once records are merged
+    // with rescaling, and this one needs no separate pass over the slice.
+    // If some term could overflow (the wave's sum exceeds 2^64, i.e. an
+    // element lies more than 64 above the shift; the sum is also non-finite
+    // for Inf or NaN inputs) or the wave holds no element of its first
+    // vector, the wave takes the true maximum and sums again. The entropy sum
+    // S is formed only when the entropy metric is requested.
     float mx = kNegInf, mt = kNegInf;
-#pragma unroll
-    for (int v = 0; v < NVEC; ++v) {
-        if (tid < nv - v * BLOCK) {
-            mx = T::vmax(mx, xs[v]);
-            if (TMODE != TM_NONE) mt = T::vmax(mt, ts[v]);
-        }
+    if (tid < nv) {
+        mx = T::vmax(mx, xs[0]);
+        if (TMODE != TM_NONE) mt = T::vmax(mt, ts[0]);
     }
-    if (has_e) {
-        mx = fmaxf(mx, xe);
-        if (TMODE != TM_NONE) mt = fmaxf(mt, te);
-    }
-    mx = wave_max(mx);
-    const float M = SOFTCAP ? (p.cap * hl_tanh(mx * p.kc)) * kLog2e : mx * p.K1;
-    float Mt = 0.f;
-    if (TMODE != TM_NONE) Mt = wave_max(mt) * p.K2;
+    const float mx0 = wave_max(mx);
+    const float mt0 = TMODE != TM_NONE ? wave_max(mt) : 0.f;
+    auto shift_of = [&](float m) -> float {
+        return SOFTCAP ? (p.cap * hl_tanh(m * p.kc)) * kLog2e : m * p.K1;
+    };
+    float M = shift_of(mx0);
+    float Mt = TMODE != TM_NONE ? mt0 * p.K2 : 0.f;
+    const bool early = mx0 != kNegInf && (TMODE == TM_NONE || mt0 != kNegInf);
+    const bool want_s = (p.flags & F_ENT) != 0u;
 
-    // ---- pass 1b: sums relative to the wave shift, in the log2 domain ----
     float Z = 0.f, S = 0.f, Zt = 0.f, SX = 0.f, St = 0.f;
-    auto accumulate = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st) {
+    // one call site per variant (below), so the slice stays in registers
+    // one term of every sum; the entropy term only when WS
+    auto term = [&](auto want_s_tag, float x, float t, float& z, float& s, float& zt, float& sx, float& st) {
+        constexpr bool WS = decltype(want_s_tag)::value;
         const float a = SOFTCAP ? fmaf(p.cap * hl_tanh(x * p.kc), kLog2e, -M) : fmaf(x, p.K1, -M);
         const float ex = fast_exp2(a);
         z += ex;
-        s = fmaf(ex, a, s);
+        if (WS) s = fmaf(ex, a, s);
         if (TMODE != TM_NONE) {
             const float u = fmaf(t, p.K2, -Mt);
             const float et = fast_exp2(u);
@@ -542,25 +553,73 @@ void fused_kernel(const FusedParams p) {
             if (TMODE == TM_FDCE) st = fmaf(et, u, st);
         }
     };
+    auto accumulate = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st) {
+        term(std::true_type(), x, t, z, s, zt, sx, st);
+    };
+    // one call site per variant (below), so the slice stays in registers
+    auto sweep = [&](auto want_s_tag) __attribute__((always_inline)) {
+        constexpr bool WS = decltype(want_s_tag)::value;
+        auto acc = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st) {
+            term(want_s_tag, x, t, z, s, zt, sx, st);
+        };
+        float z0 = 0.f, s0 = 0.f, zt0 = 0.f, sx0 = 0.f, st0 = 0.f;
 #pragma unroll
-    for (int v = 0; v < NVEC; ++v) {
-        if (tid < nv - v * BLOCK) {
-            float z = 0.f, s = 0.f, zt = 0.f, sx = 0.f, st = 0.f;
+        for (int v = 0; v < NVEC; ++v) {
+            if (tid < nv - v * BLOCK) {
+                float z = 0.f, s = 0.f, zt = 0.f, sx = 0.f, st = 0.f;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                accumulate(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z, s, zt, sx, st);
-            Z += z; S += s; Zt += zt; SX += sx; St += st;
+                for (int e = 0; e < VEC; ++e)
+                    acc(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z, s, zt, sx, st);
+                z0 += z; s0 += s; zt0 += zt; sx0 += sx; st0 += st;
+            }
         }
+        if (has_e) acc(xe, te, z0, s0, zt0, sx0, st0);
+        Z = wave_sum(z0);
+        if (WS) S = wave_sum(s0);
+        if (TMODE != TM_NONE) {
+            Zt = wave_sum(zt0);
+            SX = wave_sum(sx0);
+        }
+        if (TMODE == TM_FDCE) St = wave_sum(st0);
+    };
+    if (early) {
+        if (want_s) sweep(std::true_type());
+        else sweep(std::false_type());
     }
-    if (has_e) accumulate(xe, te, Z, S, Zt, SX, St);
-
-    Z = wave_sum(Z);
-    S = wave_sum(S);
-    if (TMODE != TM_NONE) {
-        Zt = wave_sum(Zt);
-        SX = wave_sum(SX);
+    constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
+    if (!early || !(Z <= kSumLimit) || (TMODE != TM_NONE && !(Zt <= kSumLimit))) {
+        // Rare: the true maximum, then the sums from it. This path reads the
+        // slice again from memory so that the register copy keeps a single
+        // use above (the slice must not be spilled to make room for a second).
+        mx = kNegInf;
+        mt = kNegInf;
+        for (int i = tid; i < nv; i += BLOCK) {
+            mx = T::vmax(mx, xv[i]);
+            if (TMODE != TM_NONE) mt = T::vmax(mt, tv[i]);
+        }
+        if (has_e) {
+            mx = fmaxf(mx, xe);
+            if (TMODE != TM_NONE) mt = fmaxf(mt, te);
+        }
+        M = shift_of(wave_max(mx));
+        if (TMODE != TM_NONE) Mt = wave_max(mt) * p.K2;
+        float z0 = 0.f, s0 = 0.f, zt0 = 0.f, sx0 = 0.f, st0 = 0.f;
+        for (int i = tid; i < nv; i += BLOCK) {
+            const u32x4 w = xv[i];
+            u32x4 wt = {0u, 0u, 0u, 0u};
+            if (TMODE != TM_NONE) wt = tv[i];
+            for (int e = 0; e < VEC; ++e)
+                accumulate(T::get(w, e), TMODE != TM_NONE ? T::get(wt, e) : 0.f, z0, s0, zt0, sx0, st0);
+        }
+        if (has_e) accumulate(xe, te, z0, s0, zt0, sx0, st0);
+        Z = wave_sum(z0);
+        S = wave_sum(s0);
+        if (TMODE != TM_NONE) {
+            Zt = wave_sum(zt0);
+            SX = wave_sum(sx0);
+        }
+        if (TMODE == TM_FDCE) St = wave_sum(st0);
     }
-    if (TMODE == TM_FDCE) St = wave_sum(St);
     if (lane == 0) {
         s_rec[wave][0] = M;
         s_rec[wave][1] = Z;

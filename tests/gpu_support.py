@@ -146,14 +146,15 @@ def assert_scalars(spec, got, ref, dtype, vals=None, valid=None, skip=()):
     assert not bad, f"scalar errors above {rel}: {bad}\n got={got}\n ref={ref}"
 
 
-def grad_check(got, ref, dtype, labels=None, valid=None, base=None):
-    """Compare a gradient tensor with the oracle's. Returns a dict of metrics."""
+def grad_check(got, ref, dtype, labels=None, valid=None, base=None, f32_abs=None):
+    """Compare a gradient tensor with the oracle's. Returns a dict of metrics.
+    ``f32_abs`` replaces the fp32 absolute gate where a test states why."""
     g = to_np(got)
     r = ref
     out = {}
     if dtype == "f32":
         out["max_abs"] = float(np.max(np.abs(g - r))) if g.size else 0.0
-        assert out["max_abs"] <= TOL["f32"]["grad_abs"], out
+        assert out["max_abs"] <= (f32_abs or TOL["f32"]["grad_abs"]), out
         return out
     diff = g - r
     den = np.sqrt(np.mean(r * r)) if r.size else 0.0

@@ -86,7 +86,7 @@ def _to_dev(inp):
     return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
 
 
-def _check_small(spec, inp, dtype, chunks=0, grad_mode=None):
+def _check_small(spec, inp, dtype, chunks=0, grad_mode=None, f32_abs=None, skip_scalars=()):
     grad_mode = grad_mode or ("accumulate" if spec.has(ACC) else "overwrite")
     plan = make_plan(spec, TDT[dtype], chunks)
     say(f"[gpu] N={inp['logits'].shape[0]} V={spec.V} {dtype} flags={spec.flags:#x} "
@@ -100,7 +100,8 @@ def _check_small(spec, inp, dtype, chunks=0, grad_mode=None):
                                    to_np(inp["labels"]).astype(np.int64) if inp["labels"] is not None else None,
                                    to_np(inp["mask"]))
     boundary = _grpo_boundary_rows(spec, inp) & valid
-    assert_scalars(spec, sc, ref_sc, dtype, vals, valid, skip=("CLIPFRAC",) if boundary.any() else ())
+    assert_scalars(spec, sc, ref_sc, dtype, vals, valid,
+                   skip=tuple(skip_scalars) + (("CLIPFRAC",) if boundary.any() else ()))
     if spec.has(GRPO) and not boundary.any():
         n = ref_sc[SLOT["N_VALID"]] if spec.divisor <= 0 else spec.divisor
         assert round(sc[SLOT["CLIPFRAC"]] * n) == round(ref_sc[SLOT["CLIPFRAC"]] * n)
@@ -109,7 +110,8 @@ def _check_small(spec, inp, dtype, chunks=0, grad_mode=None):
     gk = g.detach().cpu()
     keep = ~boundary
     metrics = grad_check(gk[torch.from_numpy(keep)], ref_g[keep], dtype,
-                         labels=to_np(inp["labels"])[keep] if inp["labels"] is not None else None)
+                         labels=to_np(inp["labels"])[keep] if inp["labels"] is not None else None,
+                         f32_abs=f32_abs)
     # masked rows: +0.0 in overwrite mode, bit-identical existing values in accumulate mode
     inval = torch.from_numpy(~valid)
     if grad_mode == "overwrite":
@@ -187,6 +189,25 @@ def test_forced_variants(combo, variant):
     grad_check(g.cpu(), ref_g, "bf16", labels=to_np(inp["labels"]))
 
 
+@pytest.mark.parametrize("variant", [(5, 512), (7, 512), (8, 512), (9, 512)])
+@pytest.mark.parametrize("combo", ["ce_fkl", "all_rkl", "all_fdce"])
+def test_teacher_slice_layouts(combo, variant):
+    """Teacher slices of 6, 8 and 10 vectors per thread at 512 threads, at a
+    full-length vocabulary row."""
+    chunks, block = variant
+    spec, inp = _small("bf16", combo, 4, 151936, seed=61 + chunks, softcap=12.0, scale=0.9)
+    plan = make_plan(spec, torch.bfloat16)
+    plan.set_variant(chunks, block)
+    say(f"[gpu] teacher layout {variant} -> {plan.describe()}")
+    sc, g = run_hip(plan, _to_dev(inp), "overwrite")
+    ref_sc, ref_g, _ = run_oracle(spec, inp)
+    valid, _ = oracle.row_validity(4, spec.V, to_np(inp["labels"]).astype(np.int64), None)
+    vals = oracle.row_values(spec, to_np(inp["logits"]), to_np(inp["labels"]).astype(np.int64),
+                             to_np(inp["teacher"]), to_np(inp.get("old_logprobs")), to_np(inp.get("advantages")))
+    assert_scalars(spec, sc, ref_sc, "bf16", vals, valid)
+    grad_check(g.cpu(), ref_g, "bf16", labels=to_np(inp["labels"]))
+
+
 @pytest.mark.parametrize("chunks", [0, 3])
 @pytest.mark.parametrize("combo", ["all_rkl", "all_fkl", "all_fdce"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
@@ -240,6 +261,64 @@ def test_split_vocab_calls_with_changing_batch_sizes():
 def test_split_vocab_accumulate_and_masking():
     spec, inp = _small("bf16", "all_rkl", 12, 50003, seed=9, accumulate=True, mask_frac=0.3, bad_labels=2)
     _check_small(spec, inp, "bf16", chunks=4)
+
+
+@pytest.mark.parametrize("chunks", [0, 3])
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "all_fdce"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_outlier_logits(dtype, combo, chunks):
+    """A logit (or teacher logit) far above the rest of its row, placed after
+    the first vector of a wave, in the ragged head/tail, or in the first
+    vector: the softmax shift is taken from each wave's first vector, and a
+    wave whose sums would overflow from that shift sums again from its true
+    maximum."""
+    N, V = 10, 20011
+    spec, inp = _small(dtype, combo, N, V, seed=71 + chunks, mask_frac=0.0, ignore_frac=0.0)
+    # student outlier 60 (x log2 e = 87, beyond 64 above a first vector whose
+    # maximum is about 9 in log2 units), half of it on odd rows (35 above:
+    # kept from the provisional shift); teacher outlier 100 (/ tau 1.5 =
+    # 96 log2 units)
+    big, tbig = 60.0, 100.0
+    x = inp["logits"].float()
+    t = inp["teacher"].float() if inp["teacher"] is not None else None
+    # row r: an outlier at a position spread over the row (first vector,
+    # later vectors, the last element of the row, i.e. the ragged tail)
+    pos = [0, 5, 700, 4099, 9000, 15000, 19999, V - 1, 3, 12345]
+    for r in range(N):
+        x[r, pos[r]] = big if r % 2 == 0 else big / 2
+        if t is not None and r % 3 == 0:
+            t[r, pos[(r + 4) % N]] = tbig
+    inp["logits"] = x.to(TDT[dtype])
+    if t is not None:
+        inp["teacher"] = t.to(TDT[dtype])
+    if spec.has(GRPO):
+        inp["old_logprobs"] = oracle_old_logprobs(spec, inp["logits"], inp["labels"], inp["old_noise"])
+    # fp32: the exponent argument x k log2(e) - lse2 is a difference of two
+    # numbers near |x k log2 e|, so its rounding error (about 2 ulps of that
+    # magnitude) makes each softmax entry's relative error up to
+    # 2 ln2 |x k log2 e| 2^-24; the absolute gate scales with it and with the
+    # largest gradient entry (1e-6 is the gate for ordinary logit ranges)
+    #
+    # Entropy: these rows are nearly one-hot, so the exact entropy is ~1e-7
+    # nats and the fp32 record's Z sits at 1 + O(1e-9); each rounding of Z
+    # moves log Z by up to 2^-24 nats, and a row's record goes through up to
+    # ~20 merges, so the entropy is checked to 2e-6 nats absolute instead of
+    # relative to its near-zero value.
+    ref_sc, ref_g, _ = run_oracle(spec, inp)
+    xmax = float(inp["logits"].float().abs().max()) * spec.logit_scale * 1.4427
+    f32_abs = max(1e-6, 2 * 0.6931 * xmax * 2.0 ** -23 * float(np.max(np.abs(ref_g))))
+    _, sc, _ = _check_small(spec, inp, dtype, chunks=chunks, f32_abs=f32_abs, skip_scalars=("ENTROPY",))
+    e = SLOT["ENTROPY"]
+    assert abs(sc[e] - ref_sc[e]) <= 2e-6 + TOL[dtype]["scalar_rel"] * abs(ref_sc[e]), (sc[e], ref_sc[e])
+    spec_c, inp_c = _small(dtype, combo, N, V, seed=71 + chunks, softcap=30.0, scale=0.5)
+    inp_c["logits"] = inp["logits"]
+    inp_c["teacher"] = inp["teacher"]
+    if spec_c.has(GRPO):
+        inp_c["old_logprobs"] = oracle_old_logprobs(spec_c, inp_c["logits"], inp_c["labels"], inp_c["old_noise"])
+    ref_sc, ref_c, _ = run_oracle(spec_c, inp_c)
+    _, sc, _ = _check_small(spec_c, inp_c, dtype, chunks=chunks, skip_scalars=("ENTROPY",),
+                            f32_abs=max(1e-6, 2 * 0.6931 * 30 * 1.4427 * 2.0 ** -23 * float(np.max(np.abs(ref_c)))))
+    assert abs(sc[e] - ref_sc[e]) <= 2e-6 + TOL[dtype]["scalar_rel"] * abs(ref_sc[e]), (sc[e], ref_sc[e])
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
