@@ -5,7 +5,7 @@ leg may import this package. The HIP library never does.
 """
 
 from .headloss_oracle import (  # noqa: F401
-    ACCUMULATE, CE, DISTILL_FLAGS, ENTROPY, FDCE, FKL, GRPO, GSPO, IGNORE_INDEX, POLICY_FLAGS,
+    ACCUMULATE, CE, DISTILL_FLAGS, ENTROPY, FDCE, FKL, GRPO, GSPO, HINTON, IGNORE_INDEX, POLICY_FLAGS,
     READINGS, RKL, SLOT,
     SLOTS, ZLOSS, Spec, batch_divisor, forward_backward, log_softmax_rows,
     gspo_seam, logsumexp_rows, loss_gradients_wrt_s, row_validity, row_values,

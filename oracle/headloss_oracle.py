@@ -67,6 +67,7 @@ ENTROPY = 32
 FDCE = 64
 GSPO = 128
 ACCUMULATE = 1 << 16
+HINTON = 1 << 17
 DISTILL_FLAGS = FKL | RKL | FDCE
 POLICY_FLAGS = GRPO | GSPO
 
@@ -202,19 +203,32 @@ def row_values(spec: Spec, x, labels=None, teacher=None, old_logprobs=None,
     if teacher is not None:
         t = np.asarray(teacher, dtype=np.float64)
         # READINGS["temperature"]: the temperature divides the teacher logits
-        # only; the student keeps its single softmax.
-        tt = t / spec.temperature
+        # only; the student keeps its single softmax. With the HINTON mode bit
+        # (READINGS["hinton"]) the distillation term also tempers the student,
+        # softmax(s / tau), and is multiplied by tau^2.
+        tau = spec.temperature
+        tt = t / tau
         logp_t = log_softmax_rows(tt)
         p = np.exp(logp_t)
         out["p"] = p
         out["logp_t"] = logp_t
+        if spec.has(HINTON):
+            logq_d = log_softmax_rows(s / tau)
+            scale_d = tau * tau
+        else:
+            logq_d = logq
+            scale_d = 1.0
+        q_d = np.exp(logq_d)
+        out["logq_d"] = logq_d
+        out["q_d"] = q_d
         # READINGS["kl_direction"]: forward = KL(teacher || student),
         # reverse = KL(student || teacher).
-        out["fkl"] = np.sum(p * (logp_t - logq), axis=-1)
-        out["rkl"] = np.sum(q * (logq - logp_t), axis=-1)
+        out["kl_d_rev"] = np.sum(q_d * (logq_d - logp_t), axis=-1)     # unscaled reverse KL
+        out["fkl"] = scale_d * np.sum(p * (logp_t - logq_d), axis=-1)
+        out["rkl"] = scale_d * out["kl_d_rev"]
         # [#549 Loss coverage] "from-distribution cross-entropy": the cross
         # entropy of the student against the teacher distribution.
-        out["fdce"] = -np.sum(p * logq, axis=-1)
+        out["fdce"] = -scale_d * np.sum(p * logq_d, axis=-1)
 
     if labels is not None and old_logprobs is not None and advantages is not None:
         old = np.asarray(old_logprobs, dtype=np.float64).reshape(-1)
@@ -260,6 +274,9 @@ def loss_gradients_wrt_s(spec: Spec, vals: dict) -> dict:
       FDCE: q - p          (the teacher entropy does not depend on the student)
       RKL:  q * (log q - log p - RKL)
       GRPO: -act * A * r * (onehot(y) - q)      (d logp_y / ds = onehot - q)
+    With HINTON the distillation student is q_tau = softmax(s / tau) and the
+    loss carries tau^2, so d/ds = tau^2 * (1 / tau) * (the same form in q_tau):
+      FKL, FDCE: tau * (q_tau - p);   RKL: tau * q_tau * (log q_tau - log p - KL_tau)
     """
     q = vals["q"]
     V = q.shape[1]
@@ -268,10 +285,11 @@ def loss_gradients_wrt_s(spec: Spec, vals: dict) -> dict:
         g["ce"] = q - _onehot(vals["y"], V)
     if spec.has(ZLOSS):
         g["z"] = 2.0 * vals["lse"][:, None] * q
+    f_d = spec.temperature if spec.has(HINTON) else 1.0
     if spec.has(FKL) or spec.has(FDCE):
-        g["distill"] = q - vals["p"]
+        g["distill"] = f_d * (vals["q_d"] - vals["p"])
     if spec.has(RKL):
-        g["distill"] = q * (vals["logq"] - vals["logp_t"] - vals["rkl"][:, None])
+        g["distill"] = f_d * vals["q_d"] * (vals["logq_d"] - vals["logp_t"] - vals["kl_d_rev"][:, None])
     if spec.has(GRPO):
         a = np.where(vals["grpo_active"], vals["adv"] * vals["ratio"], 0.0)
         g["grpo"] = -a[:, None] * (_onehot(vals["y"], V) - q)
@@ -281,6 +299,8 @@ def loss_gradients_wrt_s(spec: Spec, vals: dict) -> dict:
 def _check_inputs(spec: Spec, labels, teacher, old_logprobs, advantages):
     if bin(spec.flags & DISTILL_FLAGS).count("1") > 1:
         raise ValueError("at most one distillation loss per plan")
+    if spec.has(HINTON) and not (spec.flags & DISTILL_FLAGS):
+        raise ValueError("the Hinton temperature mode needs a distillation loss")
     if spec.has(GRPO) and spec.has(GSPO):
         raise ValueError("at most one policy loss per plan")
     if (spec.flags & (CE | POLICY_FLAGS)) and labels is None:
@@ -542,4 +562,5 @@ READINGS = {
     "gspo_adv": "A segment's advantage is the mean of its valid tokens' advantages (the broadcast value when the caller repeats one per sequence).",
     "gspo_slots": "With GSPO the policy slots are segment means (loss, ratio, clip fraction, k3 of the sequence ratio, advantage); NEWLOGP stays a token mean; GSPO ignores the caller divisor.",
     "policy_exclusive": "GRPO and GSPO are two policy losses of one kind: a plan holds at most one.",
+    "hinton": "Opt-in HINTON mode bit: the distillation term uses softmax(s / tau) for the student as well and is multiplied by tau^2 (so its gradient keeps the tau-independent scale); CE, z-loss, GRPO/GSPO and entropy keep the untempered student softmax; the DISTILL slot reports the tau^2-scaled value.",
 }

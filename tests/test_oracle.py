@@ -212,13 +212,19 @@ def _torch_total(spec, x, y, mask, t, old, adv, offsets=None):
     if spec.flags & oracle.ZLOSS:
         total = total + spec.w_z * (torch.logsumexp(sv, -1) ** 2).sum() / n
     if spec.flags & oracle.DISTILL_FLAGS:
-        logp = torch.log_softmax(torch.tensor(t)[valid] / spec.temperature, -1)
+        tau = spec.temperature
+        logp = torch.log_softmax(torch.tensor(t)[valid] / tau, -1)
+        hinton = bool(spec.flags & oracle.HINTON)
+        sd = sv / tau if hinton else sv
+        logq_d = torch.log_softmax(sd, -1)
         if spec.flags & oracle.FKL:
-            kl = F.kl_div(logq, logp, log_target=True, reduction="sum")
+            kl = F.kl_div(logq_d, logp, log_target=True, reduction="sum")
         elif spec.flags & oracle.RKL:
-            kl = F.kl_div(logp, logq, log_target=True, reduction="sum")
+            kl = F.kl_div(logp, logq_d, log_target=True, reduction="sum")
         else:
-            kl = F.cross_entropy(sv, logp.exp(), reduction="sum")
+            kl = F.cross_entropy(sd, logp.exp(), reduction="sum")
+        if hinton:
+            kl = kl * tau * tau
         total = total + spec.w_distill * kl / n
     if spec.flags & oracle.GRPO:
         lp = logq.gather(-1, yv[valid][:, None])[:, 0]
@@ -495,6 +501,81 @@ def test_all_rows_masked_gives_zeros():
     spec = Spec(V=10, flags=ALL_LOSSES, w_grpo=1.0)
     sc, g = oracle.forward_backward(spec, x, y, None, None, np.zeros(4), np.ones(4))
     assert np.all(sc == 0.0) and np.all(g == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Hinton temperature mode (opt-in: tau on both softmaxes, times tau^2)
+# ---------------------------------------------------------------------------
+MODES = {"fkl": oracle.FKL, "rkl": oracle.RKL, "fdce": oracle.FDCE}
+
+
+def _distill_case(seed, N=7, V=23, softcap=0.0, scale=1.0, tau=1.7, hinton=True, mode="fkl"):
+    rng = _rng(seed)
+    t = rng.normal(0, 3.0, size=(N, V))
+    x = 0.6 * t + rng.normal(0, 1.5, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    y[1] = -100
+    flags = oracle.CE | oracle.ZLOSS | MODES[mode] | (oracle.HINTON if hinton else 0)
+    spec = Spec(V=V, flags=flags, w_ce=0.7, w_z=0.05, w_distill=1.3, grad_scale=0.5,
+                temperature=tau, logit_scale=scale, softcap=softcap)
+    return spec, x, y, t
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_hinton_at_tau_one_is_the_plain_mode(mode):
+    spec_h, x, y, t = _distill_case(21, tau=1.0, mode=mode)
+    spec_p, _, _, _ = _distill_case(21, tau=1.0, mode=mode, hinton=False)
+    sc_h, g_h = oracle.forward_backward(spec_h, x, y, None, t)
+    sc_p, g_p = oracle.forward_backward(spec_p, x, y, None, t)
+    np.testing.assert_allclose(sc_h, sc_p, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(g_h, g_p, rtol=1e-13, atol=1e-16)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("softcap,tau", [(0.0, 1.7), (4.0, 0.6), (0.0, 3.0)])
+def test_hinton_gradient_vs_torch_autograd(mode, softcap, tau):
+    spec, x, y, t = _distill_case(22, softcap=softcap, scale=0.8, tau=tau, mode=mode)
+    _, grad = oracle.forward_backward(spec, x, y, None, t)
+    ref = _torch_total(spec, x, y, None, t, None, None)
+    np.testing.assert_allclose(grad, ref, atol=1e-15, rtol=1e-10)
+
+
+@pytest.mark.parametrize("mode", ["fkl", "rkl"])
+def test_hinton_identity_teacher_has_zero_kl_at_any_tau(mode):
+    """With the teacher equal to the (unscaled, uncapped) student both tempered
+    distributions coincide, so the Hinton KL and its gradient vanish for every
+    tau; the teacher-only temperature reading does not have this property."""
+    for tau in (0.5, 2.0, 7.0):
+        spec, x, y, _ = _distill_case(23, tau=tau, mode=mode)
+        spec.flags &= ~(oracle.CE | oracle.ZLOSS)
+        sc, g = oracle.forward_backward(spec, x, None, None, x.copy())
+        assert abs(sc[SLOT["DISTILL"]]) < 1e-13
+        assert np.abs(g).max() < 1e-15
+        spec_p, _, _, _ = _distill_case(23, tau=tau, mode=mode, hinton=False)
+        spec_p.flags &= ~(oracle.CE | oracle.ZLOSS)
+        sc_p, _ = oracle.forward_backward(spec_p, x, None, None, x.copy())
+        assert sc_p[SLOT["DISTILL"]] > 1e-3
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_hinton_finite_differences(mode):
+    spec, x, y, t = _distill_case(24, N=3, V=8, softcap=3.0, scale=0.9, tau=2.3, mode=mode)
+    _fd_check(spec, x, y, None, t, None, None)
+
+
+def test_hinton_planted_tau_factor_is_caught(monkeypatch):
+    orig = ho.loss_gradients_wrt_s
+
+    def tau_squared_gradient(spec, vals):
+        g = orig(spec, vals)
+        if "distill" in g and spec.has(oracle.HINTON):
+            g["distill"] = g["distill"] * spec.temperature      # tau^2 instead of tau
+        return g
+
+    monkeypatch.setattr(ho, "loss_gradients_wrt_s", tau_squared_gradient)
+    with pytest.raises(AssertionError):
+        test_hinton_gradient_vs_torch_autograd("fkl", 0.0, 1.7)
+    monkeypatch.setattr(ho, "loss_gradients_wrt_s", orig)
 
 
 # ---------------------------------------------------------------------------
