@@ -30,6 +30,7 @@ FUSED_KERNEL = "fused_kernel"
 # with GSPO the timed bracket holds the forward, the segment step and the reloading backward
 GSPO_KERNELS = "fused_kernel (forward) + seam_kernel + grad_kernel"
 LOSS_NAMES = {1: "CE", 2: "z", 4: "FKL", 8: "RKL", 64: "FDCE", 16: "GRPO", 128: "GSPO", 32: "entropy"}
+HINTON_BIT = 1 << 17
 
 
 def log(msg):
@@ -228,6 +229,8 @@ def main(argv=None):
                 if key != keep:
                     kw[key] = 0.0
             flags = bit
+            if bit in (4, 8, 64):
+                flags |= w.flags & HINTON_BIT     # the distillation pass keeps its temperature mode
             if bit != 32 and not first:
                 flags |= hl.ACCUMULATE
             if bit == 32:
@@ -306,7 +309,8 @@ def main(argv=None):
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "N": w.N, "V": w.V, "dtype": w.dtype,
-                   "losses": "+".join(LOSS_NAMES[b] for b in LOSS_NAMES if w.flags & b),
+                   "losses": "+".join(LOSS_NAMES[b] for b in LOSS_NAMES if w.flags & b)
+                             + (" (Hinton temperature)" if w.flags & HINTON_BIT else ""),
                    "accumulate": acc, "n_valid": n_valid, "variant": geo},
         "hbm_GBps_step": round(algo_bytes / (ms_step * 1e-3) / 1e9, 1),
         "frac_peak_step": round(algo_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),

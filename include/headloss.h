@@ -72,9 +72,18 @@ enum {
                               valid tokens of logp - old), averaged over
                               segments; needs hl_forward_backward_segments.
                               At most one of HL_GRPO, HL_GSPO per plan.     */
-    HL_ACCUMULATE = 1u << 16 /* mode bit: add into grad_out instead of
+    HL_ACCUMULATE = 1u << 16, /* mode bit: add into grad_out instead of
                                 overwriting it (#558 Validation: gradient
                                 accumulation)                                */
+    HL_HINTON = 1u << 17     /* mode bit, with a distillation flag: the
+                                distillation term also tempers the student,
+                                softmax(s / temperature), and is multiplied by
+                                temperature^2 (the DISTILL slot reports that
+                                scaled value); CE, z-loss, policy losses and
+                                entropy keep the untempered softmax. Without
+                                it the temperature divides the teacher only
+                                (#549 Loss coverage: distillation with
+                                temperature; both readings are offered).     */
 };
 
 /* Loss weights and gradient scaling. Each scalar slot reports its loss
@@ -132,8 +141,8 @@ typedef struct hl_plan_s* hl_plan_t;
  *                plan = one scale (#549 Approach: one softmax = one scale).
  *   softcap      0 = off; > 0: s = softcap * tanh(logit_scale * x / softcap).
  * Makes no HIP call. Errors: HL_ERR_INVALID_ARG (V < 1, unknown flag bits,
- * no loss flag, two distillation flags, HL_GRPO with HL_GSPO, temperature
- * <= 0 with distillation, eps outside (0,1) with a policy loss, bad scale or
+ * no loss flag, two distillation flags, HL_GRPO with HL_GSPO, HL_HINTON
+ * without a distillation flag, temperature <= 0 with distillation, eps outside (0,1) with a policy loss, bad scale or
  * softcap, non-finite weight),
  * HL_ERR_UNSUPPORTED (V too long for any kernel variant).
  */
@@ -246,7 +255,8 @@ const float* hl_row_values(hl_plan_t plan);
  * releases a library-owned workspace; a caller-owned one must be set again
  * with hl_plan_set_workspace before the next call (HL_ERR_WORKSPACE until
  * then). Errors: HL_ERR_INVALID_ARG (chunks < 0 or > 9),
- * HL_ERR_UNSUPPORTED (no variant fits V with that many chunks). */
+ * HL_ERR_UNSUPPORTED (no variant fits V with that many chunks, or more than
+ * 8 chunks with HL_FDCE | HL_HINTON, whose chunks exchange 8 statistics). */
 hl_status hl_plan_set_chunks(hl_plan_t plan, int chunks);
 
 /* Tuning form of hl_plan_set_chunks that also fixes the threads per

@@ -37,6 +37,7 @@ ENTROPY = 1 << 5
 FDCE = 1 << 6
 GSPO = 1 << 7
 ACCUMULATE = 1 << 16
+HINTON = 1 << 17
 
 SLOTS = ("CE", "Z", "DISTILL", "GRPO", "NEWLOGP", "RATIO", "CLIPFRAC",
          "KL_OLD_NEW", "ADV_MEAN", "ENTROPY", "TOTAL", "N_VALID", "N_BADLABEL")

@@ -150,12 +150,19 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
             if (f & F_DISTILL) {
                 const double Zt = rec[R_ZT];
                 const double l2Zt = log2(Zt);
+                // the distillation student: the shared softmax, or the tempered
+                // one (Hinton mode; its shift is M / tau), whose value carries tau^2
+                const bool hinton = (f & F_HINTON) != 0u;
+                const double Zd = hinton ? (double)rec[R_ZS] : Z;
+                const double l2Zd = hinton ? log2(Zd) : l2Z;
+                const double sc = hinton ? (double)p.tau * (double)p.tau : 1.0;
                 if (f & F_RKL) {
-                    v[RC_KL] = LN2 * ((double)rec[R_SX] / Z - l2Z + l2Zt);
+                    v[RC_KL] = sc * LN2 * ((double)rec[R_SX] / Zd - l2Zd + l2Zt);
                 } else {
-                    v[RC_KL] = LN2 * ((double)rec[R_SX] / Zt - l2Zt + l2Z);      // forward KL
+                    v[RC_KL] = LN2 * ((double)rec[R_SX] / Zt - l2Zt + l2Zd);      // forward KL
                     if (f & F_FDCE)                                                 // + teacher entropy
                         v[RC_KL] += LN2 * (l2Zt - (double)rec[R_ST] / Zt);
+                    v[RC_KL] *= sc;
                 }
             }
             if (p.labels != nullptr) {

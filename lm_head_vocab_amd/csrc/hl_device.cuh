@@ -214,13 +214,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 // merge(a, b) == merge(b, a) bit for bit; an empty slice has Z == 0.
 // ---------------------------------------------------------------------------
 struct Rec {
-    float M, Z, S, Mt, Zt, SX, St;
+    float M, Z, S, Mt, Zt, SX, St, Zs;
 };
 
-__device__ __forceinline__ Rec rec_empty() { return Rec{kNegInf, 0.f, 0.f, kNegInf, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ Rec rec_empty() { return Rec{kNegInf, 0.f, 0.f, kNegInf, 0.f, 0.f, 0.f, 0.f}; }
 
+// Merge two records (beta = 1 / tau, used by the tempered student sums of the
+// Hinton modes, whose offsets move by beta times the student's shift change).
 template <int TMODE>
-__device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b) {
+__device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b, float beta) {
     const bool ea = (a.Z == 0.f), eb = (b.Z == 0.f);
     Rec r;
     const float M = fmaxf(a.M, b.M);
@@ -236,7 +238,22 @@ __device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b) {
         const float fta = fast_exp2(dta), ftb = fast_exp2(dtb);
         r.Mt = Mt;
         r.Zt = __fadd_rn(__fmul_rn(a.Zt, fta), __fmul_rn(b.Zt, ftb));
-        if (fkl_like(TMODE)) {
+        r.Zs = 0.f;
+        if (is_hinton(TMODE)) {
+            // tempered student offsets (A_j - M) beta move by d beta
+            const float dsa = __fmul_rn(da, beta), dsb = __fmul_rn(db, beta);
+            const float fsa = fast_exp2(dsa), fsb = fast_exp2(dsb);
+            r.Zs = __fadd_rn(__fmul_rn(a.Zs, fsa), __fmul_rn(b.Zs, fsb));
+            if (fkl_like(TMODE)) {
+                // SX = sum_j 2^u_j (u_j - a_j beta)
+                r.SX = __fadd_rn(__fmul_rn(fta, __fadd_rn(a.SX, __fmul_rn(__fsub_rn(dta, dsa), a.Zt))),
+                                 __fmul_rn(ftb, __fadd_rn(b.SX, __fmul_rn(__fsub_rn(dtb, dsb), b.Zt))));
+            } else {
+                // SX = sum_j 2^(a_j beta) (a_j beta - u_j)
+                r.SX = __fadd_rn(__fmul_rn(fsa, __fadd_rn(a.SX, __fmul_rn(__fsub_rn(dsa, dta), a.Zs))),
+                                 __fmul_rn(fsb, __fadd_rn(b.SX, __fmul_rn(__fsub_rn(dsb, dtb), b.Zs))));
+            }
+        } else if (fkl_like(TMODE)) {
             // SX = sum_j 2^u_j (u_j - a_j): both offsets move
             r.SX = __fadd_rn(__fmul_rn(fta, __fadd_rn(a.SX, __fmul_rn(__fsub_rn(dta, da), a.Zt))),
                              __fmul_rn(ftb, __fadd_rn(b.SX, __fmul_rn(__fsub_rn(dtb, db), b.Zt))));
@@ -246,12 +263,12 @@ __device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b) {
                              __fmul_rn(fb, __fadd_rn(b.SX, __fmul_rn(__fsub_rn(db, dtb), b.Z))));
         }
         // St = sum_j 2^u_j u_j: the teacher offset moves, as S does for the student
-        r.St = (TMODE == TM_FDCE)
+        r.St = has_st(TMODE)
                    ? __fadd_rn(__fmul_rn(fta, __fadd_rn(a.St, __fmul_rn(dta, a.Zt))),
                                __fmul_rn(ftb, __fadd_rn(b.St, __fmul_rn(dtb, b.Zt))))
                    : 0.f;
     } else {
-        r.Mt = 0.f; r.Zt = 0.f; r.SX = 0.f; r.St = 0.f;
+        r.Mt = 0.f; r.Zt = 0.f; r.SX = 0.f; r.St = 0.f; r.Zs = 0.f;
     }
     if (ea) r = b;
     if (eb) r = a;
@@ -259,7 +276,7 @@ __device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b) {
 }
 
 template <int CTRL, int TMODE>
-__device__ __forceinline__ Rec rec_dpp_step(const Rec& a) {
+__device__ __forceinline__ Rec rec_dpp_step(const Rec& a, float beta) {
     Rec b;
     b.M = dpp<CTRL>(a.M);
     b.Z = dpp<CTRL>(a.Z);
@@ -268,21 +285,22 @@ __device__ __forceinline__ Rec rec_dpp_step(const Rec& a) {
         b.Mt = dpp<CTRL>(a.Mt);
         b.Zt = dpp<CTRL>(a.Zt);
         b.SX = dpp<CTRL>(a.SX);
-        b.St = (TMODE == TM_FDCE) ? dpp<CTRL>(a.St) : 0.f;
+        b.St = has_st(TMODE) ? dpp<CTRL>(a.St) : 0.f;
+        b.Zs = is_hinton(TMODE) ? dpp<CTRL>(a.Zs) : 0.f;
     } else {
-        b.Mt = 0.f; b.Zt = 0.f; b.SX = 0.f; b.St = 0.f;
+        b.Mt = 0.f; b.Zt = 0.f; b.SX = 0.f; b.St = 0.f; b.Zs = 0.f;
     }
-    return rec_merge<TMODE>(a, b);
+    return rec_merge<TMODE>(a, b, beta);
 }
 
 // Merge the records held by lanes 0..15 of every 16-lane row; all lanes end
 // with the same result.
 template <int TMODE>
-__device__ __forceinline__ Rec rec_reduce16(Rec r) {
-    r = rec_dpp_step<DPP_XOR1, TMODE>(r);
-    r = rec_dpp_step<DPP_XOR2, TMODE>(r);
-    r = rec_dpp_step<DPP_HALF_MIRROR, TMODE>(r);
-    r = rec_dpp_step<DPP_MIRROR, TMODE>(r);
+__device__ __forceinline__ Rec rec_reduce16(Rec r, float beta) {
+    r = rec_dpp_step<DPP_XOR1, TMODE>(r, beta);
+    r = rec_dpp_step<DPP_XOR2, TMODE>(r, beta);
+    r = rec_dpp_step<DPP_HALF_MIRROR, TMODE>(r, beta);
+    r = rec_dpp_step<DPP_MIRROR, TMODE>(r, beta);
     return r;
 }
 
@@ -312,13 +330,19 @@ __device__ __forceinline__ void row_status(const int64_t* labels, const uint8_t*
 // with P = w_ce + 2 w_z lse + w_g a + w_fkl, L = w_ce + w_g a, a = act * A * r,
 // c_j = 1 (or 1 - tanh^2 with softcap). Fast-LLM PR #558 (Triton kernel for
 // the monolithic loss), section Design: every loss only adds to the
-// probability coefficient and the label-column coefficient.
+// probability coefficient and the label-column coefficient. In the Hinton
+// modes the distillation term is written in the tempered student
+// q^tau_j = softmax(s / tau)_j instead: tau w (q^tau_j - p_j), or
+// tau w q^tau_j (lq^tau_j - lp_j - KL_tau) for the reverse KL (the tau^2 on
+// the loss times the 1 / tau of d(s / tau) / ds).
 struct Coefs {
     float B2;      // log2-domain student log-partition
     float Bt2;     // log2-domain teacher log-partition
+    float Bd;      // log2-domain tempered student log-partition (Hinton modes)
     float alpha;   // probability coefficient, times G k / n
     float beta;    // label-column coefficient, times G k / n
     float gam;     // forward-KL teacher coefficient, times G k / n
+    float gq;      // tempered student coefficient (Hinton forward KL / FDCE)
     float rho2;    // reverse-KL log-ratio coefficient (log2 domain)
     float c0;      // reverse-KL probability coefficient
 };
@@ -335,11 +359,18 @@ __device__ __forceinline__ Coefs row_coefs(const FusedParams& p, const Rec& r, i
     k.B2 = r.M + l2Z;
     const float lse = k.B2 * kLn2f;
     k.Bt2 = 0.f;
+    k.Bd = 0.f;
     float kl = 0.f;
     if (TMODE != TM_NONE) {
         const float l2Zt = __builtin_amdgcn_logf(r.Zt);
         k.Bt2 = r.Mt + l2Zt;
-        if (TMODE == TM_RKL) kl = kLn2f * (r.SX * __builtin_amdgcn_rcpf(r.Z) - l2Z + l2Zt);
+        if (is_hinton(TMODE)) {
+            const float l2Zs = __builtin_amdgcn_logf(r.Zs);
+            k.Bd = fmaf(r.M, p.beta, l2Zs);
+            if (base_mode(TMODE) == TM_RKL) kl = kLn2f * (r.SX * __builtin_amdgcn_rcpf(r.Zs) - l2Zs + l2Zt);
+        } else if (TMODE == TM_RKL) {
+            kl = kLn2f * (r.SX * __builtin_amdgcn_rcpf(r.Z) - l2Z + l2Zt);
+        }
     }
     float a_g = 0.f;
     if ((f & F_GRPO) && y >= 0) {
@@ -357,18 +388,49 @@ __device__ __forceinline__ Coefs row_coefs(const FusedParams& p, const Rec& r, i
     if ((f & F_Z) && p.w_z != 0.f) P += 2.f * p.w_z * lse;
     if ((f & F_GRPO) && p.w_g != 0.f) { P += p.w_g * a_g; L += p.w_g * a_g; }
     if ((f & F_DISTILL) && p.w_d != 0.f) wd = p.w_d;
-    if (fkl_like(TMODE)) P += wd;
+    if (fkl_like(TMODE) && !is_hinton(TMODE)) P += wd;
     k.alpha = scale * P;
     k.beta = scale * L;
-    k.gam = scale * wd;
-    k.rho2 = scale * wd * kLn2f;
-    k.c0 = scale * (P - wd * kl);
+    if (is_hinton(TMODE)) {
+        const float wt = wd * p.tau;
+        k.gam = scale * wt;
+        k.gq = scale * wt;
+        k.rho2 = scale * wt * kLn2f;
+        k.c0 = -scale * wt * kl;
+    } else {
+        k.gam = scale * wd;
+        k.gq = 0.f;
+        k.rho2 = scale * wd * kLn2f;
+        k.c0 = scale * (P - wd * kl);
+    }
     return k;
 }
 
 // Gradient of one element; lab = the label-column coefficient at the label, else 0.
 template <int TMODE, bool SOFTCAP>
 __device__ __forceinline__ float grad_one(const FusedParams& p, const Coefs& k, float x, float t, float lab) {
+    if (is_hinton(TMODE)) {
+        float sl, cfh = 1.0f;            // s log2(e)
+        if (SOFTCAP) {
+            const float th = hl_tanh(x * p.kc);
+            sl = p.cap * th * kLog2e;
+            cfh = fmaf(-th, th, 1.0f);
+        } else {
+            sl = x * p.K1;
+        }
+        const float q = fast_exp2(sl - k.B2);
+        const float aqd = fmaf(sl, p.beta, -k.Bd);     // log2 of the tempered student
+        const float qd = fast_exp2(aqd);
+        float g;
+        if (fkl_like(TMODE)) {
+            const float pt = fast_exp2(fmaf(t, p.K2, -k.Bt2));
+            g = fmaf(k.alpha, q, fmaf(k.gq, qd, fmaf(-k.gam, pt, -lab)));
+        } else {
+            const float up = fmaf(t, p.K2, -k.Bt2);
+            g = fmaf(k.alpha, q, fmaf(qd, fmaf(k.rho2, aqd - up, k.c0), -lab));
+        }
+        return SOFTCAP ? cfh * g : g;
+    }
     float aq, cf = 1.0f;
     if (SOFTCAP) {
         const float th = hl_tanh(x * p.kc);
@@ -535,10 +597,10 @@ void fused_kernel(const FusedParams p) {
     const bool early = mx0 != kNegInf && (TMODE == TM_NONE || mt0 != kNegInf);
     const bool want_s = (p.flags & F_ENT) != 0u;
 
-    float Z = 0.f, S = 0.f, Zt = 0.f, SX = 0.f, St = 0.f;
-    // one call site per variant (below), so the slice stays in registers
+    float Z = 0.f, S = 0.f, Zt = 0.f, SX = 0.f, St = 0.f, Zs = 0.f;
     // one term of every sum; the entropy term only when WS
-    auto term = [&](auto want_s_tag, float x, float t, float& z, float& s, float& zt, float& sx, float& st) {
+    auto term = [&](auto want_s_tag, float x, float t, float& z, float& s, float& zt, float& sx, float& st,
+                    float& zs) {
         constexpr bool WS = decltype(want_s_tag)::value;
         const float a = SOFTCAP ? fmaf(p.cap * hl_tanh(x * p.kc), kLog2e, -M) : fmaf(x, p.K1, -M);
         const float ex = fast_exp2(a);
@@ -548,46 +610,60 @@ void fused_kernel(const FusedParams p) {
             const float u = fmaf(t, p.K2, -Mt);
             const float et = fast_exp2(u);
             zt += et;
-            if (fkl_like(TMODE)) sx = fmaf(et, u - a, sx);
-            else sx = fmaf(ex, a - u, sx);
-            if (TMODE == TM_FDCE) st = fmaf(et, u, st);
-        }
-    };
-    auto accumulate = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st) {
-        term(std::true_type(), x, t, z, s, zt, sx, st);
-    };
-    // one call site per variant (below), so the slice stays in registers
-    auto sweep = [&](auto want_s_tag) __attribute__((always_inline)) {
-        constexpr bool WS = decltype(want_s_tag)::value;
-        auto acc = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st) {
-            term(want_s_tag, x, t, z, s, zt, sx, st);
-        };
-        float z0 = 0.f, s0 = 0.f, zt0 = 0.f, sx0 = 0.f, st0 = 0.f;
-#pragma unroll
-        for (int v = 0; v < NVEC; ++v) {
-            if (tid < nv - v * BLOCK) {
-                float z = 0.f, s = 0.f, zt = 0.f, sx = 0.f, st = 0.f;
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    acc(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z, s, zt, sx, st);
-                z0 += z; s0 += s; zt0 += zt; sx0 += sx; st0 += st;
+            if (is_hinton(TMODE)) {
+                const float ad = a * p.beta;          // tempered student, shift M beta
+                const float ed = fast_exp2(ad);
+                zs += ed;
+                if (fkl_like(TMODE)) sx = fmaf(et, u - ad, sx);
+                else sx = fmaf(ed, ad - u, sx);
+            } else if (fkl_like(TMODE)) {
+                sx = fmaf(et, u - a, sx);
+            } else {
+                sx = fmaf(ex, a - u, sx);
             }
+            if (has_st(TMODE)) st = fmaf(et, u, st);
         }
-        if (has_e) acc(xe, te, z0, s0, zt0, sx0, st0);
+    };
+    auto accumulate = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st, float& zs) {
+        term(std::true_type(), x, t, z, s, zt, sx, st, zs);
+    };
+    auto wave_sums = [&](bool ws, float z0, float s0, float zt0, float sx0, float st0, float zs0) {
         Z = wave_sum(z0);
-        if (WS) S = wave_sum(s0);
+        if (ws) S = wave_sum(s0);
         if (TMODE != TM_NONE) {
             Zt = wave_sum(zt0);
             SX = wave_sum(sx0);
         }
-        if (TMODE == TM_FDCE) St = wave_sum(st0);
+        if (has_st(TMODE)) St = wave_sum(st0);
+        if (is_hinton(TMODE)) Zs = wave_sum(zs0);
+    };
+    // one call site per variant (below), so the slice stays in registers
+    auto sweep = [&](auto want_s_tag) __attribute__((always_inline)) {
+        constexpr bool WS = decltype(want_s_tag)::value;
+        auto acc = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st, float& zs) {
+            term(want_s_tag, x, t, z, s, zt, sx, st, zs);
+        };
+        float z0 = 0.f, s0 = 0.f, zt0 = 0.f, sx0 = 0.f, st0 = 0.f, zs0 = 0.f;
+#pragma unroll
+        for (int v = 0; v < NVEC; ++v) {
+            if (tid < nv - v * BLOCK) {
+                float z = 0.f, s = 0.f, zt = 0.f, sx = 0.f, st = 0.f, zs = 0.f;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    acc(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z, s, zt, sx, st, zs);
+                z0 += z; s0 += s; zt0 += zt; sx0 += sx; st0 += st; zs0 += zs;
+            }
+        }
+        if (has_e) acc(xe, te, z0, s0, zt0, sx0, st0, zs0);
+        wave_sums(WS, z0, s0, zt0, sx0, st0, zs0);
     };
     if (early) {
         if (want_s) sweep(std::true_type());
         else sweep(std::false_type());
     }
     constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
-    if (!early || !(Z <= kSumLimit) || (TMODE != TM_NONE && !(Zt <= kSumLimit))) {
+    if (!early || !(Z <= kSumLimit) || (TMODE != TM_NONE && !(Zt <= kSumLimit)) ||
+        (is_hinton(TMODE) && !(Zs <= kSumLimit))) {
         // Rare: the true maximum, then the sums from it. This path reads the
         // slice again from memory so that the register copy keeps a single
         // use above (the slice must not be spilled to make room for a second).
@@ -603,22 +679,16 @@ void fused_kernel(const FusedParams p) {
         }
         M = shift_of(wave_max(mx));
         if (TMODE != TM_NONE) Mt = wave_max(mt) * p.K2;
-        float z0 = 0.f, s0 = 0.f, zt0 = 0.f, sx0 = 0.f, st0 = 0.f;
+        float z0 = 0.f, s0 = 0.f, zt0 = 0.f, sx0 = 0.f, st0 = 0.f, zs0 = 0.f;
         for (int i = tid; i < nv; i += BLOCK) {
             const u32x4 w = xv[i];
             u32x4 wt = {0u, 0u, 0u, 0u};
             if (TMODE != TM_NONE) wt = tv[i];
             for (int e = 0; e < VEC; ++e)
-                accumulate(T::get(w, e), TMODE != TM_NONE ? T::get(wt, e) : 0.f, z0, s0, zt0, sx0, st0);
+                accumulate(T::get(w, e), TMODE != TM_NONE ? T::get(wt, e) : 0.f, z0, s0, zt0, sx0, st0, zs0);
         }
-        if (has_e) accumulate(xe, te, z0, s0, zt0, sx0, st0);
-        Z = wave_sum(z0);
-        S = wave_sum(s0);
-        if (TMODE != TM_NONE) {
-            Zt = wave_sum(zt0);
-            SX = wave_sum(sx0);
-        }
-        if (TMODE == TM_FDCE) St = wave_sum(st0);
+        if (has_e) accumulate(xe, te, z0, s0, zt0, sx0, st0, zs0);
+        wave_sums(true, z0, s0, zt0, sx0, st0, zs0);
     }
     if (lane == 0) {
         s_rec[wave][0] = M;
@@ -628,6 +698,7 @@ void fused_kernel(const FusedParams p) {
         s_rec[wave][4] = Zt;
         s_rec[wave][5] = SX;
         s_rec[wave][6] = St;
+        s_rec[wave][7] = Zs;
     }
     __syncthreads();
 
@@ -643,11 +714,12 @@ void fused_kernel(const FusedParams p) {
                 r.Mt = s_rec[w][3];
                 r.Zt = s_rec[w][4];
                 r.SX = s_rec[w][5];
-                if (TMODE == TM_FDCE) r.St = s_rec[w][6];
+                if (has_st(TMODE)) r.St = s_rec[w][6];
+                if (is_hinton(TMODE)) r.Zs = s_rec[w][7];
             }
             if (r.Z == 0.f) r = rec_empty();
         }
-        r = rec_reduce16<TMODE>(r);
+        r = rec_reduce16<TMODE>(r, p.beta);
     }
 
     // ---- split-vocab: publish this chunk's record, wait for the others ----
@@ -659,13 +731,16 @@ void fused_kernel(const FusedParams p) {
     // one load per lane per round, then merges the C records with the same
     // fixed DPP tree in every workgroup of the row.
     if (p.chunks > 1) {
-        // statistics this mode exchanges: M, Z, S (+ Mt, Zt, SX (+ St))
-        constexpr int NXW = TMODE == TM_NONE ? 3 : (TMODE == TM_FDCE ? 7 : 6);
+        // statistics this mode exchanges: M, Z, S (+ Mt, Zt, SX (+ St) (+ Zs)),
+        // packed in that order
+        constexpr int NXW = xwords_used(TMODE);
+        constexpr int POS_ZS = has_st(TMODE) ? 7 : 6;
         const uint64_t epoch = (uint64_t)p.ctrl[CTRL_EPOCH] << 32;
         uint64_t* words = p.chunk_words + (int64_t)row * p.chunks * XWORDS;
         if (tid == 0) {
             uint64_t* mine = words + c * XWORDS;
-            const float f[XWORDS] = {r.M, r.Z, r.S, r.Mt, r.Zt, r.SX, r.St};
+            const float f[XWORDS] = {r.M, r.Z, r.S, r.Mt, r.Zt, r.SX,
+                                     has_st(TMODE) ? r.St : r.Zs, r.Zs};
 #pragma unroll
             for (int i = 0; i < NXW; ++i)
                 __hip_atomic_store(mine + i, epoch | __float_as_uint(f[i]), __ATOMIC_RELAXED,
@@ -696,19 +771,21 @@ void fused_kernel(const FusedParams p) {
                 cr.M = s_xw[l * NXW + 0]; cr.Z = s_xw[l * NXW + 1]; cr.S = s_xw[l * NXW + 2];
                 if (TMODE != TM_NONE) {
                     cr.Mt = s_xw[l * NXW + 3]; cr.Zt = s_xw[l * NXW + 4]; cr.SX = s_xw[l * NXW + 5];
-                    if (TMODE == TM_FDCE) cr.St = s_xw[l * NXW + 6];
+                    if (has_st(TMODE)) cr.St = s_xw[l * NXW + 6];
+                    if (is_hinton(TMODE)) cr.Zs = s_xw[l * NXW + POS_ZS];
                 }
                 if (cr.Z == 0.f) cr = rec_empty();
             }
-            cr = rec_reduce16<TMODE>(cr);
+            cr = rec_reduce16<TMODE>(cr, p.beta);
             if (lane == 0) {
                 s_fin[0] = cr.M; s_fin[1] = cr.Z; s_fin[2] = cr.S;
                 s_fin[3] = cr.Mt; s_fin[4] = cr.Zt; s_fin[5] = cr.SX; s_fin[6] = cr.St;
+                s_fin[7] = cr.Zs;
             }
         }
         __syncthreads();
         r.M = s_fin[0]; r.Z = s_fin[1]; r.S = s_fin[2];
-        r.Mt = s_fin[3]; r.Zt = s_fin[4]; r.SX = s_fin[5]; r.St = s_fin[6];
+        r.Mt = s_fin[3]; r.Zt = s_fin[4]; r.SX = s_fin[5]; r.St = s_fin[6]; r.Zs = s_fin[7];
     }
 
     // ---- per-row record for the batch reduction ----
@@ -716,7 +793,7 @@ void fused_kernel(const FusedParams p) {
         float* out = p.row_rec + row * REC;
         out[R_M] = r.M; out[R_Z] = r.Z; out[R_S] = r.S;
         out[R_MT] = r.Mt; out[R_ZT] = r.Zt; out[R_SX] = r.SX; out[R_ST] = r.St;
-        out[R_PAD] = 0.0f;
+        out[R_ZS] = r.Zs;
         out[R_XY] = s_row[0];
         out[R_VALID] = 1.0f;
     }
@@ -823,7 +900,7 @@ __global__ __launch_bounds__(kGradBlock) void grad_kernel(const FusedParams p) {
     const float* rec = p.row_rec + row * REC;
     Rec r;
     r.M = rec[R_M]; r.Z = rec[R_Z]; r.S = rec[R_S];
-    r.Mt = rec[R_MT]; r.Zt = rec[R_ZT]; r.SX = rec[R_SX]; r.St = rec[R_ST];
+    r.Mt = rec[R_MT]; r.Zt = rec[R_ZT]; r.SX = rec[R_SX]; r.St = rec[R_ST]; r.Zs = rec[R_ZS];
     const float old = p.old_logprobs ? p.old_logprobs[row] : 0.f;
     const float adv = p.advantages ? p.advantages[row] : 0.f;
     Coefs k = row_coefs<TMODE, SOFTCAP>(p, r, y, rec[R_XY], old, adv);
@@ -833,7 +910,8 @@ __global__ __launch_bounds__(kGradBlock) void grad_kernel(const FusedParams p) {
         const float e = n_seg > 0u ? p.grad_scale * p.k * p.w_g * p.row_coef[row] / (float)n_seg : 0.f;
         k.alpha += e;
         k.beta += e;
-        k.c0 += e;
+        if (TMODE == TM_RKL) k.c0 += e;   // there c0 multiplies q (alpha is unused); in the
+                                          // Hinton reverse KL it multiplies the tempered q
     }
     if (p.ctrl[CTRL_ERROR] != 0u) {
         // statistics or segments are not trustworthy: make the gradient say so

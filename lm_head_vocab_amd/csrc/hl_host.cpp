@@ -49,7 +49,7 @@ hl_status hip_fail(const char* where, hipError_t e) {
 constexpr uint32_t kDistillBits = HL_FKL | HL_RKL | HL_FDCE;
 constexpr uint32_t kPolicyBits = HL_GRPO | HL_GSPO;
 constexpr uint32_t kLossBits = HL_CE | HL_ZLOSS | kDistillBits | kPolicyBits | HL_ENTROPY;
-constexpr uint32_t kKnownBits = kLossBits | HL_ACCUMULATE;
+constexpr uint32_t kKnownBits = kLossBits | HL_ACCUMULATE | HL_HINTON;
 constexpr int kTwoPerCuNvec = 10;         // 64 VGPRs at 1024 threads: two workgroups per CU
 constexpr int kTwoPerCuNvecSoftcap = 8;   // the softcap instances need a few more registers
 
@@ -87,25 +87,20 @@ int round_up_to(const int* set, int n_set, int need) {
     return -1;
 }
 
+typedef FusedLauncher (*Getter)(int, int, bool);
+
+// [dtype][teacher mode] instance getters (one translation unit each)
+const Getter kGetters[3][7] = {
+    {get_fused_f32_none, get_fused_f32_fkl, get_fused_f32_rkl, get_fused_f32_fdce,
+     get_fused_f32_fklh, get_fused_f32_rklh, get_fused_f32_fdceh},
+    {get_fused_bf16_none, get_fused_bf16_fkl, get_fused_bf16_rkl, get_fused_bf16_fdce,
+     get_fused_bf16_fklh, get_fused_bf16_rklh, get_fused_bf16_fdceh},
+    {get_fused_f16_none, get_fused_f16_fkl, get_fused_f16_rkl, get_fused_f16_fdce,
+     get_fused_f16_fklh, get_fused_f16_rklh, get_fused_f16_fdceh},
+};
+
 FusedLauncher lookup(hl_dtype dt, int tmode, int block, int nvec, bool softcap) {
-    if (tmode == TM_FDCE) {
-        if (dt == HL_F32) return get_fused_f32_fdce(block, nvec, softcap);
-        if (dt == HL_F16) return get_fused_f16_fdce(block, nvec, softcap);
-        return get_fused_bf16_fdce(block, nvec, softcap);
-    }
-    if (dt == HL_F32) {
-        if (tmode == TM_NONE) return get_fused_f32_none(block, nvec, softcap);
-        if (tmode == TM_FKL) return get_fused_f32_fkl(block, nvec, softcap);
-        return get_fused_f32_rkl(block, nvec, softcap);
-    }
-    if (dt == HL_F16) {
-        if (tmode == TM_NONE) return get_fused_f16_none(block, nvec, softcap);
-        if (tmode == TM_FKL) return get_fused_f16_fkl(block, nvec, softcap);
-        return get_fused_f16_rkl(block, nvec, softcap);
-    }
-    if (tmode == TM_NONE) return get_fused_bf16_none(block, nvec, softcap);
-    if (tmode == TM_FKL) return get_fused_bf16_fkl(block, nvec, softcap);
-    return get_fused_bf16_rkl(block, nvec, softcap);
+    return kGetters[(int)dt][tmode](block, nvec, softcap);
 }
 
 // Geometry for C chunks per row with a given block size (0: the smallest
@@ -144,13 +139,15 @@ Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C, int block = 0) {
 // threads and at most 10 + 10 vectors (about 113 VGPRs). Short rows use one
 // 256-thread workgroup.
 hl_status choose(hl_plan_s* p) {
+    const int max_chunks = max_chunks_for(p->tmode);
+    if (p->forced_chunks > max_chunks) return HL_ERR_UNSUPPORTED;
     if (p->forced_chunks > 0) {
         Geometry g = geometry_for(p->V, p->dtype, p->tmode, p->forced_chunks, p->forced_block);
         if (g.chunks == 0) return HL_ERR_UNSUPPORTED;
         p->geo = g;
     } else {
         Geometry g{0, 0, 0};
-        for (int C = 1; C <= kMaxChunks; ++C) {
+        for (int C = 1; C <= max_chunks; ++C) {
             g = geometry_for(p->V, p->dtype, p->tmode, C);
             if (g.chunks == 0) continue;
             if (g.block == kSmallBlock) break;
@@ -166,7 +163,7 @@ hl_status choose(hl_plan_s* p) {
             g = Geometry{0, 0, 0};
         }
         if (g.chunks == 0) {   // very long rows: the fewest chunks that fit at all
-            for (int C = 1; C <= kMaxChunks && g.chunks == 0; ++C) g = geometry_for(p->V, p->dtype, p->tmode, C);
+            for (int C = 1; C <= max_chunks && g.chunks == 0; ++C) g = geometry_for(p->V, p->dtype, p->tmode, C);
         }
         if (g.chunks == 0) return HL_ERR_UNSUPPORTED;
         p->geo = g;
@@ -215,6 +212,7 @@ hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags
     const uint32_t dbits = loss_flags & kDistillBits;
     if (dbits & (dbits - 1u)) return HL_ERR_INVALID_ARG;   // at most one distillation loss
     const bool distill = dbits != 0u;
+    if ((loss_flags & HL_HINTON) && !distill) return HL_ERR_INVALID_ARG;   // the mode tempers distillation
     if (distill && !(finite(temperature) && temperature > 0.f)) return HL_ERR_INVALID_ARG;
     if ((loss_flags & kPolicyBits) == kPolicyBits) return HL_ERR_INVALID_ARG;   // one policy loss
     if ((loss_flags & kPolicyBits) && !(finite(eps) && eps > 0.f && eps < 1.f)) return HL_ERR_INVALID_ARG;
@@ -239,6 +237,7 @@ hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags
     p->tmode = (loss_flags & HL_FKL) ? TM_FKL
              : (loss_flags & HL_RKL) ? TM_RKL
              : (loss_flags & HL_FDCE) ? TM_FDCE : TM_NONE;
+    if (loss_flags & HL_HINTON) p->tmode += TM_FKL_H - TM_FKL;
     const hl_status st = choose(p);
     if (st != HL_OK) {
         delete p;
@@ -432,6 +431,8 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
         fp.k = plan->logit_scale;
         fp.K1 = plan->logit_scale * log2e;
         fp.K2 = log2e / plan->temperature;
+        fp.beta = (f & HL_HINTON) ? 1.0f / plan->temperature : 1.0f;
+        fp.tau = plan->temperature;
         fp.cap = plan->softcap;
         fp.kc = plan->softcap > 0.f ? plan->logit_scale / plan->softcap : 0.f;
         fp.w_ce = plan->w.ce;
@@ -489,6 +490,7 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
     rp.k = plan->logit_scale;
     rp.cap = plan->softcap;
     rp.eps = plan->eps;
+    rp.tau = plan->temperature;
     rp.scalars = scalars_out;
     rp.n_rows = n_rows;
     rp.flags = f;

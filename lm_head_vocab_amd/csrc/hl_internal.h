@@ -6,16 +6,26 @@
 
 namespace hl {
 
-// Distillation mode baked into a kernel instance.
-enum TeacherMode : int { TM_NONE = 0, TM_FKL = 1, TM_RKL = 2, TM_FDCE = 3 };
+// Distillation mode baked into a kernel instance. The _H modes temper the
+// distillation student as well (softmax(s / tau), loss times tau^2).
+enum TeacherMode : int {
+    TM_NONE = 0, TM_FKL = 1, TM_RKL = 2, TM_FDCE = 3, TM_FKL_H = 4, TM_RKL_H = 5, TM_FDCE_H = 6
+};
 
+constexpr bool is_hinton(int t) { return t >= TM_FKL_H; }
+constexpr int base_mode(int t) { return is_hinton(t) ? t - 3 : t; }
 // Forward KL and from-distribution CE share the gradient q - p.
-constexpr bool fkl_like(int t) { return t == TM_FKL || t == TM_FDCE; }
+constexpr bool fkl_like(int t) { return base_mode(t) == TM_FKL || base_mode(t) == TM_FDCE; }
+// Modes that carry the teacher entropy sum St.
+constexpr bool has_st(int t) { return base_mode(t) == TM_FDCE; }
+// Statistics a chunk publishes: M, Z, S (+ Mt, Zt, SX (+ St) (+ Zs)).
+constexpr int xwords_used(int t) { return t == TM_NONE ? 3 : 6 + (has_st(t) ? 1 : 0) + (is_hinton(t) ? 1 : 0); }
 
 // Loss bits (same values as the public HL_* flags).
 enum : uint32_t {
     F_CE = 1u << 0, F_Z = 1u << 1, F_FKL = 1u << 2, F_RKL = 1u << 3,
     F_GRPO = 1u << 4, F_ENT = 1u << 5, F_FDCE = 1u << 6, F_GSPO = 1u << 7, F_ACC = 1u << 16,
+    F_HINTON = 1u << 17,
     F_DISTILL = F_FKL | F_RKL | F_FDCE,
 };
 
@@ -31,9 +41,11 @@ constexpr int NSCALARS = 13;
 //   M  = shift, Z = sum 2^(A_j - M), S = sum 2^(A_j - M) (A_j - M)
 //   Mt, Zt = the same for the teacher, SX = the distillation cross sum.
 //   St = sum 2^(U_j - Mt) (U_j - Mt), the teacher entropy sum (FDCE only).
+//   Zs = sum 2^((A_j - M) b), b = 1 / tau: the tempered student's sum
+//        (Hinton modes only; its shift is M b).
 // The per-row record written by the fused kernel adds the raw label logit
 // and a valid flag.
-enum RecField : int { R_M = 0, R_Z, R_S, R_MT, R_ZT, R_SX, R_ST, R_XY, R_VALID, R_PAD, REC };
+enum RecField : int { R_M = 0, R_Z, R_S, R_MT, R_ZT, R_SX, R_ST, R_XY, R_VALID, R_ZS, REC };
 
 // Control words at the start of the workspace. CTRL_NSEG counts the GSPO
 // segments that hold a valid row. CTRL_ERROR: 1 = a split-vocab row never saw
@@ -48,11 +60,13 @@ enum Ctrl : int {
 // act * A * s / n_i, and the valid-token count n_i.
 enum SegField : int { SG_LOSS = 0, SG_RATIO, SG_CLIP, SG_K3, SG_ADV, SG_NONEMPTY, SG_DERIV, SG_COUNT, SEGREC };
 
-// Split-vocab exchange: each chunk publishes its 7 statistics as 64-bit words
-// (float bits low, call epoch high); at most kMaxChunks chunks per row.
-constexpr int XWORDS = 7;
+// Split-vocab exchange: each chunk publishes up to 8 statistics as 64-bit
+// words (float bits low, call epoch high), XWORDS apart. One wave polls all
+// of a row's words, so a mode allows at most 64 / xwords_used chunks.
+constexpr int XWORDS = 8;
 constexpr int kMaxChunks = 9;
-static_assert(kMaxChunks * XWORDS <= 64, "one wave polls every exchanged word of a row");
+constexpr int max_chunks_for(int t) { return 64 / xwords_used(t) < kMaxChunks ? 64 / xwords_used(t) : kMaxChunks; }
+static_assert(kMaxChunks * xwords_used(TM_FDCE) <= 64, "one wave polls every exchanged word of a row");
 
 struct Geometry {
     int chunks;      // workgroups per row
@@ -81,6 +95,8 @@ struct FusedParams {
     float k;          // logit scale
     float K1;         // k * log2(e)
     float K2;         // log2(e) / temperature
+    float beta;       // 1 / temperature for the tempered distillation student (Hinton modes), else 1
+    float tau;        // temperature (the Hinton gradient carries tau)
     float cap;        // softcap c (0 = off)
     float kc;         // k / c
     float w_ce, w_z, w_d, w_g;
@@ -119,6 +135,7 @@ struct ReduceParams {
     int64_t n_rows;
     uint32_t flags;
     float k, cap, eps;
+    float tau;                // Hinton modes: the distillation value is scaled by tau^2
     float w_ce, w_z, w_d, w_g;
     float divisor;
 };
@@ -158,6 +175,15 @@ FusedLauncher get_fused_f16_rkl(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f32_fdce(int block, int nvec, bool softcap);
 FusedLauncher get_fused_bf16_fdce(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f16_fdce(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f32_fklh(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f32_rklh(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f32_fdceh(int block, int nvec, bool softcap);
+FusedLauncher get_fused_bf16_fklh(int block, int nvec, bool softcap);
+FusedLauncher get_fused_bf16_rklh(int block, int nvec, bool softcap);
+FusedLauncher get_fused_bf16_fdceh(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f16_fklh(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f16_rklh(int block, int nvec, bool softcap);
+FusedLauncher get_fused_f16_fdceh(int block, int nvec, bool softcap);
 
 // Load-mode gradient kernels, one getter per dtype: nullptr for an unknown mode.
 GradLauncher get_grad_f32(int tmode, bool softcap);

@@ -57,6 +57,8 @@ def test_status_strings():
     (dict(flags=hl.GSPO, eps=0.0), hl.HL_ERR_INVALID_ARG),
     (dict(flags=hl.GSPO, eps=1.5), hl.HL_ERR_INVALID_ARG),
     (dict(flags=hl.GRPO | hl.GSPO), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.CE | hl.HINTON), hl.HL_ERR_INVALID_ARG),
+    (dict(flags=hl.FKL | hl.HINTON, tau=0.0), hl.HL_ERR_INVALID_ARG),
     (dict(scale=0.0), hl.HL_ERR_INVALID_ARG),
     (dict(scale=-1.0), hl.HL_ERR_INVALID_ARG),
     (dict(scale=math.inf), hl.HL_ERR_INVALID_ARG),
@@ -162,6 +164,21 @@ def test_forward_backward_host_checks_enqueue_nothing():
     assert fb(h, 4, fake, fake, None, fake, fake, fake, fake, fake, None) == hl.HL_ERR_WORKSPACE
     lib.hl_plan_destroy(h)
     lib.hl_plan_destroy(None)
+
+
+def test_hinton_plans_and_the_eight_statistic_chunk_cap():
+    for mode in (hl.FKL, hl.RKL, hl.FDCE):
+        st, h = _plan(V=151936, flags=hl.CE | mode | hl.HINTON, w=Weights(1, 0, 1, 0, 1, 0), tau=2.0)
+        assert st == 0
+        c, b, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        assert lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), ctypes.byref(n)) == 0
+        assert (c.value, b.value) == (4, 512)
+        # the from-distribution mode with Hinton exchanges 8 statistics per
+        # chunk: one wave polls at most 64 words, so 8 chunks at most
+        expect9 = hl.HL_ERR_UNSUPPORTED if mode == hl.FDCE else hl.HL_OK
+        assert lib.hl_plan_set_chunks(h, 9) == expect9
+        assert lib.hl_plan_set_chunks(h, 8) == hl.HL_OK
+        lib.hl_plan_destroy(h)
 
 
 def test_segment_call_host_checks_enqueue_nothing():

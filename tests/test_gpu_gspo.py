@@ -40,6 +40,8 @@ COMBOS = {
     "all_gspo_rkl": (CE | Z | RKL | GSPO | ENT, dict(ce=1.0, z=1e-3, distill=0.5, grpo=1.0, grad_scale=0.25)),
     "all_gspo_fkl": (CE | Z | FKL | GSPO | ENT, dict(ce=0.7, z=1e-2, distill=0.9, grpo=0.6, grad_scale=2.0)),
     "ce_gspo_fdce": (CE | FDCE | GSPO, dict(ce=0.5, distill=1.0, grpo=1.3)),
+    "all_gspo_rkl_h": (CE | Z | RKL | GSPO | ENT | oracle.HINTON,
+                       dict(ce=1.0, z=1e-3, distill=0.5, grpo=1.0, grad_scale=0.25)),
 }
 SHAPES = [(37, 1000), (16, 4099), (9, 33000), (5, 3), (3, 1), (64, 300)]
 

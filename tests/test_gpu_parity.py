@@ -38,6 +38,7 @@ F16_LOSS_SCALE = 1024.0
 CE, Z, FKL, RKL, GRPO, ENT, ACC = (oracle.CE, oracle.ZLOSS, oracle.FKL, oracle.RKL, oracle.GRPO,
                                    oracle.ENTROPY, oracle.ACCUMULATE)
 FDCE = oracle.FDCE
+HINTON = oracle.HINTON
 DISTILL = FKL | RKL | FDCE
 
 COMBOS = {
@@ -52,7 +53,12 @@ COMBOS = {
     "all_fkl": (CE | Z | FKL | GRPO | ENT, dict(ce=0.7, z=1e-2, distill=0.9, grpo=0.6, grad_scale=2.0)),
     "ce_fdce": (CE | FDCE, dict(ce=0.5, distill=1.0)),
     "all_fdce": (CE | Z | FDCE | GRPO | ENT, dict(ce=0.3, z=1e-3, distill=1.1, grpo=0.8, grad_scale=0.5)),
+    # Hinton temperature mode: tau on both softmaxes of the distillation term, times tau^2
+    "ce_fkl_h": (CE | FKL | HINTON, dict(ce=0.5, distill=1.0)),
+    "all_rkl_h": (CE | Z | RKL | GRPO | ENT | HINTON, dict(ce=1.0, z=1e-3, distill=0.5, grpo=1.0, grad_scale=0.25)),
+    "all_fdce_h": (CE | Z | FDCE | GRPO | ENT | HINTON, dict(ce=0.3, z=1e-3, distill=1.1, grpo=0.8, grad_scale=0.5)),
 }
+HINTON_COMBOS = ["ce_fkl_h", "all_rkl_h", "all_fdce_h"]
 # (N, V): aligned and ragged rows, tiny rows, both block sizes
 SHAPES = [(37, 1000), (16, 4099), (9, 33000), (5, 3), (3, 1), (64, 300), (11, 2053)]
 
@@ -263,6 +269,38 @@ def test_split_vocab_accumulate_and_masking():
     _check_small(spec, inp, "bf16", chunks=4)
 
 
+@pytest.mark.parametrize("tau", [0.7, 2.5])
+@pytest.mark.parametrize("chunks", [2, 5, 8])
+@pytest.mark.parametrize("combo", HINTON_COMBOS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hinton_split_vocab_and_temperatures(dtype, combo, chunks, tau):
+    """The tempered student sums travel through the split-vocab exchange (up
+    to 8 chunks, the cap of the 8-statistic from-distribution mode)."""
+    for V, N in ((20011, 7), (70000, 5)):
+        spec, inp = _small(dtype, combo, N, V, seed=chunks * 10 + N, softcap=15.0, scale=0.8,
+                           temperature=tau, mask_frac=0.2)
+        _check_small(spec, inp, dtype, chunks=chunks)
+
+
+@pytest.mark.parametrize("combo", HINTON_COMBOS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_hinton_accumulate_and_per_token_values(dtype, combo):
+    spec, inp = _small(dtype, combo, 19, 20011, seed=13, accumulate=True, mask_frac=0.2, softcap=30.0,
+                       scale=0.5, temperature=2.0)
+    _check_small(spec, inp, dtype)
+    spec, inp = _small(dtype, combo, 23, 4099, seed=14, mask_frac=0.2, temperature=3.0)
+    plan, _, _ = _check_small(spec, inp, dtype, grad_mode="none")
+    rv = plan.row_values().cpu().double().numpy()
+    y = to_np(inp["labels"]).astype(np.int64)
+    valid, _ = oracle.row_validity(23, spec.V, y, to_np(inp["mask"]))
+    vals = oracle.row_values(spec, to_np(inp["logits"]), y, to_np(inp["teacher"]),
+                             to_np(inp.get("old_logprobs")), to_np(inp.get("advantages")))
+    key = "fkl" if spec.has(FKL) else ("rkl" if spec.has(RKL) else "fdce")
+    ref = vals[key][valid]
+    err = np.max(np.abs(rv[valid, 2] - ref) / np.maximum(np.abs(ref), 1e-2))
+    assert err <= TOL[dtype]["scalar_rel"], err
+
+
 @pytest.mark.parametrize("chunks", [0, 3])
 @pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "all_fdce"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
@@ -403,7 +441,7 @@ def test_fused_equals_separate_passes(combo):
 # The benchmark configurations at full size
 # ---------------------------------------------------------------------------
 FULL = ["ce_z_tiny_f32", "ce_z_bf16", "ce_fkl_bf16", "ce_rkl_bf16", "grpo_z_ent_bf16", "all_combined_bf16",
-        "ce_z_f16", "ce_fdce_bf16"]
+        "ce_z_f16", "ce_fdce_bf16", "ce_fkl_hinton_bf16"]
 
 
 def _full_inputs(name):

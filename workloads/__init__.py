@@ -23,7 +23,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-CE, ZLOSS, FKL, RKL, GRPO, ENTROPY, FDCE, GSPO, ACCUMULATE = 1, 2, 4, 8, 16, 32, 64, 128, 1 << 16
+CE, ZLOSS, FKL, RKL, GRPO, ENTROPY, FDCE, GSPO, ACCUMULATE, HINTON = 1, 2, 4, 8, 16, 32, 64, 128, 1 << 16, 1 << 17
 
 
 @dataclass(frozen=True)
@@ -79,6 +79,11 @@ WORKLOADS = {
         "ce_fdce_bf16", N=4096, V=151936, dtype="bf16", flags=CE | FDCE,
         weights=dict(ce=0.5, distill=1.0), temperature=2.0,
         description="the forward-KL inputs with from-distribution cross-entropy distillation"),
+    "ce_fkl_hinton_bf16": Workload(
+        "ce_fkl_hinton_bf16", N=4096, V=151936, dtype="bf16", flags=CE | FKL | HINTON,
+        weights=dict(ce=0.5, distill=1.0), temperature=2.0,
+        description="the forward-KL inputs with the Hinton temperature mode (student tempered too, "
+                    "times tau^2)"),
     "grpo_z_ent_bf16": Workload(
         "grpo_z_ent_bf16", N=16384, V=151936, dtype="bf16", flags=GRPO | ZLOSS | ENTROPY,
         weights=dict(ce=0.0, z=0.01, grpo=1.0), eps=0.2, seq_len=512, old_noise_std=0.05,
@@ -111,6 +116,7 @@ HEADLINE = "grpo_z_ent_bf16"
 def seed_for(name: str, subcase: int = 0) -> int:
     order = ["ce_z_tiny_f32", "ce_z_bf16", "ce_fkl_bf16", "grpo_z_ent_bf16", "all_combined_bf16"]
     base = {"ce_rkl_bf16": "ce_fkl_bf16", "ce_fdce_bf16": "ce_fkl_bf16", "ce_z_f16": "ce_z_bf16",
+            "ce_fkl_hinton_bf16": "ce_fkl_bf16",
             "gspo_z_ent_bf16": "grpo_z_ent_bf16"}.get(name, name)
     return 1000 * (order.index(base) + 1) + subcase
 
@@ -171,7 +177,7 @@ def generate(w: Workload | str, device="cpu", seed: int | None = None, n_rows: i
         y = torch.where(bernoulli(N, 0.7), cols, uniform_labels(N))
         y[bernoulli(N, 0.1)] = -100
         out["labels"] = y
-    elif w.name in ("ce_fkl_bf16", "ce_rkl_bf16", "ce_fdce_bf16"):
+    elif w.name in ("ce_fkl_bf16", "ce_rkl_bf16", "ce_fdce_bf16", "ce_fkl_hinton_bf16"):
         t = torch.empty((N, V), dtype=dt, device=device)
         x = torch.empty((N, V), dtype=dt, device=device)
         for r0 in range(0, N, chunk_rows):
