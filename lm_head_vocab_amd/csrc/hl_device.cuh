@@ -12,9 +12,10 @@
 //                  registers it already holds;
 //   reduce_kernel  fixed-order fp64 sum of the per-row values into the batch
 //                  scalars.
-// With GSPO the fused kernel runs forward-only, a segment kernel turns the
-// row statistics into per-segment ratios and per-row coefficients, and
-// grad_kernel reloads each row to write the gradient.
+// With GSPO the fused kernel runs twice: forward-only (row statistics), then,
+// after a segment kernel has turned the statistics into per-segment ratios and
+// per-row coefficients, in load mode (the statistics read back from the row
+// records, the slice reloaded, the gradient written).
 //
 // The gradient is written in the two-coefficient form of Fast-LLM PR #558
 // (Triton kernel for the monolithic loss, section Design): prob_coeff times
@@ -573,6 +574,16 @@ void fused_kernel(const FusedParams p) {
         if (TMODE != TM_NONE) te = T::load1(trow, eidx);
     }
 
+    Rec r;
+    if (p.load_mode) {
+        // Load mode (the backward of a two-launch call): the row's statistics
+        // are final already, in the record the forward launch wrote; only the
+        // slice is needed again, for pass 2.
+        const float* rec = p.row_rec + row * REC;
+        r.M = rec[R_M]; r.Z = rec[R_Z]; r.S = rec[R_S];
+        r.Mt = rec[R_MT]; r.Zt = rec[R_ZT]; r.SX = rec[R_SX]; r.St = rec[R_ST]; r.Zs = rec[R_ZS];
+        __syncthreads();   // s_row, written by thread 0 above
+    } else {
     // ---- pass 1: sums relative to a provisional wave shift, log2 domain ----
     // The shift is the wave's maximum over its first vector, not the row
     // maximum: any shift gives the same statistics once records are merged
@@ -703,7 +714,7 @@ void fused_kernel(const FusedParams p) {
     __syncthreads();
 
     // ---- combine the waves' records (every wave, DPP tree over 16 lanes) ----
-    Rec r = rec_empty();
+    r = rec_empty();
     {
         const int w = lane & 15;
         if (w < NW) {
@@ -797,10 +808,24 @@ void fused_kernel(const FusedParams p) {
         out[R_XY] = s_row[0];
         out[R_VALID] = 1.0f;
     }
+    }   // pass 1
     if (p.grad == nullptr) return;
 
     // ---- gradient coefficients (fp32, every thread) ----
-    const Coefs kf = row_coefs<TMODE, SOFTCAP>(p, r, y, s_row[0], s_row[1], s_row[2]);
+    Coefs kf = row_coefs<TMODE, SOFTCAP>(p, r, y, s_row[0], s_row[1], s_row[2]);
+    if (p.row_coef != nullptr && p.w_g != 0.f) {
+        // GSPO: d(loss)/d(logp_t) = -coef_t / n_seg; d logp_t / d s_j = [j == y] - q_j
+        const uint32_t n_seg = p.ctrl[CTRL_NSEG];
+        const float e = n_seg > 0u ? p.grad_scale * p.k * p.w_g * p.row_coef[row] / (float)n_seg : 0.f;
+        kf.alpha += e;
+        kf.beta += e;
+        if (TMODE == TM_RKL) kf.c0 += e;   // there c0 multiplies q (alpha is unused); in the
+                                           // Hinton reverse KL it multiplies the tempered q
+    }
+    if (p.load_mode && p.ctrl[CTRL_ERROR] != 0u) {
+        // statistics or segments are not trustworthy: make the gradient say so
+        kf.alpha = kf.beta = kf.c0 = __builtin_nanf("");
+    }
     auto grad_elem = [&](float x, float t, float lab) -> float {
         return grad_one<TMODE, SOFTCAP>(p, kf, x, t, lab);
     };
@@ -846,128 +871,6 @@ template <typename T, int BLOCK, int NVEC, int TMODE, bool SOFTCAP>
 hipError_t launch_fused(const FusedParams& p, dim3 grid, hipStream_t s) {
     (void)hipGetLastError();   // drop an error left by an earlier, unrelated call
     hipLaunchKernelGGL((fused_kernel<T, BLOCK, NVEC, TMODE, SOFTCAP>), grid, dim3(BLOCK), 0, s, p);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// grad_kernel: the load-mode backward. One workgroup per row reloads the row
-// (and the teacher row) after the softmax statistics are final, and writes the
-// gradient with the same coefficients as the fused kernel plus a per-row
-// label-column coefficient from the GSPO segment step. Fast-LLM PR #558, section
-// Design: with GSPO present, a per-segment step runs between the forward and
-// a load-mode backward and hands it a per-token coefficient that superposes
-// with the in-kernel losses.
-// ---------------------------------------------------------------------------
-template <typename T, int TMODE, bool SOFTCAP>
-__global__ __launch_bounds__(kGradBlock) void grad_kernel(const FusedParams p) {
-    constexpr int VEC = T::VEC;
-    constexpr int ES = T::ESIZE;
-    constexpr int U = 4;                      // vectors in flight per thread and tensor
-    const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
-
-    bool valid, bad;
-    int64_t y;
-    row_status(p.labels, p.mask, row, p.V, valid, bad, y);
-
-    const int64_t V = p.V;
-    const int64_t rowoff = row * V;
-    const int mis = (int)((rowoff * ES) & 15);
-    int head = mis ? (16 - mis) / ES : 0;
-    if (head > V) head = (int)V;
-    const int64_t nbv = (V - head) / VEC;
-    const int tail = (int)(V - head - nbv * VEC);
-    const int n_extra = head + tail;
-    const char* xrow = static_cast<const char*>(p.logits) + rowoff * ES;
-    const char* trow = static_cast<const char*>(p.teacher) + rowoff * ES;
-    char* grow = static_cast<char*>(p.grad) + rowoff * ES;
-    const u32x4* xv = reinterpret_cast<const u32x4*>(xrow + (int64_t)head * ES);
-    const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)head * ES);
-    u32x4* gv = reinterpret_cast<u32x4*>(grow + (int64_t)head * ES);
-
-    if (!valid) {
-        if (!p.accumulate) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            for (int64_t i = tid; i < nbv; i += kGradBlock) st_stream(gv + i, z);
-            for (int e = tid; e < n_extra; e += kGradBlock) {
-                const int64_t ei = e < head ? e : head + nbv * VEC + (e - head);
-                T::store1(grow, ei, 0.0f);
-            }
-        }
-        return;
-    }
-
-    const float* rec = p.row_rec + row * REC;
-    Rec r;
-    r.M = rec[R_M]; r.Z = rec[R_Z]; r.S = rec[R_S];
-    r.Mt = rec[R_MT]; r.Zt = rec[R_ZT]; r.SX = rec[R_SX]; r.St = rec[R_ST]; r.Zs = rec[R_ZS];
-    const float old = p.old_logprobs ? p.old_logprobs[row] : 0.f;
-    const float adv = p.advantages ? p.advantages[row] : 0.f;
-    Coefs k = row_coefs<TMODE, SOFTCAP>(p, r, y, rec[R_XY], old, adv);
-    if (p.row_coef != nullptr && p.w_g != 0.f) {
-        // GSPO: d(loss)/d(logp_t) = -coef_t / n_seg; d logp_t / d s_j = [j == y] - q_j
-        const uint32_t n_seg = p.ctrl[CTRL_NSEG];
-        const float e = n_seg > 0u ? p.grad_scale * p.k * p.w_g * p.row_coef[row] / (float)n_seg : 0.f;
-        k.alpha += e;
-        k.beta += e;
-        if (TMODE == TM_RKL) k.c0 += e;   // there c0 multiplies q (alpha is unused); in the
-                                          // Hinton reverse KL it multiplies the tempered q
-    }
-    if (p.ctrl[CTRL_ERROR] != 0u) {
-        // statistics or segments are not trustworthy: make the gradient say so
-        k.alpha = k.beta = k.c0 = __builtin_nanf("");
-    }
-
-    int64_t yv = -1;
-    int ly = 0;
-    if (y >= head && y < head + nbv * VEC) {
-        yv = (y - head) / VEC;
-        ly = (int)((y - head) % VEC);
-    }
-
-    for (int64_t base = 0; base < nbv; base += (int64_t)kGradBlock * U) {
-        u32x4 xs[U], ts[TMODE != TM_NONE ? U : 1], gs[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = base + u * kGradBlock + tid;
-            if (i < nbv) {
-                xs[u] = ld_stream(xv + i);
-                if (TMODE != TM_NONE) ts[u] = ld_stream(tv + i);
-                if (p.accumulate) gs[u] = ld_stream(gv + i);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = base + u * kGradBlock + tid;
-            if (i < nbv) {
-                float g[VEC];
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    g[e] = grad_one<TMODE, SOFTCAP>(p, k, T::get(xs[u], e),
-                                                    TMODE != TM_NONE ? T::get(ts[u], e) : 0.f,
-                                                    (i == yv && e == ly) ? k.beta : 0.f);
-                if (p.accumulate) {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) g[e] = T::get(gs[u], e) + g[e];
-                }
-                st_stream(gv + i, T::pack(g));
-            }
-        }
-    }
-    for (int e = tid; e < n_extra; e += kGradBlock) {
-        const int64_t ei = e < head ? e : head + nbv * VEC + (e - head);
-        const float x = T::load1(xrow, ei);
-        const float t = TMODE != TM_NONE ? T::load1(trow, ei) : 0.f;
-        float g = grad_one<TMODE, SOFTCAP>(p, k, x, t, ei == y ? k.beta : 0.f);
-        if (p.accumulate) g = T::load1(grow, ei) + g;
-        T::store1(grow, ei, g);
-    }
-}
-
-template <typename T, int TMODE, bool SOFTCAP>
-hipError_t launch_grad(const FusedParams& p, hipStream_t s) {
-    (void)hipGetLastError();
-    hipLaunchKernelGGL((grad_kernel<T, TMODE, SOFTCAP>), dim3((unsigned)p.n_rows), dim3(kGradBlock), 0, s, p);
     return hipGetLastError();
 }
 

@@ -26,7 +26,6 @@ struct hl_plan_s {
     int forced_block;
     Geometry geo;
     FusedLauncher fused;
-    GradLauncher grad;   // load-mode backward (GSPO plans)
     void* ws;
     size_t ws_bytes;
     bool ws_owned;
@@ -169,12 +168,6 @@ hl_status choose(hl_plan_s* p) {
         p->geo = g;
     }
     p->fused = lookup(p->dtype, p->tmode, p->geo.block, p->geo.nvec, p->softcap > 0.f);
-    if (p->flags & HL_GSPO) {
-        const bool sc = p->softcap > 0.f;
-        p->grad = p->dtype == HL_F32 ? get_grad_f32(p->tmode, sc)
-                : p->dtype == HL_F16 ? get_grad_f16(p->tmode, sc) : get_grad_bf16(p->tmode, sc);
-        if (p->grad == nullptr) return HL_ERR_UNSUPPORTED;
-    }
     return p->fused ? HL_OK : HL_ERR_UNSUPPORTED;
 }
 
@@ -419,6 +412,7 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
         fp.grad = gspo ? nullptr : grad_out;
         fp.row_rec = row_rec;
         fp.row_coef = nullptr;
+        fp.load_mode = 0;
         fp.chunk_words = chunk_words;
         fp.ctrl = ctrl;
         fp.n_rows = n_rows;
@@ -466,10 +460,13 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
             e = launch_seam(sp, stream);
             if (e != hipSuccess) return hip_fail("segment kernel launch", e);
             if (grad_out != nullptr) {
+                // the backward: the fused kernel again, in load mode, with the
+                // per-row GSPO coefficient on the label column
                 fp.grad = grad_out;
                 fp.row_coef = sp.row_coef;
-                e = plan->grad(fp, stream);
-                if (e != hipSuccess) return hip_fail("gradient kernel launch", e);
+                fp.load_mode = 1;
+                e = plan->fused(fp, grid, stream);
+                if (e != hipSuccess) return hip_fail("fused kernel launch (load mode)", e);
             }
         }
         if (plan->ev_after && (e = hipEventRecord(plan->ev_after, stream)) != hipSuccess)

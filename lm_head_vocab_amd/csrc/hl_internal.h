@@ -85,7 +85,8 @@ struct FusedParams {
     float* row_rec;           // [N, REC]
     uint64_t* chunk_words;    // [N, C, XWORDS]
     uint32_t* ctrl;           // [NCTRL]
-    const float* row_coef;    // [N] GSPO label-column coefficient per row (gradient kernel only)
+    const float* row_coef;    // [N] GSPO label-column coefficient per row, or nullptr
+    int load_mode;            // 1: statistics from row_rec (second launch of a GSPO call)
     int64_t n_rows;
     int64_t V;
     int chunks;
@@ -156,10 +157,7 @@ struct SeamParams {
     float k, cap, eps;
 };
 
-constexpr int kGradBlock = 512;     // threads per row in the load-mode gradient kernel
-
 typedef hipError_t (*FusedLauncher)(const FusedParams&, dim3 grid, hipStream_t);
-typedef hipError_t (*GradLauncher)(const FusedParams&, hipStream_t);
 
 // One getter per (dtype, teacher mode) translation unit; nullptr when the
 // requested (block, nvec, softcap) instance does not exist.
@@ -184,11 +182,6 @@ FusedLauncher get_fused_bf16_fdceh(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f16_fklh(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f16_rklh(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f16_fdceh(int block, int nvec, bool softcap);
-
-// Load-mode gradient kernels, one getter per dtype: nullptr for an unknown mode.
-GradLauncher get_grad_f32(int tmode, bool softcap);
-GradLauncher get_grad_bf16(int tmode, bool softcap);
-GradLauncher get_grad_f16(int tmode, bool softcap);
 
 hipError_t launch_count(const CountParams& p, hipStream_t s);  // grid grows when p.fresh
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);

@@ -1,9 +1,10 @@
 """GPU parity of the GSPO path against the fp64 oracle.
 
-The path is three kernels behind hl_forward_backward_segments: the fused
-kernel in forward-only mode (row statistics), the segment step (sequence
-ratios and per-token label-column coefficients) and the load-mode gradient
-kernel, as in the GSPO case of Fast-LLM PR #558 (section Design).
+The path behind hl_forward_backward_segments: the fused kernel in
+forward-only mode (row statistics), the segment step (sequence ratios and
+per-token label-column coefficients) and the fused kernel again in load mode
+(statistics read back, slice reloaded, gradient written), as in the GSPO case
+of Fast-LLM PR #558 (section Design).
 
 Tolerances are those of the other parity tests (fp32: scalars 1e-5 relative,
 gradient 1e-6 absolute; bf16: scalars 1e-4 relative, gradient rms-relative
