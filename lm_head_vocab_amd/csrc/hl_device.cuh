@@ -148,17 +148,16 @@ __device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) { __builtin_nontemp
 __device__ __forceinline__ float fast_exp2(float a) { return __builtin_amdgcn_exp2f(a); }
 
 // tanh from its definition: the odd Taylor polynomial (coefficients
-// 2^(2n) (2^(2n)-1) B_2n / (2n)!, terms z .. z^11) for |z| < 0.3, where the
-// truncation error is below 1e-9 and the fp32 result within 1.2e-7 relative,
-// and 1 - 2 / (exp(2|z|) + 1) above, where that form has no cancellation
-// (within 2.6e-7 relative).
+// 2^(2n) (2^(2n)-1) B_2n / (2n)!, terms z .. z^9) for |z| < 0.25, where the
+// truncation error is below 1e-8 relative and the fp32 result within 1.2e-7,
+// and 1 - 2 / (exp(2|z|) + 1) above, where that form has no damaging
+// cancellation (within 2.6e-7 relative).
 __device__ __forceinline__ float hl_tanh(float z) {
     const float az = fabsf(z);
     float r;
-    if (az < 0.3f) {
+    if (az < 0.25f) {
         const float z2 = z * z;
-        float p = -0.008863235529902197f;
-        p = fmaf(p, z2, 0.021869488536155203f);
+        float p = 0.021869488536155203f;
         p = fmaf(p, z2, -0.05396825396825397f);
         p = fmaf(p, z2, 0.13333333333333333f);
         p = fmaf(p, z2, -0.3333333333333333f);

@@ -68,6 +68,9 @@ def test_status_strings():
     (dict(w=Weights(1, 0, 0, 0, math.inf, 0)), hl.HL_ERR_INVALID_ARG),
     (dict(V=10**9), hl.HL_ERR_UNSUPPORTED),
     (dict(V=1_500_000), hl.HL_ERR_UNSUPPORTED),
+    (dict(V=1_474_561 + 8), hl.HL_ERR_UNSUPPORTED),              # past 9 x 1024 x 20 vectors
+    (dict(V=737_280 + 8, flags=hl.RKL), hl.HL_ERR_UNSUPPORTED),   # past 9 x 1024 x 10 teacher vectors
+    (dict(V=655_360 + 8, flags=hl.FDCE | hl.HINTON), hl.HL_ERR_UNSUPPORTED),   # 8 chunks at most
 ])
 def test_plan_rejects(kwargs, status):
     st, h = _plan(**kwargs)

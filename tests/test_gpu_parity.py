@@ -359,6 +359,23 @@ def test_outlier_logits(dtype, combo, chunks):
     assert abs(sc[e] - ref_sc[e]) <= 2e-6 + TOL[dtype]["scalar_rel"] * abs(ref_sc[e]), (sc[e], ref_sc[e])
 
 
+# the longest rows each mode supports: 9 chunks x 1024 threads x 20 vectors
+# (student), x 10 vectors (teacher), 8 chunks for from-distribution CE with
+# the Hinton temperature (8 exchanged statistics per chunk)
+MAX_V = [("bf16", "ce_z", 1_474_560, (9, 1024, 20)), ("bf16", "ce_z", 1_474_553, (9, 1024, 20)),
+         ("f32", "ce_z", 737_280, (9, 1024, 20)), ("bf16", "all_rkl", 737_280, (9, 1024, 10)),
+         ("bf16", "all_fdce_h", 655_360, (8, 1024, 10))]
+
+
+@pytest.mark.parametrize("case", MAX_V, ids=[f"{d}-{c}-{v}" for d, c, v, _ in MAX_V])
+def test_maximum_vocabulary(case):
+    dtype, combo, V, geo = case
+    spec, inp = _small(dtype, combo, 3, V, seed=V % 1000, mask_frac=0.0, ignore_frac=0.0)
+    plan, _, _ = _check_small(spec, inp, dtype)
+    d = plan.describe()
+    assert (d["chunks"], d["block"], d["vec_per_thread"]) == geo
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_edge_cases(dtype):
     dt = TDT[dtype]
