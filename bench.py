@@ -126,7 +126,7 @@ def cpu_baseline(w, budget_s: float, threads: int):
 def stored_traffic(w, src_hash):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources; else None."""
-    tag = "fused_seam_grad" if w.flags & workloads.GSPO else FUSED_KERNEL
+    tag = "fused_seam" if w.flags & workloads.GSPO else FUSED_KERNEL
     path = os.path.join(ROOT, "profiles", f"{tag}_{w.name}_pmc.json")
     if not os.path.exists(path):
         return None
