@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of the fused LM-head loss on one MI355X.
 
-A step is one hl_forward_backward call (valid-row count, fused softmax +
-losses + gradient kernel, batch reduction) over one batch of synthetic
+A step is one hl_forward_backward call (valid-row count, the fused kernel:
+shared softmax, every loss and the gradient, then the batch reduction; GSPO
+workloads call hl_forward_backward_segments) over one batch of synthetic
 inputs already resident in HBM. Prints one JSON line on stdout; progress
 goes to stderr.
 

@@ -271,8 +271,8 @@ hl_status hl_plan_describe(hl_plan_t plan, int* chunks, int* block, int* vec_per
 
 /* Record the two events (hipEvent_t, may be NULL to stop) immediately before
  * and after the fused kernel of every later call (with HL_GSPO: before the
- * forward kernel and after the gradient kernel), on the call's stream, so a
- * profiler can time the dominant kernel alone. */
+ * forward launch and after the load-mode launch of the fused kernel), on the
+ * call's stream, so a profiler can time the dominant kernel alone. */
 hl_status hl_plan_set_timing_events(hl_plan_t plan, hipEvent_t before, hipEvent_t after);
 
 /* Text of the last HIP failure seen by this thread (which call, the HIP
