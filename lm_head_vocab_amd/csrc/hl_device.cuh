@@ -51,6 +51,10 @@ struct F32T {
     __device__ static __forceinline__ float load1(const char* rowbase, int64_t i) {
         return reinterpret_cast<const float*>(rowbase)[i];
     }
+    __device__ static __forceinline__ uint32_t raw1(const char* rowbase, int64_t i) {
+        return reinterpret_cast<const uint32_t*>(rowbase)[i];
+    }
+    __device__ static __forceinline__ float from_raw(uint32_t b) { return __uint_as_float(b); }
     __device__ static __forceinline__ void store1(char* rowbase, int64_t i, float g) {
         reinterpret_cast<float*>(rowbase)[i] = g;
     }
@@ -81,6 +85,10 @@ struct BF16T {
         const uint32_t h = reinterpret_cast<const uint16_t*>(rowbase)[i];
         return __uint_as_float(h << 16);
     }
+    __device__ static __forceinline__ uint32_t raw1(const char* rowbase, int64_t i) {
+        return reinterpret_cast<const uint16_t*>(rowbase)[i];
+    }
+    __device__ static __forceinline__ float from_raw(uint32_t b) { return __uint_as_float(b << 16); }
     // Running max over the 8 elements of a vector, used only as the softmax
     // shift: the odd element is read as the whole 32-bit word (its bf16 bits
     // plus the even element's bits below them), which is within one bf16 ulp
@@ -118,6 +126,12 @@ struct F16T {
     }
     __device__ static __forceinline__ float load1(const char* rowbase, int64_t i) {
         return (float)reinterpret_cast<const _Float16*>(rowbase)[i];
+    }
+    __device__ static __forceinline__ uint32_t raw1(const char* rowbase, int64_t i) {
+        return reinterpret_cast<const uint16_t*>(rowbase)[i];
+    }
+    __device__ static __forceinline__ float from_raw(uint32_t b) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
     }
     __device__ static __forceinline__ float vmax(float acc, const u32x4& w) {
 #pragma unroll
@@ -168,6 +182,18 @@ __device__ __forceinline__ float hl_tanh(float z) {
         r = copysignf(r, z);
     }
     return r;
+}
+
+// Softcap on the element paths, branch-free: with r = 1 / (exp(2 k x / c) + 1),
+// tanh(k x / c) = 1 - 2 r, so the log2-domain logit is s log2(e) =
+// c log2(e) - 2 c log2(e) r and the chain factor 1 - tanh^2 is 4 r (1 - r).
+// 1 - 2 r is exact given r, so the absolute error of tanh stays within a few
+// 2^-24 for every argument; the relative error near zero is larger than the
+// polynomial's above, but the softmax, the z-loss and the entropy see s only
+// through differences and through s itself. exp overflow gives r = 0
+// (tanh = 1) and underflow r = 1 (tanh = -1), each with a zero chain factor.
+__device__ __forceinline__ float cap_r(float x, float kc2) {
+    return __builtin_amdgcn_rcpf(fast_exp2(x * kc2) + 1.0f);
 }
 
 // ---------------------------------------------------------------------------
@@ -345,6 +371,8 @@ struct Coefs {
     float gq;      // tempered student coefficient (Hinton forward KL / FDCE)
     float rho2;    // reverse-KL log-ratio coefficient (log2 domain)
     float c0;      // reverse-KL probability coefficient
+    float sB;      // pass-2 student exponent offset: -B2, or c log2(e) - B2 with softcap
+    float sBd;     // tempered student offset: -Bd, or c log2(e) beta - Bd with softcap
 };
 
 // All data registers are live where the fused kernel calls this, so only
@@ -372,6 +400,8 @@ __device__ __forceinline__ Coefs row_coefs(const FusedParams& p, const Rec& r, i
             kl = kLn2f * (r.SX * __builtin_amdgcn_rcpf(r.Z) - l2Z + l2Zt);
         }
     }
+    k.sB = SOFTCAP ? p.cl - k.B2 : -k.B2;
+    k.sBd = SOFTCAP ? fmaf(p.cl, p.beta, -k.Bd) : -k.Bd;
     float a_g = 0.f;
     if ((f & F_GRPO) && y >= 0) {
         const float sy = SOFTCAP ? p.cap * hl_tanh(xy * p.kc) : p.k * xy;
@@ -410,16 +440,17 @@ __device__ __forceinline__ Coefs row_coefs(const FusedParams& p, const Rec& r, i
 template <int TMODE, bool SOFTCAP>
 __device__ __forceinline__ float grad_one(const FusedParams& p, const Coefs& k, float x, float t, float lab) {
     if (is_hinton(TMODE)) {
-        float sl, cfh = 1.0f;            // s log2(e)
+        float aq, aqd, cfh = 1.0f;       // log2 of the student and of the tempered student
         if (SOFTCAP) {
-            const float th = hl_tanh(x * p.kc);
-            sl = p.cap * th * kLog2e;
-            cfh = fmaf(-th, th, 1.0f);
+            const float r = cap_r(x, p.kc2);
+            aq = fmaf(r, -2.0f * p.cl, k.sB);
+            aqd = fmaf(r, -2.0f * p.cl * p.beta, k.sBd);
+            cfh = r * fmaf(-4.0f, r, 4.0f);
         } else {
-            sl = x * p.K1;
+            aq = fmaf(x, p.K1, k.sB);
+            aqd = fmaf(x, p.K1 * p.beta, k.sBd);
         }
-        const float q = fast_exp2(sl - k.B2);
-        const float aqd = fmaf(sl, p.beta, -k.Bd);     // log2 of the tempered student
+        const float q = fast_exp2(aq);
         const float qd = fast_exp2(aqd);
         float g;
         if (fkl_like(TMODE)) {
@@ -433,11 +464,11 @@ __device__ __forceinline__ float grad_one(const FusedParams& p, const Coefs& k, 
     }
     float aq, cf = 1.0f;
     if (SOFTCAP) {
-        const float th = hl_tanh(x * p.kc);
-        aq = fmaf(p.cap * th, kLog2e, -k.B2);
-        cf = fmaf(-th, th, 1.0f);
+        const float r = cap_r(x, p.kc2);
+        aq = fmaf(r, -2.0f * p.cl, k.sB);
+        cf = r * fmaf(-4.0f, r, 4.0f);
     } else {
-        aq = fmaf(x, p.K1, -k.B2);
+        aq = fmaf(x, p.K1, k.sB);
     }
     const float q = fast_exp2(aq);
     float g;
@@ -482,6 +513,7 @@ void fused_kernel(const FusedParams p) {
     __shared__ float s_fin[REC];
     __shared__ float s_xw[kMaxChunks * XWORDS];
     __shared__ float s_row[8];
+    __shared__ float s_lrec[REC];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -547,41 +579,74 @@ void fused_kernel(const FusedParams p) {
         return;
     }
 
-    // Per-row scalars, fetched early by one thread.
+    // ---- loads, in the order their values are needed ----
+    // Vector loads complete in issue order, so the small loads go first and
+    // are consumed only after the slice's loads are in flight: threads 0..2
+    // fetch the per-row scalars (label logit, old log-prob, advantage), in
+    // load mode threads 8.. the row's statistics, and the head/tail lanes
+    // their element.
+    uint32_t small_b = 0u;
     if (tid == 0) {
-        s_row[0] = (y >= 0) ? T::load1(xrow, y) : 0.0f;
-        s_row[1] = p.old_logprobs ? p.old_logprobs[row] : 0.0f;
-        s_row[2] = p.advantages ? p.advantages[row] : 0.0f;
+        if (y >= 0) small_b = T::raw1(xrow, y);
+    } else if (tid == 1) {
+        if (p.old_logprobs) small_b = __float_as_uint(p.old_logprobs[row]);
+    } else if (tid == 2) {
+        if (p.advantages) small_b = __float_as_uint(p.advantages[row]);
+    } else if (p.load_mode && tid >= 8 && tid < 8 + REC) {
+        small_b = __float_as_uint(p.row_rec[row * REC + (tid - 8)]);
+    }
+    uint32_t xe_b = 0u, te_b = 0u;
+    if (has_e) {
+        xe_b = T::raw1(xrow, eidx);
+        if (TMODE != TM_NONE) te_b = T::raw1(trow, eidx);
     }
 
-    // ---- load the slice into registers (read once) ----
-    // Per-vector bounds and addresses are uniform (vector v of thread tid is
-    // element v * BLOCK + tid of the slice), so each test is tid < uniform and
-    // every address is a uniform base plus the one per-thread offset.
+    // The slice into registers (read once). Vector v of thread tid is element
+    // v * BLOCK + tid of the slice, so each wave instruction covers 1 KiB of
+    // consecutive bytes.
+    //
+    // With a teacher every slot is loaded, without a branch (a skipped load
+    // would leave the compiler unable to wait for the first vectors alone), so
+    // that pass 1 starts on the first vectors while later ones are still
+    // arriving: a slot past the slice re-reads the row's last body vector (in
+    // bounds) and its value is never used; a row without body vectors points
+    // the loads at the workspace's row records instead. A student-only slice
+    // loads only its own slots and starts once all have arrived: timed on the
+    // student rows, the extra requests and the earlier start were each about
+    // 1% slower, while on the teacher rows the early start is 5-8% faster.
     u32x4 xs[NVEC];
     u32x4 ts[TMODE != TM_NONE ? NVEC : 1];
+    if (TMODE == TM_NONE) {
 #pragma unroll
-    for (int v = 0; v < NVEC; ++v) {
-        if (tid < nv - v * BLOCK) {
-            xs[v] = ld_stream(xv + v * BLOCK + tid);
-            if (TMODE != TM_NONE) ts[v] = ld_stream(tv + v * BLOCK + tid);
+        for (int v = 0; v < NVEC; ++v)
+            if (tid < nv - v * BLOCK) xs[v] = ld_stream(xv + v * BLOCK + tid);
+    } else {
+        const bool body = nbv > 0;
+        const u32x4* xb = body ? xv : reinterpret_cast<const u32x4*>(p.row_rec);
+        const u32x4* tb = body ? tv : reinterpret_cast<const u32x4*>(p.row_rec);
+        const int lastv = body ? (int)(nbv - 1 - vb) : 0;   // negative for an empty chunk
+#pragma unroll
+        for (int v = 0; v < NVEC; ++v) {
+            int i = v * BLOCK + tid;
+            i = i < lastv ? i : lastv;
+            xs[v] = ld_stream(xb + i);
+            ts[v] = ld_stream(tb + i);
         }
     }
-    float xe = 0.f, te = 0.f;
-    if (has_e) {
-        xe = T::load1(xrow, eidx);
-        if (TMODE != TM_NONE) te = T::load1(trow, eidx);
-    }
+    if (tid < 3) s_row[tid] = tid == 0 ? T::from_raw(small_b) : __uint_as_float(small_b);
+    if (p.load_mode && tid >= 8 && tid < 8 + REC) s_lrec[tid - 8] = __uint_as_float(small_b);
+    const float xe = has_e ? T::from_raw(xe_b) : 0.f;
+    const float te = (has_e && TMODE != TM_NONE) ? T::from_raw(te_b) : 0.f;
 
     Rec r;
     if (p.load_mode) {
         // Load mode (the backward of a two-launch call): the row's statistics
         // are final already, in the record the forward launch wrote; only the
         // slice is needed again, for pass 2.
-        const float* rec = p.row_rec + row * REC;
-        r.M = rec[R_M]; r.Z = rec[R_Z]; r.S = rec[R_S];
-        r.Mt = rec[R_MT]; r.Zt = rec[R_ZT]; r.SX = rec[R_SX]; r.St = rec[R_ST]; r.Zs = rec[R_ZS];
-        __syncthreads();   // s_row, written by thread 0 above
+        __syncthreads();   // s_row and s_lrec, written above
+        r.M = s_lrec[R_M]; r.Z = s_lrec[R_Z]; r.S = s_lrec[R_S];
+        r.Mt = s_lrec[R_MT]; r.Zt = s_lrec[R_ZT]; r.SX = s_lrec[R_SX]; r.St = s_lrec[R_ST];
+        r.Zs = s_lrec[R_ZS];
     } else {
     // ---- pass 1: sums relative to a provisional wave shift, log2 domain ----
     // The shift is the wave's maximum over its first vector, not the row
@@ -612,7 +677,7 @@ void fused_kernel(const FusedParams p) {
     auto term = [&](auto want_s_tag, float x, float t, float& z, float& s, float& zt, float& sx, float& st,
                     float& zs) {
         constexpr bool WS = decltype(want_s_tag)::value;
-        const float a = SOFTCAP ? fmaf(p.cap * hl_tanh(x * p.kc), kLog2e, -M) : fmaf(x, p.K1, -M);
+        const float a = SOFTCAP ? fmaf(cap_r(x, p.kc2), -2.0f * p.cl, p.cl - M) : fmaf(x, p.K1, -M);
         const float ex = fast_exp2(a);
         z += ex;
         if (WS) s = fmaf(ex, a, s);
@@ -712,51 +777,53 @@ void fused_kernel(const FusedParams p) {
     }
     __syncthreads();
 
-    // ---- combine the waves' records (every wave, DPP tree over 16 lanes) ----
-    r = rec_empty();
-    {
-        const int w = lane & 15;
-        if (w < NW) {
-            r.M = s_rec[w][0];
-            r.Z = s_rec[w][1];
-            r.S = s_rec[w][2];
-            if (TMODE != TM_NONE) {
-                r.Mt = s_rec[w][3];
-                r.Zt = s_rec[w][4];
-                r.SX = s_rec[w][5];
-                if (has_st(TMODE)) r.St = s_rec[w][6];
-                if (is_hinton(TMODE)) r.Zs = s_rec[w][7];
+    // ---- combine the waves' records, then (split-vocab) the chunks' ----
+    // Wave 0 alone merges (the other waves wait at the barrier below, so
+    // their SIMDs are free for the other workgroups of the CU) and leaves the
+    // row's final statistics in shared memory.
+    //
+    // Split-vocab exchange: each statistic travels as one 64-bit atomic word,
+    // its float bits and the call's epoch (bumped by the count kernel before
+    // this kernel starts). A sibling's word is taken once it carries the
+    // current epoch, so nothing depends on the order in which different
+    // words become visible, and no L2 write-back or invalidate is needed.
+    // Wave 0 polls all C x words in one load per lane per round, then merges
+    // the C records with the same fixed DPP tree in every workgroup of the row.
+    if (wave == 0) {
+        Rec wr = rec_empty();
+        {
+            const int w = lane & 15;
+            if (w < NW) {
+                wr.M = s_rec[w][0];
+                wr.Z = s_rec[w][1];
+                wr.S = s_rec[w][2];
+                if (TMODE != TM_NONE) {
+                    wr.Mt = s_rec[w][3];
+                    wr.Zt = s_rec[w][4];
+                    wr.SX = s_rec[w][5];
+                    if (has_st(TMODE)) wr.St = s_rec[w][6];
+                    if (is_hinton(TMODE)) wr.Zs = s_rec[w][7];
+                }
+                if (wr.Z == 0.f) wr = rec_empty();
             }
-            if (r.Z == 0.f) r = rec_empty();
+            wr = rec_reduce16<TMODE>(wr, p.beta);
         }
-        r = rec_reduce16<TMODE>(r, p.beta);
-    }
-
-    // ---- split-vocab: publish this chunk's record, wait for the others ----
-    // Each statistic travels as one 64-bit atomic word: its float bits and the
-    // call's epoch (bumped by the count kernel before this kernel starts). A
-    // sibling's word is taken once it carries the current epoch, so nothing
-    // depends on the order in which different words become visible, and no
-    // L2 write-back or invalidate is needed. Wave 0 polls all C x 6 words in
-    // one load per lane per round, then merges the C records with the same
-    // fixed DPP tree in every workgroup of the row.
-    if (p.chunks > 1) {
-        // statistics this mode exchanges: M, Z, S (+ Mt, Zt, SX (+ St) (+ Zs)),
-        // packed in that order
-        constexpr int NXW = xwords_used(TMODE);
-        constexpr int POS_ZS = has_st(TMODE) ? 7 : 6;
-        const uint64_t epoch = (uint64_t)p.ctrl[CTRL_EPOCH] << 32;
-        uint64_t* words = p.chunk_words + (int64_t)row * p.chunks * XWORDS;
-        if (tid == 0) {
-            uint64_t* mine = words + c * XWORDS;
-            const float f[XWORDS] = {r.M, r.Z, r.S, r.Mt, r.Zt, r.SX,
-                                     has_st(TMODE) ? r.St : r.Zs, r.Zs};
+        if (p.chunks > 1) {
+            // statistics this mode exchanges: M, Z, S (+ Mt, Zt, SX (+ St) (+ Zs)),
+            // packed in that order
+            constexpr int NXW = xwords_used(TMODE);
+            constexpr int POS_ZS = has_st(TMODE) ? 7 : 6;
+            const uint64_t epoch = (uint64_t)p.ctrl[CTRL_EPOCH] << 32;
+            uint64_t* words = p.chunk_words + (int64_t)row * p.chunks * XWORDS;
+            if (lane == 0) {
+                uint64_t* mine = words + c * XWORDS;
+                const float f[XWORDS] = {wr.M, wr.Z, wr.S, wr.Mt, wr.Zt, wr.SX,
+                                         has_st(TMODE) ? wr.St : wr.Zs, wr.Zs};
 #pragma unroll
-            for (int i = 0; i < NXW; ++i)
-                __hip_atomic_store(mine + i, epoch | __float_as_uint(f[i]), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (wave == 0) {
+                for (int i = 0; i < NXW; ++i)
+                    __hip_atomic_store(mine + i, epoch | __float_as_uint(f[i]), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
             // lane l polls word (l % NXW) of chunk (l / NXW)
             const int nwords = p.chunks * NXW;
             const int lw = (lane / NXW) * XWORDS + lane % NXW;
@@ -786,27 +853,27 @@ void fused_kernel(const FusedParams p) {
                 }
                 if (cr.Z == 0.f) cr = rec_empty();
             }
-            cr = rec_reduce16<TMODE>(cr, p.beta);
-            if (lane == 0) {
-                s_fin[0] = cr.M; s_fin[1] = cr.Z; s_fin[2] = cr.S;
-                s_fin[3] = cr.Mt; s_fin[4] = cr.Zt; s_fin[5] = cr.SX; s_fin[6] = cr.St;
-                s_fin[7] = cr.Zs;
+            wr = rec_reduce16<TMODE>(cr, p.beta);
+        }
+        if (lane == 0) {
+            s_fin[0] = wr.M; s_fin[1] = wr.Z; s_fin[2] = wr.S;
+            s_fin[3] = wr.Mt; s_fin[4] = wr.Zt; s_fin[5] = wr.SX; s_fin[6] = wr.St;
+            s_fin[7] = wr.Zs;
+            // per-row record for the batch reduction (s_row[0] was written by
+            // this thread)
+            if (c == 0) {
+                float* out = p.row_rec + row * REC;
+                out[R_M] = wr.M; out[R_Z] = wr.Z; out[R_S] = wr.S;
+                out[R_MT] = wr.Mt; out[R_ZT] = wr.Zt; out[R_SX] = wr.SX; out[R_ST] = wr.St;
+                out[R_ZS] = wr.Zs;
+                out[R_XY] = s_row[0];
+                out[R_VALID] = 1.0f;
             }
         }
-        __syncthreads();
-        r.M = s_fin[0]; r.Z = s_fin[1]; r.S = s_fin[2];
-        r.Mt = s_fin[3]; r.Zt = s_fin[4]; r.SX = s_fin[5]; r.St = s_fin[6]; r.Zs = s_fin[7];
     }
-
-    // ---- per-row record for the batch reduction ----
-    if (c == 0 && tid == 0) {
-        float* out = p.row_rec + row * REC;
-        out[R_M] = r.M; out[R_Z] = r.Z; out[R_S] = r.S;
-        out[R_MT] = r.Mt; out[R_ZT] = r.Zt; out[R_SX] = r.SX; out[R_ST] = r.St;
-        out[R_ZS] = r.Zs;
-        out[R_XY] = s_row[0];
-        out[R_VALID] = 1.0f;
-    }
+    __syncthreads();
+    r.M = s_fin[0]; r.Z = s_fin[1]; r.S = s_fin[2];
+    r.Mt = s_fin[3]; r.Zt = s_fin[4]; r.SX = s_fin[5]; r.St = s_fin[6]; r.Zs = s_fin[7];
     }   // pass 1
     if (p.grad == nullptr) return;
 

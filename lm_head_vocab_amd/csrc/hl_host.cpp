@@ -429,6 +429,10 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
         fp.tau = plan->temperature;
         fp.cap = plan->softcap;
         fp.kc = plan->softcap > 0.f ? plan->logit_scale / plan->softcap : 0.f;
+        fp.kc2 = plan->softcap > 0.f ? (float)(2.0 * (double)plan->logit_scale * 1.4426950408889634 /
+                                               (double)plan->softcap)
+                                     : 0.f;
+        fp.cl = (float)((double)plan->softcap * 1.4426950408889634);
         fp.w_ce = plan->w.ce;
         fp.w_z = plan->w.z;
         fp.w_d = plan->w.distill;

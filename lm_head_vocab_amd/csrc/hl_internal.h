@@ -100,6 +100,8 @@ struct FusedParams {
     float tau;        // temperature (the Hinton gradient carries tau)
     float cap;        // softcap c (0 = off)
     float kc;         // k / c
+    float kc2;        // 2 k log2(e) / c: exp2 of kc2 x is exp(2 k x / c)
+    float cl;         // c log2(e)
     float w_ce, w_z, w_d, w_g;
     float grad_scale;
     float divisor;
