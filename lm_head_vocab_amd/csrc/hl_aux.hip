@@ -4,8 +4,18 @@
 namespace hl {
 
 // ---------------------------------------------------------------------------
-// count_kernel: one workgroup of 1024 threads.
+// count_kernel: one workgroup of 1024 threads. With 16-byte aligned labels
+// (and mask), thread t takes rows [16 t, 16 t + 16) of every 16384-row tile
+// with eight 16-byte label loads and one 16-byte mask load, all issued before
+// any is used, so a tile costs one memory latency; a ragged last tile and
+// unaligned inputs go one row at a time.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void count_row(int64_t y, bool unmasked, int64_t V, uint32_t& nv, uint32_t& nb) {
+    const bool in_range = (y >= 0) && (y < V);
+    nv += (unmasked && in_range) ? 1u : 0u;
+    nb += (unmasked && !in_range && y != -100) ? 1u : 0u;
+}
+
 __global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
     if (p.fresh) {
         const int64_t stride = (int64_t)gridDim.x * 1024;
@@ -14,13 +24,36 @@ __global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
     }
     __shared__ uint32_t s_v[16], s_b[16];
     uint32_t nv = 0, nb = 0;
-#pragma unroll 8
-    for (int64_t r = threadIdx.x; r < p.n_rows; r += 1024) {
-        bool valid, bad;
-        int64_t y;
-        row_status(p.labels, p.mask, r, p.V, valid, bad, y);
-        nv += valid;
-        nb += bad;
+    if (p.vec) {
+        for (int64_t base = 0; base < p.n_rows; base += 16384) {
+            const int64_t r0 = base + 16 * (int64_t)threadIdx.x;
+            if (r0 + 16 <= p.n_rows) {
+                const u32x4* lv = reinterpret_cast<const u32x4*>(p.labels + r0);
+                u32x4 L[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) L[k] = lv[k];
+                u32x4 m = {~0u, ~0u, ~0u, ~0u};
+                if (p.mask != nullptr) m = *reinterpret_cast<const u32x4*>(p.mask + r0);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const uint64_t lo = L[j >> 1][2 * (j & 1)], hi = L[j >> 1][2 * (j & 1) + 1];
+                    const int64_t y = (int64_t)((hi << 32) | lo);
+                    const bool unmasked = ((m[j >> 2] >> (8 * (j & 3))) & 0xffu) != 0u;
+                    count_row(y, unmasked, p.V, nv, nb);
+                }
+            } else {
+                for (int64_t r = r0; r < p.n_rows && r < r0 + 16; ++r)
+                    count_row(p.labels[r], p.mask == nullptr || p.mask[r] != 0, p.V, nv, nb);
+            }
+        }
+    } else {
+        for (int64_t r = threadIdx.x; r < p.n_rows; r += 1024) {
+            bool valid, bad;
+            int64_t y;
+            row_status(p.labels, p.mask, r, p.V, valid, bad, y);
+            nv += valid;
+            nb += bad;
+        }
     }
     for (int m = 32; m >= 1; m >>= 1) {
         nv += __shfl_xor(nv, m, 64);

@@ -608,12 +608,14 @@ void fused_kernel(const FusedParams p) {
     // With a teacher every slot is loaded, without a branch (a skipped load
     // would leave the compiler unable to wait for the first vectors alone), so
     // that pass 1 starts on the first vectors while later ones are still
-    // arriving: a slot past the slice re-reads the row's last body vector (in
-    // bounds) and its value is never used; a row without body vectors points
-    // the loads at the workspace's row records instead. A student-only slice
-    // loads only its own slots and starts once all have arrived: timed on the
-    // student rows, the extra requests and the earlier start were each about
-    // 1% slower, while on the teacher rows the early start is 5-8% faster.
+    // arriving: a slot past the slice re-reads the slice's own last vector
+    // (the lanes of one instruction that share it make one request, and no
+    // byte outside the slice is fetched) and its value is never used; an
+    // empty slice points the loads at the workspace's row records. A
+    // student-only slice loads only its own slots and starts once all have
+    // arrived: timed on the student rows, the extra requests and the earlier
+    // start were each about 1% slower, while on the teacher rows the early
+    // start is 5-8% faster.
     u32x4 xs[NVEC];
     u32x4 ts[TMODE != TM_NONE ? NVEC : 1];
     if (TMODE == TM_NONE) {
@@ -621,10 +623,10 @@ void fused_kernel(const FusedParams p) {
         for (int v = 0; v < NVEC; ++v)
             if (tid < nv - v * BLOCK) xs[v] = ld_stream(xv + v * BLOCK + tid);
     } else {
-        const bool body = nbv > 0;
+        const bool body = nv > 0;
         const u32x4* xb = body ? xv : reinterpret_cast<const u32x4*>(p.row_rec);
         const u32x4* tb = body ? tv : reinterpret_cast<const u32x4*>(p.row_rec);
-        const int lastv = body ? (int)(nbv - 1 - vb) : 0;   // negative for an empty chunk
+        const int lastv = body ? nv - 1 : 0;
 #pragma unroll
         for (int v = 0; v < NVEC; ++v) {
             int i = v * BLOCK + tid;

@@ -394,6 +394,7 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
     // kernel first, and the epoch restarts.
     const bool fresh = C > 1 && plan->clean_rows < n_rows;
     cp.fresh = fresh ? 1 : 0;
+    cp.vec = (labels != nullptr && aligned16(labels) && (mask == nullptr || aligned16(mask))) ? 1 : 0;
     cp.fill = chunk_words;
     cp.fill_words = C > 1 ? n_rows * C * XWORDS : 0;
     hipError_t e = launch_count(cp, stream);

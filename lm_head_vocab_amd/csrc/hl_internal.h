@@ -119,6 +119,7 @@ struct CountParams {
     int fresh;
     uint64_t* fill;
     int64_t fill_words;
+    int vec;   // labels (and mask, if any) 16-byte aligned: the tiled load path
 };
 
 constexpr int kReduceBlock = 256;   // rows per reduction workgroup

@@ -402,6 +402,41 @@ def test_edge_cases(dtype):
     _check_small(spec, inp, dtype)
 
 
+@pytest.mark.parametrize("N", [15, 16, 16383, 16384, 16401, 40000])
+@pytest.mark.parametrize("layout", ["aligned", "offset_views", "no_mask"])
+def test_valid_row_count_paths(N, layout):
+    """The valid-row and bad-label counts (tiled 16-byte loads when labels and
+    mask are 16-byte aligned, one row at a time otherwise; ragged last tiles)
+    against the oracle's row validity, with the CE mean as a cross-check."""
+    V = 37
+    spec = spec_from(V, CE, dict(ce=1.0))
+    g = torch.Generator().manual_seed(N)
+    y = torch.randint(0, V, (N + 3,), generator=g, dtype=torch.int64)
+    y[torch.rand(N + 3, generator=g) < 0.1] = -100
+    bad = torch.rand(N + 3, generator=g) < 0.05
+    y[bad] = torch.where(torch.rand(N + 3, generator=g)[bad] < 0.5, V + 7, -5)
+    m = (torch.rand(N + 3, generator=g) >= 0.2).to(torch.uint8)
+    x = torch.randn(N, V, generator=g).to(torch.bfloat16)
+    if layout == "offset_views":          # 8-byte (labels) / 1-byte (mask) aligned views
+        yv, mv = y.to(DEV)[1:N + 1], m.to(DEV)[3:N + 3]
+        y_c, m_c = y[1:N + 1], m[3:N + 3]
+    else:
+        yv, mv = y[:N].to(DEV), m[:N].to(DEV)
+        y_c, m_c = y[:N], m[:N]
+    if layout == "no_mask":
+        mv, m_c = None, None
+    plan = make_plan(spec, torch.bfloat16)
+    say(f"[gpu] count N={N} layout={layout}")
+    sc = plan(x.to(DEV), labels=yv, mask=mv).cpu().double().numpy()
+    torch.cuda.synchronize()
+    valid, bad_rows = oracle.row_validity(N, V, y_c.numpy(), None if m_c is None else m_c.numpy())
+    assert sc[SLOT["N_VALID"]] == valid.sum()
+    assert sc[SLOT["N_BADLABEL"]] == bad_rows.sum()
+    ref = oracle.forward_backward(spec, x.double().numpy(), y_c.numpy(), None if m_c is None else m_c.numpy(),
+                                  want_grad=False)[0]
+    assert abs(sc[SLOT["CE"]] - ref[SLOT["CE"]]) <= 1e-4 * abs(ref[SLOT["CE"]])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_zero_weight_keeps_scalars_and_drops_gradient_term(dtype):
     spec, inp = _small(dtype, "all_rkl", 17, 1500, seed=21)
