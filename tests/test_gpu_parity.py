@@ -173,6 +173,19 @@ def test_split_vocab_variant(dtype, combo, chunks):
         _check_small(spec, inp, dtype, chunks=chunks)
 
 
+@pytest.mark.parametrize("chunks", [2, 4, 8])
+@pytest.mark.parametrize("V", [3, 13, 20, 41])
+@pytest.mark.parametrize("combo", ["ce_fkl", "all_rkl", "all_fdce_h"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_vocab_short_rows(dtype, combo, V, chunks):
+    """More chunks than 16-byte body vectors: some chunks of a row own no
+    vector at all (their loads point at the workspace and every value is
+    discarded), head and tail elements sit with chunk 0, and every row still
+    merges all of its chunks."""
+    spec, inp = _small(dtype, combo, 9, V, seed=V * 10 + chunks, mask_frac=0.2, softcap=6.0, scale=0.9)
+    _check_small(spec, inp, dtype, chunks=chunks)
+
+
 @pytest.mark.parametrize("variant", [(2, 512), (4, 512), (3, 1024), (1, 1024), (6, 256)])
 @pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "grpo_z_ent", "ce_fkl"])
 def test_forced_variants(combo, variant):
