@@ -173,7 +173,16 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
 #pragma unroll
     for (int c = 0; c < NCOL; ++c) v[c] = 0.0;
     if (r < p.n_rows) {
-        const float* rec = p.row_rec + r * REC;
+        // every input of the row first, in one round of loads (a masked row's
+        // record is all zeros), then the arithmetic
+        const float* recp = p.row_rec + r * REC;
+        float rec[REC];
+#pragma unroll
+        for (int c = 0; c < REC; ++c) rec[c] = recp[c];
+        const bool grpo_in = (f & F_GRPO) && p.labels != nullptr;
+        const float adv_r = grpo_in ? p.advantages[r] : 0.f;
+        const float old_r = grpo_in ? p.old_logprobs[r] : 0.f;
+        const int64_t sid = (f & F_GSPO) ? (int64_t)p.seg_of_row[r] : -1;
         if (rec[R_VALID] != 0.f) {
             const double Z = rec[R_Z];
             const double l2Z = log2(Z);
@@ -205,8 +214,8 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
                 v[RC_CE] = lse - sy;
                 v[RC_LOGP] = sy - lse;
                 if (f & F_GRPO) {
-                    const double adv = p.advantages[r];
-                    const double d = v[RC_LOGP] - (double)p.old_logprobs[r];
+                    const double adv = adv_r;
+                    const double d = v[RC_LOGP] - (double)old_r;
                     const double ratio = exp(d);
                     const double eps = p.eps;
                     const double rc = ratio < 1.0 - eps ? 1.0 - eps : (ratio > 1.0 + eps ? 1.0 + eps : ratio);
@@ -220,7 +229,6 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
             }
             if (f & F_GSPO) {
                 // per-token view of the token's segment
-                const int64_t sid = p.seg_of_row[r];
                 const bool in = sid >= 0 && sid < p.n_segments;
                 const double* sr = p.seg_rec + (in ? sid : 0) * SEGREC;
                 const double qnan = __builtin_nan("");
