@@ -177,6 +177,16 @@ def test_gspo_split_vocab_forward(combo, chunks):
     _check(spec, inp, "bf16", chunks=chunks)
 
 
+@pytest.mark.parametrize("chunks", [4, 8])
+@pytest.mark.parametrize("V", [13, 41])
+@pytest.mark.parametrize("combo", ["gspo_z_ent", "all_gspo_rkl", "ce_gspo_fdce"])
+def test_gspo_split_vocab_short_rows(combo, V, chunks):
+    """Load mode on rows with more chunks than 16-byte body vectors (empty
+    chunks, head and tail on chunk 0), with and without a teacher."""
+    spec, inp = _case("bf16", combo, 14, V, seed=V + chunks, mask_frac=0.2)
+    _check(spec, inp, "bf16", chunks=chunks)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_gspo_one_token_segments_match_grpo(dtype):
     """With one token per segment the sequence ratio is the token ratio: GSPO
