@@ -50,7 +50,7 @@ __global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
         for (int64_t r = threadIdx.x; r < p.n_rows; r += 1024) {
             bool valid, bad;
             int64_t y;
-            row_status(p.labels, p.mask, r, p.V, valid, bad, y);
+            row_status(p.labels, p.mask, r, p.V, p.ctrl, valid, bad, y);
             nv += valid;
             nb += bad;
         }

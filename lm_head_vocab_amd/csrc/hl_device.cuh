@@ -334,18 +334,23 @@ __device__ __forceinline__ Rec rec_reduce16(Rec r, float beta) {
 // Row validity (shared by the count and fused kernels): masked when the mask
 // byte is 0, the label is -100, or the label is outside [0, V).
 // ---------------------------------------------------------------------------
+// Both the mask byte and the label are loaded, without a branch, before
+// either is used (a missing input reads the 8-byte-aligned word at `spare`,
+// any readable device memory, and its value is ignored), so the row's status
+// costs one memory latency, not two.
 __device__ __forceinline__ void row_status(const int64_t* labels, const uint8_t* mask, int64_t row,
-                                           int64_t V, bool& valid, bool& bad, int64_t& y) {
-    const bool unmasked = (mask == nullptr) || (mask[row] != 0);
-    valid = unmasked;
-    bad = false;
-    y = -1;
-    if (labels != nullptr) {
-        y = labels[row];
-        const bool in_range = (y >= 0) && (y < V);
-        valid = unmasked && in_range;
-        bad = unmasked && !in_range && (y != -100);
-    }
+                                           int64_t V, const void* spare, bool& valid, bool& bad,
+                                           int64_t& y) {
+    const uint8_t* mp = mask != nullptr ? mask + row : static_cast<const uint8_t*>(spare);
+    const int64_t* lp = labels != nullptr ? labels + row : static_cast<const int64_t*>(spare);
+    const uint32_t mk = *mp;
+    const int64_t yl = *lp;
+    const bool has_l = labels != nullptr;
+    const bool unmasked = (mask == nullptr) || (mk != 0u);
+    y = has_l ? yl : -1;
+    const bool in_range = !has_l || ((y >= 0) && (y < V));
+    valid = unmasked && in_range;
+    bad = unmasked && !in_range && (y != -100);
 }
 
 // ---------------------------------------------------------------------------
@@ -540,7 +545,7 @@ void fused_kernel(const FusedParams p) {
 
     bool valid, bad;
     int64_t y;
-    row_status(p.labels, p.mask, row, p.V, valid, bad, y);
+    row_status(p.labels, p.mask, row, p.V, p.ctrl, valid, bad, y);
 
     // Row geometry: an unaligned head (< VEC elements), full 16-byte body
     // vectors, a tail (< VEC elements). Head and tail belong to chunk 0.
