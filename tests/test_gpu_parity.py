@@ -450,6 +450,49 @@ def test_valid_row_count_paths(N, layout):
     assert abs(sc[SLOT["CE"]] - ref[SLOT["CE"]]) <= 1e-4 * abs(ref[SLOT["CE"]])
 
 
+@pytest.mark.parametrize("chunks", [0, 3])
+@pytest.mark.parametrize("combo", ["ce_z", "all_rkl"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nonfinite_logits(dtype, combo, chunks):
+    """NaN and Inf inputs propagate without sanitizing: a masked row that holds
+    them changes nothing (its gradient row is +0.0, the scalars match the
+    oracle on the other rows); a valid row with a NaN makes its own gradient
+    row and the means of its per-row values NaN and leaves every other row's
+    gradient as the oracle computes it."""
+    N, V = 9, 3001
+    spec, inp = _small(dtype, combo, N, V, seed=91 + chunks, ignore_frac=0.0, mask_frac=0.0)
+    x = inp["logits"].clone()
+    x[2, 5] = float("nan")
+    x[2, 700] = float("inf")
+    x[2, 2000] = float("-inf")
+    inp["logits"] = x
+    if inp.get("teacher") is not None:
+        inp["teacher"][2, 9] = float("nan")
+    labels = inp["labels"].clone()
+    labels[2] = -100                     # row 2 masked through its label
+    inp["labels"] = labels
+    if spec.has(GRPO):
+        inp["old_logprobs"] = oracle_old_logprobs(spec, x.nan_to_num(0.0), labels, inp["old_noise"])
+    # masked non-finite row: parity everywhere, +0.0 gradient on that row
+    _check_small(spec, inp, dtype, chunks=chunks)
+
+    # the same NaN in a valid row
+    labels2 = labels.clone()
+    labels2[2] = 11
+    inp2 = dict(inp, labels=labels2)
+    plan = make_plan(spec, TDT[dtype], chunks)
+    say(f"[gpu] non-finite valid row {dtype} {combo} {plan.describe()}")
+    sc, g = run_hip(plan, _to_dev(inp2), "overwrite")
+    _, ref_g, _ = run_oracle(spec, inp2)
+    assert np.isnan(sc[SLOT["CE"]]) and np.isnan(sc[SLOT["TOTAL"]])
+    assert sc[SLOT["N_VALID"]] == N
+    gk = to_np(g.detach().cpu())
+    assert np.isnan(gk[2]).all()
+    keep = np.ones(N, dtype=bool)
+    keep[2] = False
+    grad_check(g.detach().cpu()[torch.from_numpy(keep)], ref_g[keep], dtype, labels=to_np(labels2)[keep])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_zero_weight_keeps_scalars_and_drops_gradient_term(dtype):
     spec, inp = _small(dtype, "all_rkl", 17, 1500, seed=21)
