@@ -519,6 +519,13 @@ void fused_kernel(const FusedParams p) {
     __shared__ float s_xw[kMaxChunks * XWORDS];
     __shared__ float s_row[8];
     __shared__ float s_lrec[REC];
+    // Accumulate mode reads the existing gradient in pass 2. Loaded slot by
+    // slot next to the stores, every load would wait for the stores before
+    // it as well (they share one counter); teacher instances whose slots fit
+    // in 72 KiB of LDS stage the whole old slice there with direct-to-LDS
+    // loads issued before the first store, one latency per workgroup.
+    constexpr bool STAGE_OLD = TMODE != TM_NONE && (size_t)NVEC * BLOCK * 16 <= 73728;
+    __shared__ u32x4 s_old[STAGE_OLD ? NVEC : 1][STAGE_OLD ? BLOCK : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -904,6 +911,21 @@ void fused_kernel(const FusedParams p) {
     };
     const float beta = kf.beta;
 
+    if (STAGE_OLD && p.accumulate && nv > 0) {
+        // slots past the slice re-read its last vector (in bounds, unused)
+        const char* gc = reinterpret_cast<const char*>(gv);
+#pragma unroll
+        for (int v = 0; v < NVEC; ++v) {
+            int i = v * BLOCK + tid;
+            i = i < nv - 1 ? i : nv - 1;
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(gc + (int64_t)i * 16),
+                                             (__attribute__((address_space(3))) void*)&s_old[v][wave * 64],
+                                             16, 0, 2);
+        }
+        // wait here, once, for the staged slice (no store is outstanding yet)
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unconstrained
+    }
+
     // label position relative to this chunk's body vectors (-1: not here)
     int yv = -1;
     int ly = 0;
@@ -926,7 +948,7 @@ void fused_kernel(const FusedParams p) {
                         g[e] = grad_elem(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, beta);
             }
             if (p.accumulate) {
-                const u32x4 old = ld_stream(gv + v * BLOCK + tid);
+                const u32x4 old = STAGE_OLD ? s_old[v][tid] : ld_stream(gv + v * BLOCK + tid);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) g[e] = T::get(old, e) + g[e];
             }

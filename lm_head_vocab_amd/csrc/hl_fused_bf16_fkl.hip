@@ -14,6 +14,7 @@ FusedLauncher get_fused_bf16_fkl(int block, int nvec, bool softcap) {
     HL_FUSED_CASE(hl::BF16T, 1024, 10, hl::TM_FKL)
     HL_FUSED_CASE(hl::BF16T, 512, 6, hl::TM_FKL)
     HL_FUSED_CASE(hl::BF16T, 512, 8, hl::TM_FKL)
+    HL_FUSED_CASE(hl::BF16T, 512, 9, hl::TM_FKL)
     HL_FUSED_CASE(hl::BF16T, 512, 10, hl::TM_FKL)
     return nullptr;
 }

@@ -14,6 +14,7 @@ FusedLauncher get_fused_f32_fdceh(int block, int nvec, bool softcap) {
     HL_FUSED_CASE(hl::F32T, 1024, 10, hl::TM_FDCE_H)
     HL_FUSED_CASE(hl::F32T, 512, 6, hl::TM_FDCE_H)
     HL_FUSED_CASE(hl::F32T, 512, 8, hl::TM_FDCE_H)
+    HL_FUSED_CASE(hl::F32T, 512, 9, hl::TM_FDCE_H)
     HL_FUSED_CASE(hl::F32T, 512, 10, hl::TM_FDCE_H)
     return nullptr;
 }

@@ -118,7 +118,7 @@ Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C, int block = 0) {
     }
     if (block == kMidBlock) {
         const int* set = tmode == TM_NONE ? kMidNvecStudent : kMidNvecTeacher;
-        const int n_set = tmode == TM_NONE ? 4 : 3;
+        const int n_set = 4;
         const int64_t need = (per + kMidBlock - 1) / kMidBlock;
         if (need > set[n_set - 1]) return g;
         return Geometry{C, kMidBlock, round_up_to(set, n_set, (int)need)};

@@ -196,7 +196,7 @@ constexpr int kMidBlock = 512;
 constexpr int kLargeBlock = 1024;
 constexpr int kSmallNvec[] = {1, 2, 4};
 constexpr int kMidNvecStudent[] = {10, 12, 16, 20};
-constexpr int kMidNvecTeacher[] = {6, 8, 10};
+constexpr int kMidNvecTeacher[] = {6, 8, 9, 10};
 constexpr int kLargeNvecStudent[] = {2, 4, 6, 8, 10, 12, 14, 16, 18, 20};
 constexpr int kLargeNvecTeacher[] = {2, 4, 6, 8, 10};
 
