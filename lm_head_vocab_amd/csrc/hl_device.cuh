@@ -319,14 +319,16 @@ __device__ __forceinline__ Rec rec_dpp_step(const Rec& a, float beta) {
     return rec_merge<TMODE>(a, b, beta);
 }
 
-// Merge the records held by lanes 0..15 of every 16-lane row; all lanes end
-// with the same result.
+// Merge the records held by lanes 0..n-1 of every 16-lane row (lanes n..15
+// hold empty records); all lanes end with the same result. A step whose
+// partners are all empty is skipped: merging with an empty record returns
+// the other one unchanged, so the result is the same for any n.
 template <int TMODE>
-__device__ __forceinline__ Rec rec_reduce16(Rec r, float beta) {
-    r = rec_dpp_step<DPP_XOR1, TMODE>(r, beta);
-    r = rec_dpp_step<DPP_XOR2, TMODE>(r, beta);
-    r = rec_dpp_step<DPP_HALF_MIRROR, TMODE>(r, beta);
-    r = rec_dpp_step<DPP_MIRROR, TMODE>(r, beta);
+__device__ __forceinline__ Rec rec_reduce16(Rec r, float beta, int n) {
+    if (n > 1) r = rec_dpp_step<DPP_XOR1, TMODE>(r, beta);
+    if (n > 2) r = rec_dpp_step<DPP_XOR2, TMODE>(r, beta);
+    if (n > 4) r = rec_dpp_step<DPP_HALF_MIRROR, TMODE>(r, beta);
+    if (n > 8) r = rec_dpp_step<DPP_MIRROR, TMODE>(r, beta);
     return r;
 }
 
@@ -820,7 +822,7 @@ void fused_kernel(const FusedParams p) {
                 }
                 if (wr.Z == 0.f) wr = rec_empty();
             }
-            wr = rec_reduce16<TMODE>(wr, p.beta);
+            wr = rec_reduce16<TMODE>(wr, p.beta, NW);
         }
         if (p.chunks > 1) {
             // statistics this mode exchanges: M, Z, S (+ Mt, Zt, SX (+ St) (+ Zs)),
@@ -867,7 +869,7 @@ void fused_kernel(const FusedParams p) {
                 }
                 if (cr.Z == 0.f) cr = rec_empty();
             }
-            wr = rec_reduce16<TMODE>(cr, p.beta);
+            wr = rec_reduce16<TMODE>(cr, p.beta, p.chunks);
         }
         if (lane == 0) {
             s_fin[0] = wr.M; s_fin[1] = wr.Z; s_fin[2] = wr.S;
