@@ -198,7 +198,7 @@ __device__ __forceinline__ float cap_r(float x, float kc2) {
 
 // ---------------------------------------------------------------------------
 // Wave64 reductions. Within a row of 16 lanes: DPP quad_perm (xor 1, xor 2),
-// row_half_mirror, row_mirror; across rows: lane permutes. Every lane ends
+// row_half_mirror, row_mirror; across rows: permlane swaps. Every lane ends
 // with the same value, combined in the same pairing order.
 // ---------------------------------------------------------------------------
 template <int CTRL>
@@ -210,8 +210,21 @@ constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;  // row_half_mirror
 constexpr int DPP_MIRROR = 0x140;       // row_mirror
 
-__device__ __forceinline__ float xor_lanes(float v, int mask) {
-    return __shfl_xor(v, mask, 64);
+// Across the four 16-lane rows: v_permlane16_swap exchanges odd rows of one
+// copy with even rows of the other, and v_permlane32_swap the two 32-lane
+// halves, so each lane receives its own value and its partner's (row r and
+// r ^ 1, resp. half h and h ^ 1) without an LDS round trip; combining the pair
+// gives every lane the same bits (the combines are commutative).
+struct LanePair {
+    float a, b;
+};
+__device__ __forceinline__ LanePair pair16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return LanePair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair pair32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return LanePair{__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -219,9 +232,10 @@ __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp<DPP_XOR2>(v));
     v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
     v = fmaxf(v, dpp<DPP_MIRROR>(v));
-    v = fmaxf(v, xor_lanes(v, 16));
-    v = fmaxf(v, xor_lanes(v, 32));
-    return v;
+    LanePair q = pair16(v);
+    v = fmaxf(q.a, q.b);
+    q = pair32(v);
+    return fmaxf(q.a, q.b);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -229,9 +243,10 @@ __device__ __forceinline__ float wave_sum(float v) {
     v = __fadd_rn(v, dpp<DPP_XOR2>(v));
     v = __fadd_rn(v, dpp<DPP_HALF_MIRROR>(v));
     v = __fadd_rn(v, dpp<DPP_MIRROR>(v));
-    v = __fadd_rn(v, xor_lanes(v, 16));
-    v = __fadd_rn(v, xor_lanes(v, 32));
-    return v;
+    LanePair q = pair16(v);
+    v = __fadd_rn(q.a, q.b);
+    q = pair32(v);
+    return __fadd_rn(q.a, q.b);
 }
 
 // ---------------------------------------------------------------------------
