@@ -170,28 +170,34 @@ hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t byte
  * Approach; #558 Design).
  *   n_rows          number of tokens N >= 0 (0: scalars are all written 0).
  *   logits          device [N, V] row-major contiguous, plan dtype, base
- *                   16-byte aligned. Raw student logits.
+ *                   aligned to the element size. Raw student logits.
  *   labels          device int64[N] or NULL; -100 = ignored token. Needed by
  *                   HL_CE, HL_GRPO and HL_GSPO. An unmasked label outside [0, V) that
  *                   is not -100 masks the row and counts in N_BADLABEL.
  *   mask            device uint8[N] or NULL; 0 = masked token. Masking
  *                   applies to every loss and metric.
- *   teacher_logits  device [N, V], plan dtype, 16-byte aligned base, or
+ *   teacher_logits  device [N, V], plan dtype, element-aligned base, or
  *                   NULL; needed by HL_FKL / HL_RKL / HL_FDCE.
  *   old_logprobs    device float[N] or NULL; needed by HL_GRPO.
  *   advantages      device float[N] (per token) or NULL; needed by HL_GRPO.
- *   grad_out        device [N, V], plan dtype, 16-byte aligned base, or NULL
+ *   grad_out        device [N, V], plan dtype, element-aligned base, or NULL
  *                   (NULL: metrics only, no gradient written). Overwrite
  *                   mode writes every element (masked rows +0.0);
  *                   HL_ACCUMULATE adds in fp32 and rounds once, and leaves
  *                   masked rows untouched.
  *   scalars_out     device float[HL_NUM_SCALARS], must not be NULL.
  *   stream          HIP stream for all work of the call.
+ * Alignment: rows are split into 16-byte vectors (plus a head and a tail of
+ * single elements when V * element size is not a multiple of 16); this needs
+ * the logits, teacher and gradient bases to agree modulo 16 bytes (as 16-byte
+ * aligned allocations, PyTorch's among them, do). When they do not, a row-wise
+ * kernel with element loads and stores computes the same results, more
+ * slowly; it is never an error.
  * Gradient with respect to the raw logits of a valid row:
  *   grad_scale / n * ds/dx * sum_k weight_k * dloss_k/ds
  * with n the number of valid rows (or weights.divisor when > 0).
  * Errors: HL_ERR_INVALID_ARG (NULL plan, n_rows < 0, NULL logits or
- * scalars_out, misaligned base pointer), HL_ERR_MISSING_INPUT (see above),
+ * scalars_out, a base not aligned to the element size), HL_ERR_MISSING_INPUT (see above),
  * HL_ERR_WORKSPACE (a workspace that is too small was set by the caller),
  * HL_ERR_HIP. Allocates device memory only when no workspace was set (first
  * call, or a larger n_rows than before); the allocation is kept by the plan.

@@ -506,6 +506,38 @@ __device__ __forceinline__ float grad_one(const FusedParams& p, const Coefs& k, 
     return SOFTCAP ? cf * g : g;
 }
 
+// One element's terms of the pass-1 sums, in the log2 domain, relative to
+// the student shift M and the teacher shift Mt: Z += 2^a, S += 2^a a (only
+// when WS: the entropy sum), Zt += 2^u, the distillation cross sum SX (and
+// St = sum 2^u u, Zs = sum 2^(a / tau) in the modes that need them), with
+// a = s log2(e) - M the student's and u = t log2(e) / tau - Mt the teacher's
+// offset.
+template <int TMODE, bool SOFTCAP, bool WS>
+__device__ __forceinline__ void stat_term(const FusedParams& p, float M, float Mt, float x, float t, float& z,
+                                          float& s, float& zt, float& sx, float& st, float& zs) {
+    const float a = SOFTCAP ? fmaf(cap_r(x, p.kc2), -2.0f * p.cl, p.cl - M) : fmaf(x, p.K1, -M);
+    const float ex = fast_exp2(a);
+    z += ex;
+    if (WS) s = fmaf(ex, a, s);
+    if (TMODE != TM_NONE) {
+        const float u = fmaf(t, p.K2, -Mt);
+        const float et = fast_exp2(u);
+        zt += et;
+        if (is_hinton(TMODE)) {
+            const float ad = a * p.beta;          // tempered student, shift M beta
+            const float ed = fast_exp2(ad);
+            zs += ed;
+            if (fkl_like(TMODE)) sx = fmaf(et, u - ad, sx);
+            else sx = fmaf(ed, ad - u, sx);
+        } else if (fkl_like(TMODE)) {
+            sx = fmaf(et, u - a, sx);
+        } else {
+            sx = fmaf(ex, a - u, sx);
+        }
+        if (has_st(TMODE)) st = fmaf(et, u, st);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // fused_kernel
 // ---------------------------------------------------------------------------
@@ -575,7 +607,7 @@ void fused_kernel(const FusedParams p) {
     // vectors, a tail (< VEC elements). Head and tail belong to chunk 0.
     const int64_t V = p.V;
     const int64_t rowoff = row * V;
-    const int mis = (int)((rowoff * ES) & 15);
+    const int mis = (int)((reinterpret_cast<uintptr_t>(p.logits) + (uint64_t)rowoff * ES) & 15);
     int head = mis ? (16 - mis) / ES : 0;
     if (head > V) head = (int)V;
     const int64_t nbv = (V - head) / VEC;
@@ -707,28 +739,7 @@ void fused_kernel(const FusedParams p) {
     // one term of every sum; the entropy term only when WS
     auto term = [&](auto want_s_tag, float x, float t, float& z, float& s, float& zt, float& sx, float& st,
                     float& zs) {
-        constexpr bool WS = decltype(want_s_tag)::value;
-        const float a = SOFTCAP ? fmaf(cap_r(x, p.kc2), -2.0f * p.cl, p.cl - M) : fmaf(x, p.K1, -M);
-        const float ex = fast_exp2(a);
-        z += ex;
-        if (WS) s = fmaf(ex, a, s);
-        if (TMODE != TM_NONE) {
-            const float u = fmaf(t, p.K2, -Mt);
-            const float et = fast_exp2(u);
-            zt += et;
-            if (is_hinton(TMODE)) {
-                const float ad = a * p.beta;          // tempered student, shift M beta
-                const float ed = fast_exp2(ad);
-                zs += ed;
-                if (fkl_like(TMODE)) sx = fmaf(et, u - ad, sx);
-                else sx = fmaf(ed, ad - u, sx);
-            } else if (fkl_like(TMODE)) {
-                sx = fmaf(et, u - a, sx);
-            } else {
-                sx = fmaf(ex, a - u, sx);
-            }
-            if (has_st(TMODE)) st = fmaf(et, u, st);
-        }
+        stat_term<TMODE, SOFTCAP, decltype(want_s_tag)::value>(p, M, Mt, x, t, z, s, zt, sx, st, zs);
     };
     auto accumulate = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st, float& zs) {
         term(std::true_type(), x, t, z, s, zt, sx, st, zs);
@@ -986,7 +997,178 @@ hipError_t launch_fused(const FusedParams& p, dim3 grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// rowwise_kernel: the same losses, row records and gradient for inputs whose
+// base addresses differ modulo 16 bytes, where no split of a row into 16-byte
+// vectors is aligned in all of logits, teacher and gradient at once. One
+// 256-thread workgroup per row with element loads and stores; the row is read
+// three times (exact maxima, sums, gradient), the later reads mostly from the
+// caches. The statistics are taken relative to the exact row maxima, merged
+// over the waves in wave order; the coefficients and the per-element gradient
+// are the fused kernel's.
+// ---------------------------------------------------------------------------
+constexpr int kRowwiseBlock = 256;
+
+template <typename T, int TMODE, bool SOFTCAP>
+__global__ __launch_bounds__(kRowwiseBlock) void rowwise_kernel(const FusedParams p) {
+    constexpr int NW = kRowwiseBlock / 64;
+    constexpr int ES = T::ESIZE;
+    __shared__ float s_m[NW][2];
+    __shared__ float s_rec[NW][8];
+    __shared__ float s_fin[8];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t row = blockIdx.x;
+    const int64_t V = p.V;
+
+    bool valid, bad;
+    int64_t y;
+    row_status(p.labels, p.mask, row, V, p.ctrl, valid, bad, y);
+    const char* xrow = static_cast<const char*>(p.logits) + row * V * ES;
+    const char* trow = TMODE != TM_NONE ? static_cast<const char*>(p.teacher) + row * V * ES : nullptr;
+    char* grow = p.grad != nullptr ? static_cast<char*>(p.grad) + row * V * ES : nullptr;
+    if (!valid) {
+        if (grow != nullptr && !p.accumulate)
+            for (int64_t j = tid; j < V; j += kRowwiseBlock) T::store1(grow, j, 0.0f);
+        if (tid < REC) p.row_rec[row * REC + tid] = 0.0f;
+        return;
+    }
+    const float xy = y >= 0 ? T::load1(xrow, y) : 0.f;
+    const float old = p.old_logprobs != nullptr ? p.old_logprobs[row] : 0.f;
+    const float adv = p.advantages != nullptr ? p.advantages[row] : 0.f;
+
+    Rec r;
+    if (p.load_mode) {
+        const float* rec = p.row_rec + row * REC;
+        r.M = rec[R_M]; r.Z = rec[R_Z]; r.S = rec[R_S];
+        r.Mt = rec[R_MT]; r.Zt = rec[R_ZT]; r.SX = rec[R_SX]; r.St = rec[R_ST]; r.Zs = rec[R_ZS];
+    } else {
+        float mx = kNegInf, mt = kNegInf;
+        for (int64_t j = tid; j < V; j += kRowwiseBlock) {
+            mx = fmaxf(mx, T::load1(xrow, j));
+            if (TMODE != TM_NONE) mt = fmaxf(mt, T::load1(trow, j));
+        }
+        mx = wave_max(mx);
+        if (TMODE != TM_NONE) mt = wave_max(mt);
+        if (lane == 0) {
+            s_m[wave][0] = mx;
+            s_m[wave][1] = mt;
+        }
+        __syncthreads();
+        mx = s_m[0][0];
+        mt = s_m[0][1];
+        for (int w = 1; w < NW; ++w) {
+            mx = fmaxf(mx, s_m[w][0]);
+            mt = fmaxf(mt, s_m[w][1]);
+        }
+        const float M = SOFTCAP ? (p.cap * hl_tanh(mx * p.kc)) * kLog2e : mx * p.K1;
+        const float Mt = TMODE != TM_NONE ? mt * p.K2 : 0.f;
+        float z = 0.f, sv = 0.f, zt = 0.f, sx = 0.f, st = 0.f, zs = 0.f;
+        for (int64_t j = tid; j < V; j += kRowwiseBlock) {
+            const float x = T::load1(xrow, j);
+            const float t = TMODE != TM_NONE ? T::load1(trow, j) : 0.f;
+            stat_term<TMODE, SOFTCAP, true>(p, M, Mt, x, t, z, sv, zt, sx, st, zs);
+        }
+        z = wave_sum(z);
+        sv = wave_sum(sv);
+        if (TMODE != TM_NONE) {
+            zt = wave_sum(zt);
+            sx = wave_sum(sx);
+        }
+        if (has_st(TMODE)) st = wave_sum(st);
+        if (is_hinton(TMODE)) zs = wave_sum(zs);
+        if (lane == 0) {
+            s_rec[wave][0] = M; s_rec[wave][1] = z; s_rec[wave][2] = sv; s_rec[wave][3] = Mt;
+            s_rec[wave][4] = zt; s_rec[wave][5] = sx; s_rec[wave][6] = st; s_rec[wave][7] = zs;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            Rec acc = rec_empty();
+            for (int w = 0; w < NW; ++w) {
+                Rec b;
+                b.M = s_rec[w][0]; b.Z = s_rec[w][1]; b.S = s_rec[w][2];
+                if (TMODE != TM_NONE) {
+                    b.Mt = s_rec[w][3]; b.Zt = s_rec[w][4]; b.SX = s_rec[w][5];
+                    b.St = has_st(TMODE) ? s_rec[w][6] : 0.f;
+                    b.Zs = is_hinton(TMODE) ? s_rec[w][7] : 0.f;
+                } else {
+                    b.Mt = 0.f; b.Zt = 0.f; b.SX = 0.f; b.St = 0.f; b.Zs = 0.f;
+                }
+                if (b.Z == 0.f) b = rec_empty();
+                acc = rec_merge<TMODE>(acc, b, p.beta);
+            }
+            s_fin[0] = acc.M; s_fin[1] = acc.Z; s_fin[2] = acc.S; s_fin[3] = acc.Mt;
+            s_fin[4] = acc.Zt; s_fin[5] = acc.SX; s_fin[6] = acc.St; s_fin[7] = acc.Zs;
+            float* out = p.row_rec + row * REC;
+            out[R_M] = acc.M; out[R_Z] = acc.Z; out[R_S] = acc.S;
+            out[R_MT] = acc.Mt; out[R_ZT] = acc.Zt; out[R_SX] = acc.SX; out[R_ST] = acc.St;
+            out[R_ZS] = acc.Zs;
+            out[R_XY] = xy;
+            out[R_VALID] = 1.0f;
+        }
+        __syncthreads();
+        r.M = s_fin[0]; r.Z = s_fin[1]; r.S = s_fin[2]; r.Mt = s_fin[3];
+        r.Zt = s_fin[4]; r.SX = s_fin[5]; r.St = s_fin[6]; r.Zs = s_fin[7];
+    }
+    if (grow == nullptr) return;
+
+    Coefs kf = row_coefs<TMODE, SOFTCAP>(p, r, y, xy, old, adv);
+    if (p.row_coef != nullptr && p.w_g != 0.f) {
+        // GSPO: the per-token coefficient of the segment step on the label column
+        const uint32_t n_seg = p.ctrl[CTRL_NSEG];
+        const float e = n_seg > 0u ? p.grad_scale * p.k * p.w_g * p.row_coef[row] / (float)n_seg : 0.f;
+        kf.alpha += e;
+        kf.beta += e;
+        if (TMODE == TM_RKL) kf.c0 += e;
+    }
+    if (p.load_mode && p.ctrl[CTRL_ERROR] != 0u) kf.alpha = kf.beta = kf.c0 = __builtin_nanf("");
+    for (int64_t j = tid; j < V; j += kRowwiseBlock) {
+        const float x = T::load1(xrow, j);
+        const float t = TMODE != TM_NONE ? T::load1(trow, j) : 0.f;
+        float g = grad_one<TMODE, SOFTCAP>(p, kf, x, t, j == y ? kf.beta : 0.f);
+        if (p.accumulate) g = T::load1(grow, j) + g;
+        T::store1(grow, j, g);
+    }
+}
+
+template <typename T, int TMODE, bool SOFTCAP>
+hipError_t launch_rowwise(const FusedParams& p, dim3 grid, hipStream_t s) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((rowwise_kernel<T, TMODE, SOFTCAP>), grid, dim3(kRowwiseBlock), 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace hl
+
+// Instance getter of the row-wise kernel for one element type.
+#define HL_ROWWISE_GETTER(NAME, T)                                                         \
+    FusedLauncher NAME(int tmode, bool softcap) {                                          \
+        switch (tmode) {                                                                   \
+            case hl::TM_NONE:                                                              \
+                return softcap ? &hl::launch_rowwise<T, hl::TM_NONE, true>                 \
+                               : &hl::launch_rowwise<T, hl::TM_NONE, false>;               \
+            case hl::TM_FKL:                                                               \
+                return softcap ? &hl::launch_rowwise<T, hl::TM_FKL, true>                  \
+                               : &hl::launch_rowwise<T, hl::TM_FKL, false>;                \
+            case hl::TM_RKL:                                                               \
+                return softcap ? &hl::launch_rowwise<T, hl::TM_RKL, true>                  \
+                               : &hl::launch_rowwise<T, hl::TM_RKL, false>;                \
+            case hl::TM_FDCE:                                                              \
+                return softcap ? &hl::launch_rowwise<T, hl::TM_FDCE, true>                 \
+                               : &hl::launch_rowwise<T, hl::TM_FDCE, false>;               \
+            case hl::TM_FKL_H:                                                             \
+                return softcap ? &hl::launch_rowwise<T, hl::TM_FKL_H, true>                \
+                               : &hl::launch_rowwise<T, hl::TM_FKL_H, false>;              \
+            case hl::TM_RKL_H:                                                             \
+                return softcap ? &hl::launch_rowwise<T, hl::TM_RKL_H, true>                \
+                               : &hl::launch_rowwise<T, hl::TM_RKL_H, false>;              \
+            case hl::TM_FDCE_H:                                                            \
+                return softcap ? &hl::launch_rowwise<T, hl::TM_FDCE_H, true>               \
+                               : &hl::launch_rowwise<T, hl::TM_FDCE_H, false>;             \
+        }                                                                                  \
+        return nullptr;                                                                    \
+    }
 
 // Instantiation helper for the per-(dtype, mode) translation units.
 #define HL_FUSED_CASE(T, BLOCK, NVEC, TMODE)                                 \

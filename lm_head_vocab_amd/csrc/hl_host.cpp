@@ -26,6 +26,7 @@ struct hl_plan_s {
     int forced_block;
     Geometry geo;
     FusedLauncher fused;
+    FusedLauncher rowwise;   // inputs whose base addresses differ modulo 16 bytes
     void* ws;
     size_t ws_bytes;
     bool ws_owned;
@@ -98,6 +99,11 @@ const Getter kGetters[3][7] = {
      get_fused_f16_fklh, get_fused_f16_rklh, get_fused_f16_fdceh},
 };
 
+FusedLauncher lookup_rowwise(hl_dtype dt, int tmode, bool softcap) {
+    return dt == HL_F32 ? get_rowwise_f32(tmode, softcap)
+         : dt == HL_BF16 ? get_rowwise_bf16(tmode, softcap) : get_rowwise_f16(tmode, softcap);
+}
+
 FusedLauncher lookup(hl_dtype dt, int tmode, int block, int nvec, bool softcap) {
     return kGetters[(int)dt][tmode](block, nvec, softcap);
 }
@@ -168,11 +174,15 @@ hl_status choose(hl_plan_s* p) {
         p->geo = g;
     }
     p->fused = lookup(p->dtype, p->tmode, p->geo.block, p->geo.nvec, p->softcap > 0.f);
-    return p->fused ? HL_OK : HL_ERR_UNSUPPORTED;
+    p->rowwise = lookup_rowwise(p->dtype, p->tmode, p->softcap > 0.f);
+    return (p->fused && p->rowwise) ? HL_OK : HL_ERR_UNSUPPORTED;
 }
 
 bool finite(float x) { return std::isfinite(x); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t elem_size(hl_dtype dt) { return dt == HL_F32 ? 4 : 2; }
+bool elem_aligned(const void* p, size_t es) { return (reinterpret_cast<uintptr_t>(p) % es) == 0; }
+uintptr_t mod16(const void* p) { return reinterpret_cast<uintptr_t>(p) & 15u; }
 
 // The workspace layout depends on the variant: a library-owned buffer is
 // released (the next call allocates a zeroed one); a caller's buffer must be
@@ -351,9 +361,10 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
         if ((f & (HL_CE | kPolicyBits)) && labels == nullptr) return HL_ERR_MISSING_INPUT;
         if ((f & kDistillBits) && teacher_logits == nullptr) return HL_ERR_MISSING_INPUT;
         if ((f & kPolicyBits) && (old_logprobs == nullptr || advantages == nullptr)) return HL_ERR_MISSING_INPUT;
-        if (!aligned16(logits)) return HL_ERR_INVALID_ARG;
-        if (plan->tmode != TM_NONE && !aligned16(teacher_logits)) return HL_ERR_INVALID_ARG;
-        if (grad_out != nullptr && !aligned16(grad_out)) return HL_ERR_INVALID_ARG;
+        const size_t es = elem_size(plan->dtype);
+        if (!elem_aligned(logits, es)) return HL_ERR_INVALID_ARG;
+        if (plan->tmode != TM_NONE && !elem_aligned(teacher_logits, es)) return HL_ERR_INVALID_ARG;
+        if (grad_out != nullptr && !elem_aligned(grad_out, es)) return HL_ERR_INVALID_ARG;
         if ((uint64_t)(n_rows + 7) * (uint64_t)plan->geo.chunks > 0x7fffffffull) return HL_ERR_UNSUPPORTED;
     }
 
@@ -441,11 +452,20 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
         fp.grad_scale = plan->w.grad_scale;
         fp.divisor = plan->w.divisor;
         fp.eps = plan->eps;
+        // The fused kernel splits every row at the same 16-byte boundaries in
+        // logits, teacher and gradient, which exist only when the three base
+        // addresses agree modulo 16; otherwise the row-wise kernel runs (one
+        // workgroup per row, element loads and stores).
+        const uintptr_t xa = mod16(logits);
+        const bool rowwise = (plan->tmode != TM_NONE && mod16(teacher_logits) != xa) ||
+                             (grad_out != nullptr && mod16(grad_out) != xa);
+        const FusedLauncher launch = rowwise ? plan->rowwise : plan->fused;
         // split-vocab: 8 XCD groups of rows_per_xcd rows, C workgroups per row
-        const dim3 grid(C > 1 ? (unsigned)(8 * fp.rows_per_xcd * C) : (unsigned)n_rows);
+        const dim3 grid(rowwise ? (unsigned)n_rows
+                        : C > 1 ? (unsigned)(8 * fp.rows_per_xcd * C) : (unsigned)n_rows);
         if (plan->ev_before && (e = hipEventRecord(plan->ev_before, stream)) != hipSuccess)
             return hip_fail("hipEventRecord(before)", e);
-        e = plan->fused(fp, grid, stream);
+        e = launch(fp, grid, stream);
         if (e != hipSuccess) return hip_fail("fused kernel launch", e);
         if (gspo) {
             SeamParams sp;
@@ -470,7 +490,7 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
                 fp.grad = grad_out;
                 fp.row_coef = sp.row_coef;
                 fp.load_mode = 1;
-                e = plan->fused(fp, grid, stream);
+                e = launch(fp, grid, stream);
                 if (e != hipSuccess) return hip_fail("fused kernel launch (load mode)", e);
             }
         }

@@ -185,6 +185,11 @@ FusedLauncher get_fused_bf16_fdceh(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f16_fklh(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f16_rklh(int block, int nvec, bool softcap);
 FusedLauncher get_fused_f16_fdceh(int block, int nvec, bool softcap);
+// Row-wise kernel (inputs whose base addresses differ modulo 16 bytes), by
+// teacher mode, one getter per element type.
+FusedLauncher get_rowwise_f32(int tmode, bool softcap);
+FusedLauncher get_rowwise_bf16(int tmode, bool softcap);
+FusedLauncher get_rowwise_f16(int tmode, bool softcap);
 
 hipError_t launch_count(const CountParams& p, hipStream_t s);  // grid grows when p.fresh
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);

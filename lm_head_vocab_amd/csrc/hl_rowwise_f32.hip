@@ -1,0 +1,8 @@
+// Row-wise kernel instances (every teacher mode, softcap on and off): dtype f32.
+#include "hl_device.cuh"
+
+namespace hl {
+
+HL_ROWWISE_GETTER(get_rowwise_f32, hl::F32T)
+
+}  // namespace hl

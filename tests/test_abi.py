@@ -147,7 +147,8 @@ def test_forward_backward_host_checks_enqueue_nothing():
     st, h = _plan(V=64, flags=hl.CE | hl.GRPO | hl.FKL, w=Weights(1, 0, 1, 1, 1, 0))
     assert st == 0
     fake = VP(4096)           # 16-byte aligned stand-in pointer, never dereferenced
-    mis = VP(4098)
+    mis = VP(4097)            # not aligned to the bf16 element size (a 16-byte misalignment that
+                              # keeps element alignment is valid: it selects the row-wise kernel)
     fb = lib.hl_forward_backward
     assert fb(None, 4, fake, fake, None, fake, fake, fake, fake, fake, None) == hl.HL_ERR_INVALID_ARG
     assert fb(h, -1, fake, fake, None, fake, fake, fake, fake, fake, None) == hl.HL_ERR_INVALID_ARG
