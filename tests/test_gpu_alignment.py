@@ -89,6 +89,10 @@ CASES = [
     ("bf16", "all_fkl", 12, 1000, 0.0, 1.0, False),
     ("bf16", "all_fdce_h", 7, 4099, 0.0, 1.0, False),
     ("f16", "ce_fkl_h", 7, 2053, 0.0, 1.0, False),
+    # degenerate rows and the largest vocabulary of the benchmark configurations
+    ("bf16", "all_rkl", 5, 3, 0.0, 1.0, False),
+    ("f32", "ce_z", 4, 1, 0.0, 1.0, False),
+    ("bf16", "all_rkl", 3, 256000, 30.0, 0.5, True),
 ]
 
 
