@@ -181,7 +181,10 @@ hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t byte
  *   old_logprobs    device float[N] or NULL; needed by HL_GRPO.
  *   advantages      device float[N] (per token) or NULL; needed by HL_GRPO.
  *   grad_out        device [N, V], plan dtype, element-aligned base, or NULL
- *                   (NULL: metrics only, no gradient written). Overwrite
+ *                   (NULL: metrics only, no gradient written; the row
+ *                   statistics then come from a streaming kernel, so the
+ *                   scalars agree with a gradient call's to float rounding,
+ *                   not bit for bit). Overwrite
  *                   mode writes every element (masked rows +0.0);
  *                   HL_ACCUMULATE adds in fp32 and rounds once, and leaves
  *                   masked rows untouched.

@@ -1139,35 +1139,232 @@ hipError_t launch_rowwise(const FusedParams& p, dim3 grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// stream_stats_kernel: the forward-only pass (row statistics and records, no
+// gradient), used when no gradient is requested and for the forward launch
+// of a GSPO call. Nothing of the row is needed after its sums, so instead of
+// holding a register-resident slice per (row, chunk) this kernel gives each
+// row one workgroup that streams it in batches of SU 16-byte vectors per
+// thread and tensor, the next batch's loads in flight while the
+// current one is summed: no chunk exchange, one read of every byte. The sums
+// use the wave's provisional shift (the maximum of its first vectors) with
+// the fused kernel's overflow fallback; records merge over the waves in
+// order. Same record format as the fused kernel.
+// ---------------------------------------------------------------------------
+// Batches of 4 vectors (2 per tensor with a teacher) keep two double-buffered
+// batches within 64 VGPRs, so two 1024-thread workgroups share a CU.
+constexpr int kStreamBlock = 1024;
+
+template <typename T, int TMODE, bool SOFTCAP>
+__global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const FusedParams p) {
+    constexpr int VEC = T::VEC;
+    constexpr int ES = T::ESIZE;
+    constexpr int NW = kStreamBlock / 64;
+    constexpr int SU = TMODE == TM_NONE ? 4 : 2;
+    __shared__ float s_rec[16][8];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t row = blockIdx.x;
+    const int64_t V = p.V;
+
+    bool valid, bad;
+    int64_t y;
+    row_status(p.labels, p.mask, row, V, p.ctrl, valid, bad, y);
+    if (!valid) {
+        if (tid < REC) p.row_rec[row * REC + tid] = 0.0f;
+        return;
+    }
+    // the fused kernel's row geometry (head, 16-byte body vectors, tail)
+    const int64_t rowoff = row * V;
+    const int mis = (int)((reinterpret_cast<uintptr_t>(p.logits) + (uint64_t)rowoff * ES) & 15);
+    int head = mis ? (16 - mis) / ES : 0;
+    if (head > V) head = (int)V;
+    const int64_t nbv = (V - head) / VEC;
+    const int tail = (int)(V - head - nbv * VEC);
+    const bool has_e = tid < head + tail;
+    const int eidx = (tid < head) ? tid : head + (int)nbv * VEC + (tid - head);
+    const char* xrow = static_cast<const char*>(p.logits) + rowoff * ES;
+    const char* trow = static_cast<const char*>(p.teacher) + rowoff * ES;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(xrow + (int64_t)head * ES);
+    const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)head * ES);
+
+    uint32_t xy_b = 0u, xe_b = 0u, te_b = 0u;
+    if (tid == 0 && y >= 0) xy_b = T::raw1(xrow, y);
+    if (has_e) {
+        xe_b = T::raw1(xrow, eidx);
+        if (TMODE != TM_NONE) te_b = T::raw1(trow, eidx);
+    }
+    // batch b of thread tid: vectors (b * SU + u) * BLOCK + tid; loads past
+    // the row re-read its last vector (in bounds, never summed); a row with no
+    // body vector points them at the workspace's row records
+    const bool body = nbv > 0;
+    const u32x4* xb = body ? xv : reinterpret_cast<const u32x4*>(p.row_rec);
+    const u32x4* tb = body ? tv : reinterpret_cast<const u32x4*>(p.row_rec);
+    const int64_t lastv = body ? nbv - 1 : 0;
+    const int64_t nbatch = (nbv + (int64_t)SU * kStreamBlock - 1) / ((int64_t)SU * kStreamBlock);
+    u32x4 xa[SU], ta[TMODE != TM_NONE ? SU : 1];
+    auto load_batch = [&](int64_t b, u32x4* xd, u32x4* td) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            int64_t i = (b * SU + u) * kStreamBlock + tid;
+            i = i < lastv ? i : lastv;
+            xd[u] = ld_stream(xb + i);
+            if (TMODE != TM_NONE) td[u] = ld_stream(tb + i);
+        }
+    };
+    load_batch(0, xa, ta);
+    const float xe = has_e ? T::from_raw(xe_b) : 0.f;
+    const float te = (has_e && TMODE != TM_NONE) ? T::from_raw(te_b) : 0.f;
+
+    // provisional shift: the wave's maximum over its first vectors
+    float mx = kNegInf, mt = kNegInf;
+    if (tid < nbv) {
+        mx = T::vmax(mx, xa[0]);
+        if (TMODE != TM_NONE) mt = T::vmax(mt, ta[0]);
+    }
+    const float mx0 = wave_max(mx);
+    const float mt0 = TMODE != TM_NONE ? wave_max(mt) : 0.f;
+    auto shift_of = [&](float m) -> float {
+        return SOFTCAP ? (p.cap * hl_tanh(m * p.kc)) * kLog2e : m * p.K1;
+    };
+    float M = shift_of(mx0);
+    float Mt = TMODE != TM_NONE ? mt0 * p.K2 : 0.f;
+    const bool early = mx0 != kNegInf && (TMODE == TM_NONE || mt0 != kNegInf);
+    float z = 0.f, sv = 0.f, zt = 0.f, sx = 0.f, st = 0.f, zs = 0.f;
+    if (early) {
+        for (int64_t b = 0; b < nbatch; ++b) {
+            u32x4 xn[SU], tn[TMODE != TM_NONE ? SU : 1];
+            if (b + 1 < nbatch) load_batch(b + 1, xn, tn);
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                if ((b * SU + u) * kStreamBlock + tid < nbv) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        stat_term<TMODE, SOFTCAP, true>(p, M, Mt, T::get(xa[u], e),
+                                                        TMODE != TM_NONE ? T::get(ta[u], e) : 0.f,
+                                                        z, sv, zt, sx, st, zs);
+                }
+            }
+            if (b + 1 < nbatch) {
+#pragma unroll
+                for (int u = 0; u < SU; ++u) {
+                    xa[u] = xn[u];
+                    if (TMODE != TM_NONE) ta[u] = tn[u];
+                }
+            }
+        }
+        if (has_e) stat_term<TMODE, SOFTCAP, true>(p, M, Mt, xe, te, z, sv, zt, sx, st, zs);
+    }
+    auto wave_sums = [&]() {
+        z = wave_sum(z);
+        sv = wave_sum(sv);
+        if (TMODE != TM_NONE) {
+            zt = wave_sum(zt);
+            sx = wave_sum(sx);
+        }
+        if (has_st(TMODE)) st = wave_sum(st);
+        if (is_hinton(TMODE)) zs = wave_sum(zs);
+    };
+    wave_sums();
+    constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
+    if (!early || !(z <= kSumLimit) || (TMODE != TM_NONE && !(zt <= kSumLimit)) ||
+        (is_hinton(TMODE) && !(zs <= kSumLimit))) {
+        // rare: the true maxima of the wave's vectors, then the sums again
+        mx = kNegInf;
+        mt = kNegInf;
+        for (int64_t i = tid; i < nbv; i += kStreamBlock) {
+            mx = T::vmax(mx, xv[i]);
+            if (TMODE != TM_NONE) mt = T::vmax(mt, tv[i]);
+        }
+        if (has_e) {
+            mx = fmaxf(mx, xe);
+            if (TMODE != TM_NONE) mt = fmaxf(mt, te);
+        }
+        M = shift_of(wave_max(mx));
+        if (TMODE != TM_NONE) Mt = wave_max(mt) * p.K2;
+        z = sv = zt = sx = st = zs = 0.f;
+        for (int64_t i = tid; i < nbv; i += kStreamBlock) {
+            const u32x4 w = xv[i];
+            u32x4 wt = {0u, 0u, 0u, 0u};
+            if (TMODE != TM_NONE) wt = tv[i];
+            for (int e = 0; e < VEC; ++e)
+                stat_term<TMODE, SOFTCAP, true>(p, M, Mt, T::get(w, e), TMODE != TM_NONE ? T::get(wt, e) : 0.f,
+                                                z, sv, zt, sx, st, zs);
+        }
+        if (has_e) stat_term<TMODE, SOFTCAP, true>(p, M, Mt, xe, te, z, sv, zt, sx, st, zs);
+        wave_sums();
+    }
+    if (lane == 0) {
+        s_rec[wave][0] = M; s_rec[wave][1] = z; s_rec[wave][2] = sv; s_rec[wave][3] = Mt;
+        s_rec[wave][4] = zt; s_rec[wave][5] = sx; s_rec[wave][6] = st; s_rec[wave][7] = zs;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        Rec wr = rec_empty();
+        const int w = lane & 15;
+        if (w < NW) {
+            wr.M = s_rec[w][0];
+            wr.Z = s_rec[w][1];
+            wr.S = s_rec[w][2];
+            if (TMODE != TM_NONE) {
+                wr.Mt = s_rec[w][3];
+                wr.Zt = s_rec[w][4];
+                wr.SX = s_rec[w][5];
+                if (has_st(TMODE)) wr.St = s_rec[w][6];
+                if (is_hinton(TMODE)) wr.Zs = s_rec[w][7];
+            }
+            if (wr.Z == 0.f) wr = rec_empty();
+        }
+        wr = rec_reduce16<TMODE>(wr, p.beta, NW);
+        if (lane == 0) {
+            float* out = p.row_rec + row * REC;
+            out[R_M] = wr.M; out[R_Z] = wr.Z; out[R_S] = wr.S;
+            out[R_MT] = wr.Mt; out[R_ZT] = wr.Zt; out[R_SX] = wr.SX; out[R_ST] = wr.St;
+            out[R_ZS] = wr.Zs;
+            out[R_XY] = T::from_raw(xy_b);
+            out[R_VALID] = 1.0f;
+        }
+    }
+}
+
+template <typename T, int TMODE, bool SOFTCAP>
+hipError_t launch_stream_stats(const FusedParams& p, dim3 grid, hipStream_t s) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((stream_stats_kernel<T, TMODE, SOFTCAP>), grid, dim3(kStreamBlock), 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace hl
 
-// Instance getter of the row-wise kernel for one element type.
-#define HL_ROWWISE_GETTER(NAME, T)                                                         \
-    FusedLauncher NAME(int tmode, bool softcap) {                                          \
-        switch (tmode) {                                                                   \
-            case hl::TM_NONE:                                                              \
-                return softcap ? &hl::launch_rowwise<T, hl::TM_NONE, true>                 \
-                               : &hl::launch_rowwise<T, hl::TM_NONE, false>;               \
-            case hl::TM_FKL:                                                               \
-                return softcap ? &hl::launch_rowwise<T, hl::TM_FKL, true>                  \
-                               : &hl::launch_rowwise<T, hl::TM_FKL, false>;                \
-            case hl::TM_RKL:                                                               \
-                return softcap ? &hl::launch_rowwise<T, hl::TM_RKL, true>                  \
-                               : &hl::launch_rowwise<T, hl::TM_RKL, false>;                \
-            case hl::TM_FDCE:                                                              \
-                return softcap ? &hl::launch_rowwise<T, hl::TM_FDCE, true>                 \
-                               : &hl::launch_rowwise<T, hl::TM_FDCE, false>;               \
-            case hl::TM_FKL_H:                                                             \
-                return softcap ? &hl::launch_rowwise<T, hl::TM_FKL_H, true>                \
-                               : &hl::launch_rowwise<T, hl::TM_FKL_H, false>;              \
-            case hl::TM_RKL_H:                                                             \
-                return softcap ? &hl::launch_rowwise<T, hl::TM_RKL_H, true>                \
-                               : &hl::launch_rowwise<T, hl::TM_RKL_H, false>;              \
-            case hl::TM_FDCE_H:                                                            \
-                return softcap ? &hl::launch_rowwise<T, hl::TM_FDCE_H, true>               \
-                               : &hl::launch_rowwise<T, hl::TM_FDCE_H, false>;             \
-        }                                                                                  \
-        return nullptr;                                                                    \
+// Instance getter, by teacher mode and softcap, of a one-workgroup-per-row kernel
+// (LAUNCH: hl::launch_rowwise or hl::launch_stream_stats) for one element type.
+#define HL_ROW_KERNEL_GETTER(NAME, LAUNCH, T)                                             \
+    FusedLauncher NAME(int tmode, bool softcap) {                                         \
+        switch (tmode) {                                                                  \
+            case hl::TM_NONE:                                                             \
+                return softcap ? &LAUNCH<T, hl::TM_NONE, true>                            \
+                               : &LAUNCH<T, hl::TM_NONE, false>;                          \
+            case hl::TM_FKL:                                                              \
+                return softcap ? &LAUNCH<T, hl::TM_FKL, true>                             \
+                               : &LAUNCH<T, hl::TM_FKL, false>;                           \
+            case hl::TM_RKL:                                                              \
+                return softcap ? &LAUNCH<T, hl::TM_RKL, true>                             \
+                               : &LAUNCH<T, hl::TM_RKL, false>;                           \
+            case hl::TM_FDCE:                                                             \
+                return softcap ? &LAUNCH<T, hl::TM_FDCE, true>                            \
+                               : &LAUNCH<T, hl::TM_FDCE, false>;                          \
+            case hl::TM_FKL_H:                                                            \
+                return softcap ? &LAUNCH<T, hl::TM_FKL_H, true>                           \
+                               : &LAUNCH<T, hl::TM_FKL_H, false>;                         \
+            case hl::TM_RKL_H:                                                            \
+                return softcap ? &LAUNCH<T, hl::TM_RKL_H, true>                           \
+                               : &LAUNCH<T, hl::TM_RKL_H, false>;                         \
+            case hl::TM_FDCE_H:                                                           \
+                return softcap ? &LAUNCH<T, hl::TM_FDCE_H, true>                          \
+                               : &LAUNCH<T, hl::TM_FDCE_H, false>;                        \
+        }                                                                                 \
+        return nullptr;                                                                   \
     }
 
 // Instantiation helper for the per-(dtype, mode) translation units.

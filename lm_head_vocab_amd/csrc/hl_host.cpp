@@ -27,6 +27,7 @@ struct hl_plan_s {
     Geometry geo;
     FusedLauncher fused;
     FusedLauncher rowwise;   // inputs whose base addresses differ modulo 16 bytes
+    FusedLauncher stream;    // forward only: row statistics streamed, one workgroup per row
     void* ws;
     size_t ws_bytes;
     bool ws_owned;
@@ -104,6 +105,11 @@ FusedLauncher lookup_rowwise(hl_dtype dt, int tmode, bool softcap) {
          : dt == HL_BF16 ? get_rowwise_bf16(tmode, softcap) : get_rowwise_f16(tmode, softcap);
 }
 
+FusedLauncher lookup_stream(hl_dtype dt, int tmode, bool softcap) {
+    return dt == HL_F32 ? get_stream_f32(tmode, softcap)
+         : dt == HL_BF16 ? get_stream_bf16(tmode, softcap) : get_stream_f16(tmode, softcap);
+}
+
 FusedLauncher lookup(hl_dtype dt, int tmode, int block, int nvec, bool softcap) {
     return kGetters[(int)dt][tmode](block, nvec, softcap);
 }
@@ -175,7 +181,8 @@ hl_status choose(hl_plan_s* p) {
     }
     p->fused = lookup(p->dtype, p->tmode, p->geo.block, p->geo.nvec, p->softcap > 0.f);
     p->rowwise = lookup_rowwise(p->dtype, p->tmode, p->softcap > 0.f);
-    return (p->fused && p->rowwise) ? HL_OK : HL_ERR_UNSUPPORTED;
+    p->stream = lookup_stream(p->dtype, p->tmode, p->softcap > 0.f);
+    return (p->fused && p->rowwise && p->stream) ? HL_OK : HL_ERR_UNSUPPORTED;
 }
 
 bool finite(float x) { return std::isfinite(x); }
@@ -463,9 +470,15 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
         // split-vocab: 8 XCD groups of rows_per_xcd rows, C workgroups per row
         const dim3 grid(rowwise ? (unsigned)n_rows
                         : C > 1 ? (unsigned)(8 * fp.rows_per_xcd * C) : (unsigned)n_rows);
+        // A launch without a gradient (no grad_out, or GSPO's forward) keeps
+        // nothing of the row after its sums: the streaming kernel reads each
+        // row once with one workgroup and no chunk exchange.
+        const bool fwd_only = fp.grad == nullptr;
+        const FusedLauncher first = (fwd_only && !rowwise) ? plan->stream : launch;
+        const dim3 first_grid = (fwd_only && !rowwise) ? dim3((unsigned)n_rows) : grid;
         if (plan->ev_before && (e = hipEventRecord(plan->ev_before, stream)) != hipSuccess)
             return hip_fail("hipEventRecord(before)", e);
-        e = launch(fp, grid, stream);
+        e = first(fp, first_grid, stream);
         if (e != hipSuccess) return hip_fail("fused kernel launch", e);
         if (gspo) {
             SeamParams sp;

@@ -190,6 +190,10 @@ FusedLauncher get_fused_f16_fdceh(int block, int nvec, bool softcap);
 FusedLauncher get_rowwise_f32(int tmode, bool softcap);
 FusedLauncher get_rowwise_bf16(int tmode, bool softcap);
 FusedLauncher get_rowwise_f16(int tmode, bool softcap);
+// Forward-only streaming statistics kernel (no gradient; GSPO's forward).
+FusedLauncher get_stream_f32(int tmode, bool softcap);
+FusedLauncher get_stream_bf16(int tmode, bool softcap);
+FusedLauncher get_stream_f16(int tmode, bool softcap);
 
 hipError_t launch_count(const CountParams& p, hipStream_t s);  // grid grows when p.fresh
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);

@@ -3,6 +3,6 @@
 
 namespace hl {
 
-HL_ROWWISE_GETTER(get_rowwise_bf16, hl::BF16T)
+HL_ROW_KERNEL_GETTER(get_rowwise_bf16, hl::launch_rowwise, hl::BF16T)
 
 }  // namespace hl

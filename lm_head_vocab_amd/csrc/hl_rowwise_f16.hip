@@ -3,6 +3,6 @@
 
 namespace hl {
 
-HL_ROWWISE_GETTER(get_rowwise_f16, hl::F16T)
+HL_ROW_KERNEL_GETTER(get_rowwise_f16, hl::launch_rowwise, hl::F16T)
 
 }  // namespace hl

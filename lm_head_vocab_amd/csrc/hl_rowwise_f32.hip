@@ -3,6 +3,6 @@
 
 namespace hl {
 
-HL_ROWWISE_GETTER(get_rowwise_f32, hl::F32T)
+HL_ROW_KERNEL_GETTER(get_rowwise_f32, hl::launch_rowwise, hl::F32T)
 
 }  // namespace hl

@@ -156,11 +156,49 @@ def test_accumulate(dtype, combo, V):
 @pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "grpo_z_ent"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_forward_only_matches_and_writes_nothing(dtype, combo):
+    """Without a gradient the statistics come from the streaming kernel, with
+    a different summation order than the register-resident fused kernel of a
+    gradient call: the scalars agree to float rounding (2e-6 relative), and
+    repeated forward-only calls agree bit for bit."""
     spec, inp = _small(dtype, combo, 21, 3001, seed=5)
-    _, sc_fo, _ = _check_small(spec, inp, dtype, grad_mode="none")
+    plan_fo, sc_fo, _ = _check_small(spec, inp, dtype, grad_mode="none")
+    sc_fo2, _ = run_hip(plan_fo, _to_dev(inp), "none")
+    np.testing.assert_array_equal(sc_fo, sc_fo2)
     plan = make_plan(spec, TDT[dtype])
     sc_full, _ = run_hip(plan, _to_dev(inp), "overwrite")
-    np.testing.assert_array_equal(sc_fo, sc_full)
+    np.testing.assert_allclose(sc_fo, sc_full, rtol=2e-6, atol=1e-7)
+
+
+FWD_COMBOS = ["ce_z", "z_ent", "grpo_z_ent", "all_rkl", "all_fkl", "fkl_ent", "all_fdce_h"]
+FWD_SHAPES = SHAPES + [(3, 300_007)]   # long ragged rows every fp32 teacher mode takes
+
+
+@pytest.mark.parametrize("shape", FWD_SHAPES, ids=[f"{n}x{v}" for n, v in FWD_SHAPES])
+@pytest.mark.parametrize("combo", FWD_COMBOS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_forward_only_streaming(dtype, combo, shape):
+    """Forward only: the streaming statistics kernel (one workgroup per row,
+    double-buffered batches of 16-byte vectors, no chunk exchange) against the
+    oracle, scalars and per-row values, on aligned, ragged, tiny and very long
+    rows, with softcap on the reverse-KL combination."""
+    N, V = shape
+    spec, inp = _small(dtype, combo, N, V, seed=3 * N + V, softcap=15.0 if combo == "all_rkl" else 0.0,
+                       bad_labels=1 if N > 4 else 0, mask_frac=0.2 if N > 8 else 0.0)
+    plan, _, _ = _check_small(spec, inp, dtype, grad_mode="none")
+    y = to_np(inp["labels"]).astype(np.int64)
+    vals = oracle.row_values(spec, to_np(inp["logits"]), y, to_np(inp["teacher"]),
+                             to_np(inp.get("old_logprobs")), to_np(inp.get("advantages")))
+    valid, _ = oracle.row_validity(N, V, y, to_np(inp["mask"]))
+    ok = valid & ~_grpo_boundary_rows(spec, inp)
+    rows = plan.row_values().cpu().double().numpy()
+    tol = TOL[dtype]["scalar_rel"]
+    np.testing.assert_allclose(rows[ok, 0], vals["ce"][ok], rtol=tol, atol=tol)
+    if spec.has(ENT):
+        np.testing.assert_allclose(rows[ok, 9], vals["entropy"][ok], rtol=tol, atol=tol)
+    for key, flag in (("fkl", FKL), ("rkl", RKL), ("fdce", FDCE)):
+        if spec.has(flag):
+            np.testing.assert_allclose(rows[ok, 2], vals[key][ok], rtol=tol, atol=tol)
+    assert np.all(rows[~valid] == 0.0)
 
 
 @pytest.mark.parametrize("chunks", [2, 3, 5, 9])
@@ -317,7 +355,8 @@ def test_hinton_accumulate_and_per_token_values(dtype, combo):
 @pytest.mark.parametrize("chunks", [0, 3])
 @pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "all_fdce"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-def test_outlier_logits(dtype, combo, chunks):
+@pytest.mark.parametrize("mode", ["gradient", "forward_only"])
+def test_outlier_logits(dtype, combo, chunks, mode):
     """A logit (or teacher logit) far above the rest of its row, placed after
     the first vector of a wave, in the ragged head/tail, or in the first
     vector: the softmax shift is taken from each wave's first vector, and a
@@ -358,7 +397,9 @@ def test_outlier_logits(dtype, combo, chunks):
     ref_sc, ref_g, _ = run_oracle(spec, inp)
     xmax = float(inp["logits"].float().abs().max()) * spec.logit_scale * 1.4427
     f32_abs = max(1e-6, 2 * 0.6931 * xmax * 2.0 ** -23 * float(np.max(np.abs(ref_g))))
-    _, sc, _ = _check_small(spec, inp, dtype, chunks=chunks, f32_abs=f32_abs, skip_scalars=("ENTROPY",))
+    gm = None if mode == "gradient" else "none"
+    _, sc, _ = _check_small(spec, inp, dtype, chunks=chunks, grad_mode=gm, f32_abs=f32_abs,
+                            skip_scalars=("ENTROPY",))
     e = SLOT["ENTROPY"]
     assert abs(sc[e] - ref_sc[e]) <= 2e-6 + TOL[dtype]["scalar_rel"] * abs(ref_sc[e]), (sc[e], ref_sc[e])
     spec_c, inp_c = _small(dtype, combo, N, V, seed=71 + chunks, softcap=30.0, scale=0.5)
@@ -367,7 +408,7 @@ def test_outlier_logits(dtype, combo, chunks):
     if spec_c.has(GRPO):
         inp_c["old_logprobs"] = oracle_old_logprobs(spec_c, inp_c["logits"], inp_c["labels"], inp_c["old_noise"])
     ref_sc, ref_c, _ = run_oracle(spec_c, inp_c)
-    _, sc, _ = _check_small(spec_c, inp_c, dtype, chunks=chunks, skip_scalars=("ENTROPY",),
+    _, sc, _ = _check_small(spec_c, inp_c, dtype, chunks=chunks, grad_mode=gm, skip_scalars=("ENTROPY",),
                             f32_abs=max(1e-6, 2 * 0.6931 * 30 * 1.4427 * 2.0 ** -23 * float(np.max(np.abs(ref_c)))))
     assert abs(sc[e] - ref_sc[e]) <= 2e-6 + TOL[dtype]["scalar_rel"] * abs(ref_sc[e]), (sc[e], ref_sc[e])
 
