@@ -29,7 +29,7 @@ METRIC = "tokens/s + achieved HBM GB/s (% peak), CE+z+GRPO+entropy, V=151936 bf1
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, vendor figure
 FUSED_KERNEL = "fused_kernel"
 # with GSPO the timed bracket holds the forward, the segment step and the reloading backward
-GSPO_KERNELS = "fused_kernel (forward) + seam_kernel + fused_kernel (load mode)"
+GSPO_KERNELS = "stream_stats_kernel (forward) + seam_kernel + fused_kernel (load mode)"
 LOSS_NAMES = {1: "CE", 2: "z", 4: "FKL", 8: "RKL", 64: "FDCE", 16: "GRPO", 128: "GSPO", 32: "entropy"}
 HINTON_BIT = 1 << 17
 
