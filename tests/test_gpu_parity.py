@@ -532,6 +532,17 @@ def test_nonfinite_logits(dtype, combo, chunks):
     keep = np.ones(N, dtype=bool)
     keep[2] = False
     grad_check(g.detach().cpu()[torch.from_numpy(keep)], ref_g[keep], dtype, labels=to_np(labels2)[keep])
+    # without a gradient (the streaming statistics kernel): the same scalars' fate, and the
+    # per-row values of the other rows as the oracle computes them
+    sc_fo, _ = run_hip(plan, _to_dev(inp2), "none")
+    assert np.isnan(sc_fo[SLOT["CE"]]) and np.isnan(sc_fo[SLOT["TOTAL"]])
+    assert sc_fo[SLOT["N_VALID"]] == N
+    rows = plan.row_values().cpu().double().numpy()
+    assert np.isnan(rows[2, 0])
+    vals = oracle.row_values(spec, to_np(inp2["logits"]), to_np(labels2).astype(np.int64),
+                             to_np(inp2.get("teacher")), to_np(inp2.get("old_logprobs")),
+                             to_np(inp2.get("advantages")))
+    np.testing.assert_allclose(rows[keep, 0], vals["ce"][keep], rtol=TOL[dtype]["scalar_rel"])
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
