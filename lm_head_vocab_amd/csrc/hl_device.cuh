@@ -1007,8 +1007,6 @@ hipError_t launch_fused(const FusedParams& p, dim3 grid, hipStream_t s) {
 // over the waves in wave order; the coefficients and the per-element gradient
 // are the fused kernel's.
 // ---------------------------------------------------------------------------
-constexpr int kRowwiseBlock = 256;
-
 template <typename T, int TMODE, bool SOFTCAP>
 __global__ __launch_bounds__(kRowwiseBlock) void rowwise_kernel(const FusedParams p) {
     constexpr int NW = kRowwiseBlock / 64;

@@ -28,6 +28,7 @@ struct hl_plan_s {
     FusedLauncher fused;
     FusedLauncher rowwise;   // inputs whose base addresses differ modulo 16 bytes
     FusedLauncher stream;    // forward only: row statistics streamed, one workgroup per row
+    bool long_rows;          // no register-resident variant fits V: every gradient call is row-wise
     void* ws;
     size_t ws_bytes;
     bool ws_owned;
@@ -176,13 +177,16 @@ hl_status choose(hl_plan_s* p) {
         if (g.chunks == 0) {   // very long rows: the fewest chunks that fit at all
             for (int C = 1; C <= max_chunks && g.chunks == 0; ++C) g = geometry_for(p->V, p->dtype, p->tmode, C);
         }
-        if (g.chunks == 0) return HL_ERR_UNSUPPORTED;
-        p->geo = g;
+        p->long_rows = g.chunks == 0;
+        // rows longer than every register-resident slice: one row-wise
+        // workgroup per row (forward-only calls still stream)
+        p->geo = p->long_rows ? Geometry{1, kRowwiseBlock, 0} : g;
     }
-    p->fused = lookup(p->dtype, p->tmode, p->geo.block, p->geo.nvec, p->softcap > 0.f);
+    if (p->forced_chunks > 0) p->long_rows = false;
+    p->fused = p->long_rows ? nullptr : lookup(p->dtype, p->tmode, p->geo.block, p->geo.nvec, p->softcap > 0.f);
     p->rowwise = lookup_rowwise(p->dtype, p->tmode, p->softcap > 0.f);
     p->stream = lookup_stream(p->dtype, p->tmode, p->softcap > 0.f);
-    return (p->fused && p->rowwise && p->stream) ? HL_OK : HL_ERR_UNSUPPORTED;
+    return ((p->long_rows || p->fused) && p->rowwise && p->stream) ? HL_OK : HL_ERR_UNSUPPORTED;
 }
 
 bool finite(float x) { return std::isfinite(x); }
@@ -217,6 +221,7 @@ hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags
     if (out == nullptr) return HL_ERR_INVALID_ARG;
     *out = nullptr;
     if (V < 1 || weights == nullptr) return HL_ERR_INVALID_ARG;
+    if (V > kMaxRowElements) return HL_ERR_UNSUPPORTED;
     if (dtype != HL_F32 && dtype != HL_BF16 && dtype != HL_F16) return HL_ERR_INVALID_ARG;
     if ((loss_flags & ~kKnownBits) != 0u || (loss_flags & kLossBits) == 0u) return HL_ERR_INVALID_ARG;
     const uint32_t dbits = loss_flags & kDistillBits;
@@ -464,8 +469,11 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
         // addresses agree modulo 16; otherwise the row-wise kernel runs (one
         // workgroup per row, element loads and stores).
         const uintptr_t xa = mod16(logits);
-        const bool rowwise = (plan->tmode != TM_NONE && mod16(teacher_logits) != xa) ||
-                             (grad_out != nullptr && mod16(grad_out) != xa);
+        const bool teacher_ok = plan->tmode == TM_NONE || mod16(teacher_logits) == xa;
+        // rows longer than every register-resident slice go row-wise too
+        const bool rowwise = plan->long_rows || !teacher_ok || (grad_out != nullptr && mod16(grad_out) != xa);
+        // the streaming forward reads logits and teacher only, at any row length
+        const bool stream_ok = teacher_ok;
         const FusedLauncher launch = rowwise ? plan->rowwise : plan->fused;
         // split-vocab: 8 XCD groups of rows_per_xcd rows, C workgroups per row
         const dim3 grid(rowwise ? (unsigned)n_rows
@@ -474,8 +482,8 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
         // nothing of the row after its sums: the streaming kernel reads each
         // row once with one workgroup and no chunk exchange.
         const bool fwd_only = fp.grad == nullptr;
-        const FusedLauncher first = (fwd_only && !rowwise) ? plan->stream : launch;
-        const dim3 first_grid = (fwd_only && !rowwise) ? dim3((unsigned)n_rows) : grid;
+        const FusedLauncher first = (fwd_only && stream_ok) ? plan->stream : launch;
+        const dim3 first_grid = (fwd_only && stream_ok) ? dim3((unsigned)n_rows) : grid;
         if (plan->ev_before && (e = hipEventRecord(plan->ev_before, stream)) != hipSuccess)
             return hip_fail("hipEventRecord(before)", e);
         e = first(fp, first_grid, stream);

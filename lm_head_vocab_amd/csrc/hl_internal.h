@@ -199,6 +199,11 @@ hipError_t launch_count(const CountParams& p, hipStream_t s);  // grid grows whe
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_seam(const SeamParams& p, hipStream_t s);
 
+// Threads per workgroup of the row-wise kernel (one workgroup per row).
+constexpr int kRowwiseBlock = 256;
+// Longest row any kernel takes: element indices within a row are 32-bit.
+constexpr int64_t kMaxRowElements = 0x7fffffffLL;
+
 // Vector counts that have a kernel instance, per block size.
 constexpr int kSmallBlock = 256;
 constexpr int kMidBlock = 512;

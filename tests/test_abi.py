@@ -66,16 +66,39 @@ def test_status_strings():
     (dict(cap=math.nan), hl.HL_ERR_INVALID_ARG),
     (dict(w=Weights(math.nan, 0, 0, 0, 1, 0)), hl.HL_ERR_INVALID_ARG),
     (dict(w=Weights(1, 0, 0, 0, math.inf, 0)), hl.HL_ERR_INVALID_ARG),
-    (dict(V=10**9), hl.HL_ERR_UNSUPPORTED),
-    (dict(V=1_500_000), hl.HL_ERR_UNSUPPORTED),
-    (dict(V=1_474_561 + 8), hl.HL_ERR_UNSUPPORTED),              # past 9 x 1024 x 20 vectors
-    (dict(V=737_280 + 8, flags=hl.RKL), hl.HL_ERR_UNSUPPORTED),   # past 9 x 1024 x 10 teacher vectors
-    (dict(V=655_360 + 8, flags=hl.FDCE | hl.HINTON), hl.HL_ERR_UNSUPPORTED),   # 8 chunks at most
+    (dict(V=2**31), hl.HL_ERR_UNSUPPORTED),                        # 32-bit element indices
 ])
 def test_plan_rejects(kwargs, status):
     st, h = _plan(**kwargs)
     assert st == status
     assert not h.value
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(V=10**9), dict(V=2**31 - 1), dict(V=1_500_000),
+    dict(V=1_474_561 + 8),                                 # past 9 x 1024 x 20 student vectors
+    dict(V=737_280 + 8, flags=hl.RKL),                     # past 9 x 1024 x 10 teacher vectors
+    dict(V=655_360 + 8, flags=hl.FDCE | hl.HINTON),        # 8 chunks at most there
+    dict(V=368_640 + 4, dtype=hl.HL_F32, flags=hl.FKL),    # fp32: 4 elements per vector
+])
+def test_rows_past_every_slice_take_the_rowwise_kernel(kwargs):
+    st, h = _plan(**kwargs)
+    assert st == hl.HL_OK
+    c, b, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), ctypes.byref(n)) == hl.HL_OK
+    assert (c.value, b.value, n.value) == (1, 256, 0)
+    # a forced chunk count still has to fit a slice
+    assert lib.hl_plan_set_chunks(h, 9) == hl.HL_ERR_UNSUPPORTED
+    assert lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), ctypes.byref(n)) == hl.HL_OK
+    assert (c.value, b.value, n.value) == (1, 256, 0)
+    lib.hl_plan_destroy(h)
+    # one element shorter than a full slice set still plans a register-resident variant
+    if kwargs["V"] < 10**6 and "dtype" not in kwargs:
+        st, h = _plan(**dict(kwargs, V=kwargs["V"] - 8))
+        assert st == hl.HL_OK
+        lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), ctypes.byref(n))
+        assert n.value > 0
+        lib.hl_plan_destroy(h)
 
 
 def test_plan_accepts_and_describes_the_baseline_shapes():

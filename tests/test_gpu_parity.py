@@ -430,6 +430,23 @@ def test_maximum_vocabulary(case):
     assert (d["chunks"], d["block"], d["vec_per_thread"]) == geo
 
 
+# one vector past the longest register-resident slices: the row-wise kernel
+LONG_ROWS = [("bf16", "ce_z", 1_474_569, False), ("bf16", "all_rkl", 737_288, True),
+             ("f32", "ce_fkl", 368_644, False), ("bf16", "all_fdce_h", 655_368, False)]
+
+
+@pytest.mark.parametrize("case", LONG_ROWS, ids=[f"{d}-{c}-{v}" for d, c, v, _ in LONG_ROWS])
+def test_rows_past_every_slice(case):
+    """Rows longer than every register-resident slice take the row-wise kernel
+    (three reads of each row); forward-only calls the streaming kernel."""
+    dtype, combo, V, acc = case
+    spec, inp = _small(dtype, combo, 3, V, seed=V % 997, softcap=20.0 if acc else 0.0, scale=0.7 if acc else 1.0,
+                       accumulate=acc, bad_labels=1, mask_frac=0.0)
+    plan, _, _ = _check_small(spec, inp, dtype)
+    assert plan.describe() == {"chunks": 1, "block": 256, "vec_per_thread": 0}
+    _check_small(spec, inp, dtype, grad_mode="none")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_edge_cases(dtype):
     dt = TDT[dtype]
