@@ -92,6 +92,17 @@ def test_rows_past_every_slice_take_the_rowwise_kernel(kwargs):
     assert lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), ctypes.byref(n)) == hl.HL_OK
     assert (c.value, b.value, n.value) == (1, 256, 0)
     lib.hl_plan_destroy(h)
+    # a row-wise plan keeps no chunk-exchange words: its workspace is a one-chunk plan's
+    st, h = _plan(**kwargs)
+    flags = kwargs.get("flags", hl.CE)
+    st1, h1 = _plan(V=1000, dtype=kwargs.get("dtype", hl.HL_BF16), flags=flags)
+    assert st == st1 == hl.HL_OK
+    lib.hl_plan_describe(h1, ctypes.byref(c), None, None)
+    assert c.value == 1
+    for n_rows in (0, 1, 777, 32768):
+        assert lib.hl_workspace_bytes(h, n_rows) == lib.hl_workspace_bytes(h1, n_rows)
+    lib.hl_plan_destroy(h)
+    lib.hl_plan_destroy(h1)
     # one element shorter than a full slice set still plans a register-resident variant
     if kwargs["V"] < 10**6 and "dtype" not in kwargs:
         st, h = _plan(**dict(kwargs, V=kwargs["V"] - 8))
