@@ -447,6 +447,39 @@ def test_rows_past_every_slice(case):
     _check_small(spec, inp, dtype, grad_mode="none")
 
 
+def test_two_plans_on_two_streams():
+    """Two split-vocab plans (a teacher row set in 4 chunks, a student row set in
+    2) run concurrently on two streams of default priority, calls interleaved:
+    each result is bitwise the one its plan gives alone. The chunks of a row
+    wait for each other on the device; with two kernels in flight their
+    workgroups share the CUs, and the in-order dispatch of each kernel keeps
+    every wait finite (a broken wait would surface as NaN, not a hang)."""
+    spec_a, inp_a = _small("bf16", "ce_fkl", 512, 151936, seed=3, mask_frac=0.1)
+    spec_b, inp_b = _small("bf16", "grpo_z_ent", 768, 151936, seed=4, mask_frac=0.1)
+    plan_a, plan_b = make_plan(spec_a, torch.bfloat16), make_plan(spec_b, torch.bfloat16)
+    assert plan_a.describe()["chunks"] == 4 and plan_b.describe()["chunks"] == 2
+    da, db = _to_dev(inp_a), _to_dev(inp_b)
+    sc_a, g_a = run_hip(plan_a, da, "overwrite")
+    sc_b, g_b = run_hip(plan_b, db, "overwrite")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(4):
+        ga, gb = torch.empty_like(g_a), torch.empty_like(g_b)
+        with torch.cuda.stream(s1):
+            ra = plan_a(da["logits"], labels=da["labels"], mask=da["mask"], teacher=da["teacher"], grad=ga)
+        with torch.cuda.stream(s2):
+            rb = plan_b(db["logits"], labels=db["labels"], mask=db["mask"], old_logprobs=db["old_logprobs"],
+                        advantages=db["advantages"], grad=gb)
+        outs.append((ra, ga, rb, gb))
+    torch.cuda.synchronize()
+    say(f"[gpu] two streams: {len(outs)} interleaved call pairs")
+    for ra, ga, rb, gb in outs:
+        np.testing.assert_array_equal(ra.cpu().double().numpy(), sc_a)
+        np.testing.assert_array_equal(rb.cpu().double().numpy(), sc_b)
+        assert torch.equal(ga.view(torch.int16), g_a.view(torch.int16))
+        assert torch.equal(gb.view(torch.int16), g_b.view(torch.int16))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_edge_cases(dtype):
     dt = TDT[dtype]
