@@ -145,11 +145,12 @@ typedef struct hl_plan_s* hl_plan_t;
  * without a distillation flag, temperature <= 0 with distillation, eps outside (0,1) with a policy loss, bad scale or
  * softcap, non-finite weight),
  * HL_ERR_UNSUPPORTED (V >= 2^31: element indices within a row are 32-bit).
- * Rows longer than the register-resident slices of the fused kernel hold
- * (9 chunks x 1024 threads x 20 student or 10 student + teacher vectors of
- * 16 bytes; 8 chunks for HL_FDCE with HL_HINTON) are served by the row-wise
- * kernel, which reads each row three times: correct at any length, slower;
- * hl_plan_describe then reports 1 chunk, 256 threads, 0 vectors.
+ * Rows longer than the slices the on-device chunk exchange serves (9 chunks
+ * x 1024 threads x 20 student or 10 student + teacher vectors of 16 bytes;
+ * 8 chunks for HL_FDCE with HL_HINTON) take two launches: the statistics are
+ * streamed first, then the fused kernel writes the gradient from them with
+ * as many chunks as the row needs (each row read twice); hl_plan_describe
+ * reports that chunk count.
  */
 hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags,
                   const hl_weights* weights, float temperature, float eps,

@@ -17,9 +17,10 @@
 // With GSPO that kernel runs first (row statistics), then, after a segment
 // kernel has turned the statistics into per-segment ratios and per-row
 // coefficients, the fused kernel in load mode (the statistics read back from
-// the row records, the slice reloaded, the gradient written). Inputs whose
-// base addresses differ modulo 16 bytes, and rows longer than every
-// register-resident slice, take rowwise_kernel in place of the fused kernel.
+// the row records, the slice reloaded, the gradient written); rows longer
+// than every slice the chunk exchange serves take the same two launches
+// without the segment step. Inputs whose base addresses differ modulo 16
+// bytes take rowwise_kernel in place of the fused kernel.
 //
 // The gradient is written in the two-coefficient form of Fast-LLM PR #558
 // (Triton kernel for the monolithic loss, section Design): prob_coeff times
@@ -1004,12 +1005,11 @@ hipError_t launch_fused(const FusedParams& p, dim3 grid, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // rowwise_kernel: the same losses, row records and gradient for inputs whose
 // base addresses differ modulo 16 bytes, where no split of a row into 16-byte
-// vectors is aligned in all of logits, teacher and gradient at once, and for
-// rows longer than every register-resident slice. One 256-thread workgroup
-// per row with element loads and stores; the row is read three times (exact
-// maxima, sums, gradient). The statistics are taken relative to the exact row
-// maxima, merged over the waves in wave order; the coefficients and the
-// per-element gradient are the fused kernel's.
+// vectors is aligned in all of logits, teacher and gradient at once. One
+// 256-thread workgroup per row with element loads and stores; the row is read
+// three times (exact maxima, sums, gradient). The statistics are taken
+// relative to the exact row maxima, merged over the waves in wave order; the
+// coefficients and the per-element gradient are the fused kernel's.
 // ---------------------------------------------------------------------------
 template <typename T, int TMODE, bool SOFTCAP>
 __global__ __launch_bounds__(kRowwiseBlock) void rowwise_kernel(const FusedParams p) {

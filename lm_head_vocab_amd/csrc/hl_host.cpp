@@ -28,7 +28,8 @@ struct hl_plan_s {
     FusedLauncher fused;
     FusedLauncher rowwise;   // inputs whose base addresses differ modulo 16 bytes
     FusedLauncher stream;    // forward only: row statistics streamed, one workgroup per row
-    bool long_rows;          // no register-resident variant fits V: every gradient call is row-wise
+    bool long_rows;          // V past every slice the chunk exchange serves: statistics streamed first,
+                             // then the gradient from the records (fused kernel, load mode, many chunks)
     void* ws;
     size_t ws_bytes;
     bool ws_owned;
@@ -61,6 +62,10 @@ struct Layout {
     size_t ctrl, chunk_rec, row_rec, rows, partials, row_coef, seg_of_row, seg_rec, total;
 };
 
+// Chunks of a row that exchange their records on the device (1 when the
+// statistics are streamed first and the fused kernel only runs in load mode).
+int exchange_chunks(const hl_plan_s* p) { return p->long_rows ? 1 : p->geo.chunks; }
+
 // Workspace regions, in order: control words, split-vocab exchange words,
 // per-row softmax records, per-row values, reduction partials, and for GSPO
 // the per-row coefficient, the row -> segment map and the segment records
@@ -70,7 +75,7 @@ Layout layout_for(const hl_plan_s* p, int64_t n) {
     const size_t N = n > 0 ? (size_t)n : 0;
     L.ctrl = 0;
     L.chunk_rec = align256(NCTRL * sizeof(uint32_t));
-    const size_t rec_bytes = p->geo.chunks > 1 ? N * p->geo.chunks * XWORDS * sizeof(uint64_t) : 0;
+    const size_t rec_bytes = exchange_chunks(p) > 1 ? N * p->geo.chunks * XWORDS * sizeof(uint64_t) : 0;
     L.row_rec = L.chunk_rec + align256(rec_bytes);
     L.rows = L.row_rec + align256(N * REC * sizeof(float));
     L.partials = L.rows + align256(N * NCOL * sizeof(float));
@@ -178,15 +183,26 @@ hl_status choose(hl_plan_s* p) {
             for (int C = 1; C <= max_chunks && g.chunks == 0; ++C) g = geometry_for(p->V, p->dtype, p->tmode, C);
         }
         p->long_rows = g.chunks == 0;
-        // rows longer than every register-resident slice: one row-wise
-        // workgroup per row (forward-only calls still stream)
-        p->geo = p->long_rows ? Geometry{1, kRowwiseBlock, 0} : g;
+        if (p->long_rows) {
+            // Rows longer than every slice the chunk exchange serves: the
+            // statistics are streamed first (stream_stats_kernel), and the
+            // gradient comes from the fused kernel in load mode, which needs
+            // no exchange, with as many 1024-thread chunks as the row needs.
+            const int vec = p->dtype == HL_F32 ? 4 : 8;
+            const int nmax = p->tmode == TM_NONE ? kLargeNvecStudent[9] : kLargeNvecTeacher[4];
+            const int64_t per_chunk = (int64_t)kLargeBlock * nmax;
+            const int64_t nvec_row = p->V / vec;
+            const int64_t C = (nvec_row + per_chunk - 1) / per_chunk;
+            g = geometry_for(p->V, p->dtype, p->tmode, (int)C, kLargeBlock);
+            if (g.chunks == 0) return HL_ERR_UNSUPPORTED;
+        }
+        p->geo = g;
     }
     if (p->forced_chunks > 0) p->long_rows = false;
-    p->fused = p->long_rows ? nullptr : lookup(p->dtype, p->tmode, p->geo.block, p->geo.nvec, p->softcap > 0.f);
+    p->fused = lookup(p->dtype, p->tmode, p->geo.block, p->geo.nvec, p->softcap > 0.f);
     p->rowwise = lookup_rowwise(p->dtype, p->tmode, p->softcap > 0.f);
     p->stream = lookup_stream(p->dtype, p->tmode, p->softcap > 0.f);
-    return ((p->long_rows || p->fused) && p->rowwise && p->stream) ? HL_OK : HL_ERR_UNSUPPORTED;
+    return (p->fused && p->rowwise && p->stream) ? HL_OK : HL_ERR_UNSUPPORTED;
 }
 
 bool finite(float x) { return std::isfinite(x); }
@@ -404,6 +420,7 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
     float* row_rec = reinterpret_cast<float*>(ws + L.row_rec);
     float* rows = reinterpret_cast<float*>(ws + L.rows);
     const int C = plan->geo.chunks;
+    const int CX = exchange_chunks(plan);   // chunks whose records travel through the exchange words
 
     CountParams cp;
     cp.labels = labels;
@@ -415,11 +432,11 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
     // own records (older epochs). Anything else (a new workspace, or a region
     // another call's layout used for other data) is zero-filled by the count
     // kernel first, and the epoch restarts.
-    const bool fresh = C > 1 && plan->clean_rows < n_rows;
+    const bool fresh = CX > 1 && plan->clean_rows < n_rows;
     cp.fresh = fresh ? 1 : 0;
     cp.vec = (labels != nullptr && aligned16(labels) && (mask == nullptr || aligned16(mask))) ? 1 : 0;
     cp.fill = chunk_words;
-    cp.fill_words = C > 1 ? n_rows * C * XWORDS : 0;
+    cp.fill_words = CX > 1 ? n_rows * CX * XWORDS : 0;
     hipError_t e = launch_count(cp, stream);
     if (e != hipSuccess) return hip_fail("count kernel launch", e);
 
@@ -470,10 +487,12 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
         // workgroup per row, element loads and stores).
         const uintptr_t xa = mod16(logits);
         const bool teacher_ok = plan->tmode == TM_NONE || mod16(teacher_logits) == xa;
-        // rows longer than every register-resident slice go row-wise too
-        const bool rowwise = plan->long_rows || !teacher_ok || (grad_out != nullptr && mod16(grad_out) != xa);
+        const bool rowwise = !teacher_ok || (grad_out != nullptr && mod16(grad_out) != xa);
         // the streaming forward reads logits and teacher only, at any row length
         const bool stream_ok = teacher_ok;
+        // rows past every exchanged slice: statistics streamed, then the
+        // gradient from the records (the fused kernel in load mode)
+        const bool two_pass = plan->long_rows && !rowwise;
         const FusedLauncher launch = rowwise ? plan->rowwise : plan->fused;
         // split-vocab: 8 XCD groups of rows_per_xcd rows, C workgroups per row
         const dim3 grid(rowwise ? (unsigned)n_rows
@@ -482,8 +501,9 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
         // nothing of the row after its sums: the streaming kernel reads each
         // row once with one workgroup and no chunk exchange.
         const bool fwd_only = fp.grad == nullptr;
-        const FusedLauncher first = (fwd_only && stream_ok) ? plan->stream : launch;
-        const dim3 first_grid = (fwd_only && stream_ok) ? dim3((unsigned)n_rows) : grid;
+        const bool stream_first = stream_ok && (fwd_only || two_pass);
+        const FusedLauncher first = stream_first ? plan->stream : launch;
+        const dim3 first_grid = stream_first ? dim3((unsigned)n_rows) : grid;
         if (plan->ev_before && (e = hipEventRecord(plan->ev_before, stream)) != hipSuccess)
             return hip_fail("hipEventRecord(before)", e);
         e = first(fp, first_grid, stream);
@@ -514,6 +534,10 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
                 e = launch(fp, grid, stream);
                 if (e != hipSuccess) return hip_fail("fused kernel launch (load mode)", e);
             }
+        } else if (two_pass && grad_out != nullptr) {
+            fp.load_mode = 1;
+            e = launch(fp, grid, stream);
+            if (e != hipSuccess) return hip_fail("fused kernel launch (load mode)", e);
         }
         if (plan->ev_after && (e = hipEventRecord(plan->ev_after, stream)) != hipSuccess)
             return hip_fail("hipEventRecord(after)", e);

@@ -81,18 +81,25 @@ def test_plan_rejects(kwargs, status):
     dict(V=655_360 + 8, flags=hl.FDCE | hl.HINTON),        # 8 chunks at most there
     dict(V=368_640 + 4, dtype=hl.HL_F32, flags=hl.FKL),    # fp32: 4 elements per vector
 ])
-def test_rows_past_every_slice_take_the_rowwise_kernel(kwargs):
+def test_rows_past_every_exchanged_slice_plan_two_launches(kwargs):
+    """Rows longer than any slice set the chunk exchange serves: statistics
+    streamed first, the gradient from the fused kernel in load mode with as many
+    1024-thread chunks as the row needs."""
     st, h = _plan(**kwargs)
     assert st == hl.HL_OK
     c, b, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     assert lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), ctypes.byref(n)) == hl.HL_OK
-    assert (c.value, b.value, n.value) == (1, 256, 0)
-    # a forced chunk count still has to fit a slice
+    vec = 4 if kwargs.get("dtype") == hl.HL_F32 else 8
+    teacher = kwargs.get("flags", hl.CE) & (hl.FKL | hl.RKL | hl.FDCE)
+    assert b.value == 1024 and n.value <= (10 if teacher else 20) and c.value >= 8
+    assert c.value * b.value * n.value * vec >= kwargs["V"] - vec      # the slices cover the row
+    # a forced chunk count still has to fit a slice the exchange serves
+    before = (c.value, b.value, n.value)
     assert lib.hl_plan_set_chunks(h, 9) == hl.HL_ERR_UNSUPPORTED
     assert lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), ctypes.byref(n)) == hl.HL_OK
-    assert (c.value, b.value, n.value) == (1, 256, 0)
+    assert (c.value, b.value, n.value) == before
     lib.hl_plan_destroy(h)
-    # a row-wise plan keeps no chunk-exchange words: its workspace is a one-chunk plan's
+    # no chunk-exchange words for such a plan: its workspace is a one-chunk plan's
     st, h = _plan(**kwargs)
     flags = kwargs.get("flags", hl.CE)
     st1, h1 = _plan(V=1000, dtype=kwargs.get("dtype", hl.HL_BF16), flags=flags)

@@ -430,21 +430,37 @@ def test_maximum_vocabulary(case):
     assert (d["chunks"], d["block"], d["vec_per_thread"]) == geo
 
 
-# one vector past the longest register-resident slices: the row-wise kernel
+# one vector past the longest slices the chunk exchange serves: statistics
+# streamed, then the gradient from the fused kernel in load mode
 LONG_ROWS = [("bf16", "ce_z", 1_474_569, False), ("bf16", "all_rkl", 737_288, True),
              ("f32", "ce_fkl", 368_644, False), ("bf16", "all_fdce_h", 655_368, False)]
 
 
 @pytest.mark.parametrize("case", LONG_ROWS, ids=[f"{d}-{c}-{v}" for d, c, v, _ in LONG_ROWS])
 def test_rows_past_every_slice(case):
-    """Rows longer than every register-resident slice take the row-wise kernel
-    (three reads of each row); forward-only calls the streaming kernel."""
+    """Rows longer than every slice the chunk exchange serves: the statistics
+    streamed first, the gradient from the fused kernel in load mode with as many
+    chunks as the row needs; forward-only calls stream only. Misaligned bases
+    on such rows take the row-wise kernel."""
     dtype, combo, V, acc = case
     spec, inp = _small(dtype, combo, 3, V, seed=V % 997, softcap=20.0 if acc else 0.0, scale=0.7 if acc else 1.0,
                        accumulate=acc, bad_labels=1, mask_frac=0.0)
     plan, _, _ = _check_small(spec, inp, dtype)
-    assert plan.describe() == {"chunks": 1, "block": 256, "vec_per_thread": 0}
+    d = plan.describe()
+    assert d["block"] == 1024 and d["chunks"] >= 8
     _check_small(spec, inp, dtype, grad_mode="none")
+    # the same rows with a gradient buffer misaligned against the logits: row-wise
+    ref_sc, ref_g, _ = run_oracle(spec, inp)
+    dev = _to_dev(inp)
+    es = dev["logits"].element_size()
+    buf = torch.empty(dev["logits"].numel() * es + 64, dtype=torch.uint8, device=DEV)
+    g = buf[es: es + dev["logits"].numel() * es].view(dev["logits"].dtype).view(dev["logits"].shape)
+    g.copy_(inp["grad_init"].to(DEV) if acc else torch.zeros_like(dev["logits"]))
+    sc = plan(dev["logits"], labels=dev["labels"], mask=dev["mask"], teacher=dev["teacher"],
+              old_logprobs=dev.get("old_logprobs"), advantages=dev.get("advantages"), grad=g)
+    torch.cuda.synchronize()
+    assert_scalars(spec, sc.cpu().double().numpy(), ref_sc, dtype)
+    grad_check(g.detach().cpu(), ref_g, dtype, labels=to_np(inp["labels"]))
 
 
 def test_two_plans_on_two_streams():
