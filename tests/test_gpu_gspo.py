@@ -248,6 +248,19 @@ def test_gspo_forward_only_and_determinism():
     assert torch.equal(g1.view(torch.int16), g2.view(torch.int16))
 
 
+@pytest.mark.parametrize("case", [("bf16", "all_gspo_rkl", 737_288), ("f32", "gspo_z_ent", 737_284)],
+                         ids=["bf16-rkl-737288", "f32-z-737284"])
+def test_gspo_rows_past_every_exchanged_slice(case):
+    """GSPO on rows longer than any slice the chunk exchange serves: the same
+    streamed forward and segment step, then a load-mode backward with more
+    chunks than the exchange allows."""
+    dtype, combo, V = case
+    spec, inp = _case(dtype, combo, 9, V, seed=V % 991, bad_labels=1, max_len=4)
+    plan, _, _, _, _ = _check(spec, inp, dtype)
+    d = plan.describe()
+    assert d["block"] == 1024 and d["chunks"] > 9
+
+
 def test_gspo_changing_batches_and_segments():
     """One plan, calls with different row and segment counts."""
     spec, _ = _case("bf16", "all_gspo_rkl", 4, 30011, seed=1)
