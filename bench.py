@@ -7,7 +7,10 @@ workloads call hl_forward_backward_segments) over one batch of synthetic
 inputs already resident in HBM. Prints one JSON line on stdout; progress
 goes to stderr.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1] [--no-grad]
+
+--no-grad times metrics-only calls (no gradient buffer): the streaming
+statistics kernel, one read of each valid row (GSPO: plus the segment step).
 """
 
 from __future__ import annotations
@@ -30,6 +33,8 @@ PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, vendor figure
 FUSED_KERNEL = "fused_kernel"
 # with GSPO the timed bracket holds the forward, the segment step and the reloading backward
 GSPO_KERNELS = "stream_stats_kernel (forward) + seam_kernel + fused_kernel (load mode)"
+STREAM_KERNEL = "stream_stats_kernel"
+GSPO_FWD_KERNELS = "stream_stats_kernel (forward) + seam_kernel"
 LOSS_NAMES = {1: "CE", 2: "z", 4: "FKL", 8: "RKL", 64: "FDCE", 16: "GRPO", 128: "GSPO", 32: "entropy"}
 HINTON_BIT = 1 << 17
 
@@ -124,10 +129,13 @@ def cpu_baseline(w, budget_s: float, threads: int):
 # ---------------------------------------------------------------------------
 # GPU measurement
 # ---------------------------------------------------------------------------
-def stored_traffic(w, src_hash):
+def stored_traffic(w, src_hash, with_grad=True):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources; else None."""
-    tag = "fused_seam" if w.flags & workloads.GSPO else FUSED_KERNEL
+    if with_grad:
+        tag = "fused_seam" if w.flags & workloads.GSPO else FUSED_KERNEL
+    else:
+        tag = "stream_seam" if w.flags & workloads.GSPO else "stream_stats"
     path = os.path.join(ROOT, "profiles", f"{tag}_{w.name}_pmc.json")
     if not os.path.exists(path):
         return None
@@ -149,6 +157,7 @@ def main(argv=None):
     ap.add_argument("--no-separate", action="store_true")
     ap.add_argument("--chunks", type=int, default=0, help="force the split-vocab chunk count")
     ap.add_argument("--block", type=int, default=0, help="force the threads per workgroup (with --chunks)")
+    ap.add_argument("--no-grad", action="store_true", help="metrics-only calls (no gradient buffer)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -189,7 +198,7 @@ def main(argv=None):
         valid &= inp["mask"] != 0
     n_valid = int(valid.sum().item())
     acc = bool(w.flags & workloads.ACCUMULATE)
-    grad = inp["grad_init"].clone() if acc else torch.empty_like(inp["logits"])
+    grad = None if args.no_grad else (inp["grad_init"].clone() if acc else torch.empty_like(inp["logits"]))
     plan = hl.Plan(w.V, w.torch_dtype, w.flags, **plan_kwargs(w))
     if args.chunks or args.block:
         plan.set_variant(args.chunks, args.block)
@@ -219,7 +228,7 @@ def main(argv=None):
     del src, dst
 
     separate = None
-    if not args.no_separate:
+    if not args.no_separate and not args.no_grad:
         plans = []
         first = True
         for bit, lname in LOSS_NAMES.items():
@@ -285,13 +294,15 @@ def main(argv=None):
     kernel_avg = sum(kernel_ms) / K
     log(f"timed {K} steps: {ms_step:.4f} ms/step, fused kernel {kernel_avg:.4f} ms avg")
 
-    algo_bytes = workloads.algorithmic_bytes(w, n_valid)
+    algo_bytes = workloads.algorithmic_bytes(w, n_valid, with_grad=not args.no_grad)
     achieved = algo_bytes / (kernel_avg * 1e-3) / 1e9
     src_hash = source_hash()
-    traffic = stored_traffic(w, src_hash)
+    traffic = stored_traffic(w, src_hash, with_grad=not args.no_grad)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                "kernel": GSPO_KERNELS if w.flags & workloads.GSPO else FUSED_KERNEL, "kernel_ms_avg": round(kernel_avg, 5),
+                "kernel": ((GSPO_KERNELS if w.flags & workloads.GSPO else FUSED_KERNEL) if not args.no_grad else
+                           (GSPO_FWD_KERNELS if w.flags & workloads.GSPO else STREAM_KERNEL)),
+                "kernel_ms_avg": round(kernel_avg, 5),
                 "algorithmic_bytes_per_launch": algo_bytes}
 
     if separate is not None:
@@ -313,7 +324,7 @@ def main(argv=None):
         "config": {"workload": w.name, "N": w.N, "V": w.V, "dtype": w.dtype,
                    "losses": "+".join(LOSS_NAMES[b] for b in LOSS_NAMES if w.flags & b)
                              + (" (Hinton temperature)" if w.flags & HINTON_BIT else ""),
-                   "accumulate": acc, "n_valid": n_valid, "variant": geo},
+                   "accumulate": acc, "gradient": not args.no_grad, "n_valid": n_valid, "variant": geo},
         "hbm_GBps_step": round(algo_bytes / (ms_step * 1e-3) / 1e9, 1),
         "frac_peak_step": round(algo_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "copy_GBps": round(copy_gbps, 1),

@@ -61,6 +61,18 @@ def test_masked_rows_cost_their_gradient_write_only():
             - workloads.algorithmic_bytes(acc, n_valid_rows=acc.N - 10)) == 10 * 4 * row  # x, t, old grad, grad
 
 
+def test_metrics_only_calls_read_each_valid_row_once():
+    # no gradient: one read of each valid row's logits (and teacher), the side inputs;
+    # GSPO without a gradient has no reloading backward, and accumulate mode no old-gradient read
+    for name, tensors in (("grpo_z_ent_bf16", 1), ("gspo_z_ent_bf16", 1), ("ce_fkl_bf16", 2),
+                          ("all_combined_bf16", 2)):
+        w = workloads.WORKLOADS[name]
+        row = 2 * w.V
+        got = workloads.algorithmic_bytes(w, n_valid_rows=w.N - 7, with_grad=False)
+        side = {"grpo_z_ent_bf16": 17, "gspo_z_ent_bf16": 17, "ce_fkl_bf16": 8, "all_combined_bf16": 16}[name]
+        assert got == (w.N - 7) * tensors * row + w.N * side, name
+
+
 def test_headline_launch_bytes_match_the_design_figure():
     # 16384 tokens, 5% of them masked in the generated batch: 15534 valid rows
     w = workloads.WORKLOADS[workloads.HEADLINE]

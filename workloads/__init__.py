@@ -259,7 +259,7 @@ def algorithmic_bytes(w: Workload, n_valid_rows: int, n_rows: int | None = None,
             b += n_valid_rows * 2 * row
         else:
             b += N * row
-    if w.flags & GSPO:
+    if with_grad and w.flags & GSPO:
         # the backward reloads every valid row once the segment ratios are known
         b += n_valid_rows * tensors_read * row
     side = 8  # labels
