@@ -168,6 +168,9 @@ size_t hl_workspace_bytes(hl_plan_t plan, int64_t n_rows);
  * hl_workspace_bytes(plan, n_rows) for every later call). Replaces any
  * workspace the library allocated. Makes no HIP call: the next call clears
  * whatever part of the workspace must start at zero, on its own stream.
+ * Several plans may share one workspace (their calls must not overlap in
+ * time): the workspace's own control words record what its split-vocab
+ * region holds, whichever plan wrote it last.
  * Errors: HL_ERR_INVALID_ARG (NULL plan or pointer, misaligned pointer). */
 hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t bytes);
 
@@ -205,6 +208,12 @@ hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t byte
  * Gradient with respect to the raw logits of a valid row:
  *   grad_scale / n * ds/dx * sum_k weight_k * dloss_k/ds
  * with n the number of valid rows (or weights.divisor when > 0).
+ * Split-vocab rows (several workgroups per row) combine their statistics on
+ * the device with a bounded wait. If a workgroup gives up waiting (its
+ * siblings were never scheduled beside it), it writes NaN into its part of
+ * the row's gradient (and, for the row's first part, the row's values), and
+ * every float scalar of the call is NaN: a failed combine never yields a
+ * finite wrong result in the parts it writes.
  * Errors: HL_ERR_INVALID_ARG (NULL plan, n_rows < 0, NULL logits or
  * scalars_out, a base not aligned to the element size), HL_ERR_MISSING_INPUT (see above),
  * HL_ERR_WORKSPACE (a workspace that is too small was set by the caller),
@@ -289,6 +298,16 @@ hl_status hl_plan_describe(hl_plan_t plan, int* chunks, int* block, int* vec_per
  * forward launch and after the load-mode launch of the fused kernel), on the
  * call's stream, so a profiler can time the dominant kernel alone. */
 hl_status hl_plan_set_timing_events(hl_plan_t plan, hipEvent_t before, hipEvent_t after);
+
+/* Failure handling test hook (split-vocab rows): bound the device-side
+ * wait of later calls to spin_limit polls (>= 1; the default is 2^20), and
+ * make the workgroup that owns vocabulary chunk withhold_chunk of row
+ * withhold_row skip publishing its statistics (withhold_row < 0: none), so
+ * that every workgroup of that row gives up its wait and the call takes the
+ * failure path described at hl_forward_backward; every kernel still ends.
+ * Errors: HL_ERR_INVALID_ARG (NULL plan, spin_limit 0). */
+hl_status hl_plan_set_exchange_test(hl_plan_t plan, uint32_t spin_limit, int64_t withhold_row,
+                                    int withhold_chunk);
 
 /* Text of the last HIP failure seen by this thread (which call, the HIP
  * error string and code), or "" if none. Valid until the next failing call. */

@@ -113,6 +113,8 @@ def load_library(path: str | None = None):
     lib.hl_plan_describe.restype = ctypes.c_int
     lib.hl_plan_set_timing_events.argtypes = [vp, vp, vp]
     lib.hl_plan_set_timing_events.restype = ctypes.c_int
+    lib.hl_plan_set_exchange_test.argtypes = [vp, u32, i64, ctypes.c_int]
+    lib.hl_plan_set_exchange_test.restype = ctypes.c_int
     lib.hl_last_error.argtypes = []
     lib.hl_last_error.restype = ctypes.c_char_p
     lib.hl_status_str.argtypes = [ctypes.c_int]
@@ -200,7 +202,19 @@ class Plan:
             self._h, ctypes.c_void_p(before.cuda_event if before is not None else 0),
             ctypes.c_void_p(after.cuda_event if after is not None else 0))
 
+    def set_exchange_test(self, spin_limit: int = 1 << 20, withhold_row: int = -1, withhold_chunk: int = -1):
+        """Failure-handling hook of the split-vocab wait (hl_plan_set_exchange_test)."""
+        _check("hl_plan_set_exchange_test", self._lib.hl_plan_set_exchange_test(
+            self._h, int(spin_limit), int(withhold_row), int(withhold_chunk)))
+
     # -- the call -----------------------------------------------------------
+    def set_workspace(self, ws):
+        """Use a caller's uint8 device tensor as the workspace (hl_plan_set_workspace);
+        several plans may share one (their calls must not overlap)."""
+        self._ws = ws
+        _check("hl_plan_set_workspace", self._lib.hl_plan_set_workspace(
+            self._h, ctypes.c_void_p(ws.data_ptr()), ws.numel()))
+
     def _ensure_workspace(self, n_rows: int, device):
         torch = _torch()
         need = max(self.workspace_bytes(n_rows), 256)

@@ -9,6 +9,19 @@ namespace hl {
 // with eight 16-byte label loads and one 16-byte mask load, all issued before
 // any is used, so a tile costs one memory latency; a ragged last tile and
 // unaligned inputs go one row at a time.
+//
+// It also keeps the split-vocab words safe to reuse. A chunk takes a
+// sibling's word once the word carries the current call's epoch, so no word
+// left in the workspace may carry it: every call bumps the epoch (a 32-bit
+// counter in the workspace's control words, whichever plan calls), and the
+// words are trusted only where the workspace held zeros or such words
+// before. CTRL_CLEAN counts the leading words known to be so. When the
+// call's words reach past it (another call's layout kept other data there),
+// on a plan's first call on a workspace (control words undefined: `reset`),
+// and when the epoch wraps, this kernel zero-fills the call's words first.
+// Afterwards CTRL_CLEAN is the call's own word count: its other regions
+// follow its words. One workgroup reads the control words, fills and writes
+// them, so no other workgroup can see them half updated.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void count_row(int64_t y, bool unmasked, int64_t V, uint32_t& nv, uint32_t& nb) {
     const bool in_range = (y >= 0) && (y < V);
@@ -17,12 +30,19 @@ __device__ __forceinline__ void count_row(int64_t y, bool unmasked, int64_t V, u
 }
 
 __global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
-    if (p.fresh) {
-        const int64_t stride = (int64_t)gridDim.x * 1024;
-        for (int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x; i < p.fill_words; i += stride) p.fill[i] = 0ull;
-        if (blockIdx.x != 0) return;
-    }
     __shared__ uint32_t s_v[16], s_b[16];
+    // every thread reads the control words before thread 0 rewrites them
+    // (after the barrier of the count below)
+    const uint32_t old_epoch = p.reset ? 0u : p.ctrl[CTRL_EPOCH];
+    const uint64_t clean = p.reset ? 0ull
+                                   : (((uint64_t)p.ctrl[CTRL_CLEAN_HI] << 32) | (uint64_t)p.ctrl[CTRL_CLEAN_LO]);
+    const bool wrap = old_epoch == 0xffffffffu;
+    if (p.fill_words > 0 && (p.reset || wrap || clean < (uint64_t)p.fill_words)) {
+        // the words start 256-byte aligned and come in groups of 8 per (row, chunk)
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        u32x4* w = reinterpret_cast<u32x4*>(p.fill);
+        for (int64_t i = threadIdx.x; i < p.fill_words / 2; i += 1024) w[i] = z;
+    }
     uint32_t nv = 0, nb = 0;
     if (p.vec) {
         for (int64_t base = 0; base < p.n_rows; base += 16384) {
@@ -67,13 +87,16 @@ __global__ __launch_bounds__(1024) void count_kernel(const CountParams p) {
         for (int w = 0; w < 16; ++w) { tv += s_v[w]; tb += s_b[w]; }
         p.ctrl[CTRL_NVALID] = tv;
         p.ctrl[CTRL_NBAD] = tb;
-        // tags this call's split-vocab records; a fresh workspace restarts at 1
-        // (its records were just zeroed, i.e. carry epoch 0)
-        const uint32_t next = p.ctrl[CTRL_EPOCH] + 1u;
-        p.ctrl[CTRL_EPOCH] = (p.fresh || next == 0u) ? 1u : next;
+        // this call's epoch: words carry epochs >= 1, a zero-filled word epoch 0
+        p.ctrl[CTRL_EPOCH] = (p.reset || wrap) ? 1u : old_epoch + 1u;
+        p.ctrl[CTRL_CLEAN_LO] = (uint32_t)((uint64_t)p.fill_words & 0xffffffffu);
+        p.ctrl[CTRL_CLEAN_HI] = (uint32_t)((uint64_t)p.fill_words >> 32);
         p.ctrl[CTRL_ERROR] = 0u;
         p.ctrl[CTRL_DONE] = 0u;
         p.ctrl[CTRL_NSEG] = 0u;
+        p.ctrl[CTRL_SPIN] = p.spin_limit;
+        p.ctrl[CTRL_HOLD_ROW] = p.hold_row;
+        p.ctrl[CTRL_HOLD_CHUNK] = p.hold_chunk;
     }
 }
 
@@ -360,12 +383,7 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
 
 hipError_t launch_count(const CountParams& p, hipStream_t s) {
     (void)hipGetLastError();   // drop an error left by an earlier, unrelated call
-    int64_t groups = 1;
-    if (p.fresh) {
-        groups = (p.fill_words + 4095) / 4096;
-        groups = groups < 1 ? 1 : (groups > 1024 ? 1024 : groups);
-    }
-    hipLaunchKernelGGL(count_kernel, dim3((unsigned)groups), dim3(1024), 0, s, p);
+    hipLaunchKernelGGL(count_kernel, dim3(1), dim3(1024), 0, s, p);
     return hipGetLastError();
 }
 

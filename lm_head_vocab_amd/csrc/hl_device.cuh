@@ -388,47 +388,62 @@ __device__ __forceinline__ void row_status(const int64_t* labels, const uint8_t*
 // q^tau_j = softmax(s / tau)_j instead: tau w (q^tau_j - p_j), or
 // tau w q^tau_j (lq^tau_j - lp_j - KL_tau) for the reverse KL (the tau^2 on
 // the loss times the 1 / tau of d(s / tau) / ds).
-struct Coefs {
-    float B2;      // log2-domain student log-partition
-    float Bt2;     // log2-domain teacher log-partition
-    float Bd;      // log2-domain tempered student log-partition (Hinton modes)
-    float alpha;   // probability coefficient, times G k / n
-    float beta;    // label-column coefficient, times G k / n
-    float gam;     // forward-KL teacher coefficient, times G k / n
-    float gq;      // tempered student coefficient (Hinton forward KL / FDCE)
-    float rho2;    // reverse-KL log-ratio coefficient (log2 domain)
-    float c0;      // reverse-KL probability coefficient
-    float sB;      // pass-2 student exponent offset: -B2, or c log2(e) - B2 with softcap
-    float sBd;     // tempered student offset: -Bd, or c log2(e) beta - Bd with softcap
+//
+// Precision of the fp32 instances (HP). An fp32 exponent x k log2(e) - B2 is
+// off by up to |x k log2 e| 2^-24 through the rounding of k log2(e) alone,
+// and by up to |B2| 2^-24 through that of the log-partition B2, which moves
+// every softmax entry by as much relatively; the GRPO ratio exp(s_y - lse -
+// old) suffers the same from lse, and the hardware exp2 and every fp32
+// product add about an ulp each. The fp32 instances therefore carry
+// k log2(e), log2(e) / tau and 1 / tau as hi + lo pairs, take each wave's
+// exact maxima as the pass-1 shifts (the largest elements then sit at offset
+// ~0, where an fp32 offset is exact), form the per-row coefficients in fp64
+// and evaluate each gradient element in fp64 from the fp32 inputs (and, with
+// softcap, the same fp32 cap_r value pass 1 summed), rounding it once.
+template <typename R>
+struct CoefsT {
+    R alpha;   // probability coefficient, times G k / n
+    R beta;    // label-column coefficient, times G k / n
+    R gam;     // forward-KL teacher coefficient, times G k / n
+    R gq;      // tempered student coefficient (Hinton forward KL / FDCE)
+    R rho2;    // reverse-KL log-ratio coefficient (log2 domain)
+    R c0;      // reverse-KL probability coefficient
+    R sB;      // pass-2 student exponent offset: -B2, or c log2(e) - B2 with softcap
+    R sBd;     // tempered student offset: -Bd, or c log2(e) beta - Bd with softcap
+    R sBt;     // pass-2 teacher exponent offset: -Bt2
+    R cd;      // HP Hinton: the tempered exponent is aq beta + cd, cd = log2(Z) beta - log2(Zs)
 };
+using Coefs = CoefsT<float>;
+using CoefsD = CoefsT<double>;
 
 // All data registers are live where the fused kernel calls this, so only
 // single-instruction hardware log2 / exp2 / rcp are used; the reported
 // per-row values are recomputed in fp64 by the reduction from the same record.
 template <int TMODE, bool SOFTCAP>
-__device__ __forceinline__ Coefs row_coefs(const FusedParams& p, const Rec& r, int64_t y, float xy,
-                                           float old, float adv) {
+__device__ __forceinline__ Coefs row_coefs_fast(const FusedParams& p, const Rec& r, int64_t y, float xy,
+                                                float old, float adv) {
     const uint32_t f = p.flags;
     const float l2Z = __builtin_amdgcn_logf(r.Z);
     Coefs k;
-    k.B2 = r.M + l2Z;
-    const float lse = k.B2 * kLn2f;
-    k.Bt2 = 0.f;
-    k.Bd = 0.f;
+    const float B2 = r.M + l2Z;
+    const float lse = B2 * kLn2f;
+    float Bt2 = 0.f, Bd = 0.f;
     float kl = 0.f;
     if (TMODE != TM_NONE) {
         const float l2Zt = __builtin_amdgcn_logf(r.Zt);
-        k.Bt2 = r.Mt + l2Zt;
+        Bt2 = r.Mt + l2Zt;
         if (is_hinton(TMODE)) {
             const float l2Zs = __builtin_amdgcn_logf(r.Zs);
-            k.Bd = fmaf(r.M, p.beta, l2Zs);
+            Bd = fmaf(r.M, p.beta, l2Zs);
             if (base_mode(TMODE) == TM_RKL) kl = kLn2f * (r.SX * __builtin_amdgcn_rcpf(r.Zs) - l2Zs + l2Zt);
         } else if (TMODE == TM_RKL) {
             kl = kLn2f * (r.SX * __builtin_amdgcn_rcpf(r.Z) - l2Z + l2Zt);
         }
     }
-    k.sB = SOFTCAP ? p.cl - k.B2 : -k.B2;
-    k.sBd = SOFTCAP ? fmaf(p.cl, p.beta, -k.Bd) : -k.Bd;
+    k.sB = SOFTCAP ? p.cl - B2 : -B2;
+    k.sBd = SOFTCAP ? fmaf(p.cl, p.beta, -Bd) : -Bd;
+    k.sBt = -Bt2;
+    k.cd = 0.f;
     float a_g = 0.f;
     if ((f & F_GRPO) && y >= 0) {
         const float sy = SOFTCAP ? p.cap * hl_tanh(xy * p.kc) : p.k * xy;
@@ -463,52 +478,158 @@ __device__ __forceinline__ Coefs row_coefs(const FusedParams& p, const Rec& r, i
     return k;
 }
 
-// Gradient of one element; lab = the label-column coefficient at the label, else 0.
+// The fp32 instances' coefficients: the same quantities in fp64.
 template <int TMODE, bool SOFTCAP>
-__device__ __forceinline__ float grad_one(const FusedParams& p, const Coefs& k, float x, float t, float lab) {
+__device__ __forceinline__ CoefsD row_coefs_hp(const FusedParams& p, const Rec& r, int64_t y, float xy,
+                                               float old, float adv) {
+    constexpr double LN2 = 0.69314718055994530942;
+    const uint32_t f = p.flags;
+    CoefsD k;
+    const double l2Z = log2((double)r.Z);
+    const double B2 = (double)r.M + l2Z;
+    const double lse = B2 * LN2;
+    k.sB = (SOFTCAP ? (double)p.cl : 0.0) - B2;
+    k.sBd = 0.0;
+    k.sBt = 0.0;
+    k.cd = 0.0;
+    double kl = 0.0;
+    if (TMODE != TM_NONE) {
+        const double l2Zt = log2((double)r.Zt);
+        k.sBt = -((double)r.Mt + l2Zt);
+        if (is_hinton(TMODE)) {
+            const double l2Zs = log2((double)r.Zs);
+            k.cd = l2Z * ((double)p.beta + (double)p.beta_l) - l2Zs;
+            if (base_mode(TMODE) == TM_RKL) kl = LN2 * ((double)r.SX / (double)r.Zs - l2Zs + l2Zt);
+        } else if (TMODE == TM_RKL) {
+            kl = LN2 * ((double)r.SX / (double)r.Z - l2Z + l2Zt);
+        }
+    }
+    double a_g = 0.0;
+    if ((f & F_GRPO) && y >= 0) {
+        const double sy = SOFTCAP ? (double)p.cap * tanh((double)p.k * (double)xy / (double)p.cap)
+                                  : (double)p.k * (double)xy;
+        const double ratio = exp((sy - lse) - (double)old);
+        const double eps = p.eps;
+        const bool active = !((adv > 0.f && ratio > 1.0 + eps) || (adv < 0.f && ratio < 1.0 - eps));
+        a_g = active ? (double)adv * ratio : 0.0;
+    }
+    const uint32_t n_valid = p.ctrl[CTRL_NVALID];
+    const double n = p.divisor > 0.f ? (double)p.divisor : (double)n_valid;
+    const double scale = (double)p.grad_scale * (double)p.k / n;
+    double P = 0.0, L = 0.0, wd = 0.0;
+    if ((f & F_CE) && p.w_ce != 0.f) { P += p.w_ce; L += p.w_ce; }
+    if ((f & F_Z) && p.w_z != 0.f) P += 2.0 * (double)p.w_z * lse;
+    if ((f & F_GRPO) && p.w_g != 0.f) { P += (double)p.w_g * a_g; L += (double)p.w_g * a_g; }
+    if ((f & F_DISTILL) && p.w_d != 0.f) wd = p.w_d;
+    if (fkl_like(TMODE) && !is_hinton(TMODE)) P += wd;
+    k.alpha = scale * P;
+    k.beta = scale * L;
     if (is_hinton(TMODE)) {
-        float aq, aqd, cfh = 1.0f;       // log2 of the student and of the tempered student
+        const double wt = wd * (double)p.tau;
+        k.gam = scale * wt;
+        k.gq = k.gam;
+        k.rho2 = scale * wt * LN2;
+        k.c0 = -scale * wt * kl;
+    } else {
+        k.gam = scale * wd;
+        k.gq = 0.0;
+        k.rho2 = scale * wd * LN2;
+        k.c0 = scale * (P - wd * kl);
+    }
+    return k;
+}
+
+template <bool HP>
+using CoefsFor = typename std::conditional<HP, CoefsD, Coefs>::type;
+
+template <int TMODE, bool SOFTCAP, bool HP>
+__device__ __forceinline__ CoefsFor<HP> row_coefs(const FusedParams& p, const Rec& r, int64_t y, float xy,
+                                                  float old, float adv) {
+    if constexpr (HP) return row_coefs_hp<TMODE, SOFTCAP>(p, r, y, xy, old, adv);
+    else return row_coefs_fast<TMODE, SOFTCAP>(p, r, y, xy, old, adv);
+}
+
+// 2^a in fp64: 2^a = 2^n 2^u with n = rint(a), |u| <= 1/2, and 2^u = e^(u ln 2)
+// from the Taylor series of the exponential to degree 8 (remainder below
+// 2^-32 relative, ample for a result that is rounded to fp32). A NaN
+// argument gives NaN, -Inf and arguments far below the fp64 range give 0.
+__device__ __forceinline__ double exp2_hp(double a) {
+    constexpr double LN2 = 0.69314718055994530942;
+    if (!(a > -1070.0)) return a != a ? a : 0.0;
+    const double n = rint(a);
+    const double v = (a - n) * LN2;
+    double e = 1.0 / 40320.0;
+    e = fma(e, v, 1.0 / 5040.0);
+    e = fma(e, v, 1.0 / 720.0);
+    e = fma(e, v, 1.0 / 120.0);
+    e = fma(e, v, 1.0 / 24.0);
+    e = fma(e, v, 1.0 / 6.0);
+    e = fma(e, v, 0.5);
+    e = fma(e, v, 1.0);
+    e = fma(e, v, 1.0);
+    return ldexp(e, (int)n);
+}
+
+// Gradient of one element; lab = the label-column coefficient at the label,
+// else 0. The fp32 instances (HP) compute in fp64 and return the unrounded
+// value (the caller adds the existing gradient, if any, and rounds once).
+template <int TMODE, bool SOFTCAP, bool HP>
+__device__ __forceinline__ typename std::conditional<HP, double, float>::type
+grad_one(const FusedParams& p, const CoefsFor<HP>& k, float x, float t,
+         typename std::conditional<HP, double, float>::type lab) {
+    if constexpr (HP) {
+        double aq, cf = 1.0;          // log2 of the student's softmax entry
         if (SOFTCAP) {
-            const float r = cap_r(x, p.kc2);
+            const double r = (double)cap_r(x, p.kc2);
+            aq = fma(r, -2.0 * (double)p.cl, k.sB);
+            cf = r * (4.0 - 4.0 * r);
+        } else {
+            aq = fma((double)x, (double)p.K1 + (double)p.K1l, k.sB);
+        }
+        const double q = exp2_hp(aq);
+        double up = 0.0;              // log2 of the teacher's softmax entry
+        if (TMODE != TM_NONE) up = fma((double)t, (double)p.K2 + (double)p.K2l, k.sBt);
+        double g;
+        if (is_hinton(TMODE)) {
+            const double aqd = fma(aq, (double)p.beta + (double)p.beta_l, k.cd);
+            const double qd = exp2_hp(aqd);
+            if (fkl_like(TMODE)) g = k.alpha * q + k.gq * qd - k.gam * exp2_hp(up) - lab;
+            else g = k.alpha * q + qd * (k.rho2 * (aqd - up) + k.c0) - lab;
+        } else if (TMODE == TM_NONE) {
+            g = k.alpha * q - lab;
+        } else if (fkl_like(TMODE)) {
+            g = k.alpha * q - k.gam * exp2_hp(up) - lab;
+        } else {
+            g = q * (k.rho2 * (aq - up) + k.c0) - lab;
+        }
+        return SOFTCAP ? cf * g : g;
+    } else {
+        float aq, r = 0.f, cf = 1.0f;     // aq = log2 of the student's softmax entry
+        if (SOFTCAP) {
+            r = cap_r(x, p.kc2);
             aq = fmaf(r, -2.0f * p.cl, k.sB);
-            aqd = fmaf(r, -2.0f * p.cl * p.beta, k.sBd);
-            cfh = r * fmaf(-4.0f, r, 4.0f);
+            cf = r * fmaf(-4.0f, r, 4.0f);
         } else {
             aq = fmaf(x, p.K1, k.sB);
-            aqd = fmaf(x, p.K1 * p.beta, k.sBd);
         }
         const float q = fast_exp2(aq);
-        const float qd = fast_exp2(aqd);
+        float up = 0.f;                   // log2 of the teacher's softmax entry
+        if (TMODE != TM_NONE) up = fmaf(t, p.K2, k.sBt);
         float g;
-        if (fkl_like(TMODE)) {
-            const float pt = fast_exp2(fmaf(t, p.K2, -k.Bt2));
-            g = fmaf(k.alpha, q, fmaf(k.gq, qd, fmaf(-k.gam, pt, -lab)));
+        if (is_hinton(TMODE)) {
+            const float aqd = SOFTCAP ? fmaf(r, -2.0f * p.cl * p.beta, k.sBd) : fmaf(x, p.K1 * p.beta, k.sBd);
+            const float qd = fast_exp2(aqd);
+            if (fkl_like(TMODE)) g = fmaf(k.alpha, q, fmaf(k.gq, qd, fmaf(-k.gam, fast_exp2(up), -lab)));
+            else g = fmaf(k.alpha, q, fmaf(qd, fmaf(k.rho2, aqd - up, k.c0), -lab));
+        } else if (TMODE == TM_NONE) {
+            g = fmaf(k.alpha, q, -lab);
+        } else if (fkl_like(TMODE)) {
+            g = fmaf(k.alpha, q, fmaf(-k.gam, fast_exp2(up), -lab));
         } else {
-            const float up = fmaf(t, p.K2, -k.Bt2);
-            g = fmaf(k.alpha, q, fmaf(qd, fmaf(k.rho2, aqd - up, k.c0), -lab));
+            g = fmaf(q, fmaf(k.rho2, aq - up, k.c0), -lab);
         }
-        return SOFTCAP ? cfh * g : g;
+        return SOFTCAP ? cf * g : g;
     }
-    float aq, cf = 1.0f;
-    if (SOFTCAP) {
-        const float r = cap_r(x, p.kc2);
-        aq = fmaf(r, -2.0f * p.cl, k.sB);
-        cf = r * fmaf(-4.0f, r, 4.0f);
-    } else {
-        aq = fmaf(x, p.K1, k.sB);
-    }
-    const float q = fast_exp2(aq);
-    float g;
-    if (TMODE == TM_NONE) {
-        g = fmaf(k.alpha, q, -lab);
-    } else if (fkl_like(TMODE)) {
-        const float pt = fast_exp2(fmaf(t, p.K2, -k.Bt2));
-        g = fmaf(k.alpha, q, fmaf(-k.gam, pt, -lab));
-    } else {
-        const float up = fmaf(t, p.K2, -k.Bt2);
-        g = fmaf(q, fmaf(k.rho2, aq - up, k.c0), -lab);
-    }
-    return SOFTCAP ? cf * g : g;
 }
 
 // One element's terms of the pass-1 sums, in the log2 domain, relative to
@@ -516,20 +637,27 @@ __device__ __forceinline__ float grad_one(const FusedParams& p, const Coefs& k, 
 // when WS: the entropy sum), Zt += 2^u, the distillation cross sum SX (and
 // St = sum 2^u u, Zs = sum 2^(a / tau) in the modes that need them), with
 // a = s log2(e) - M the student's and u = t log2(e) / tau - Mt the teacher's
-// offset.
-template <int TMODE, bool SOFTCAP, bool WS>
+// offset (HP: with the low parts of the constants).
+template <int TMODE, bool SOFTCAP, bool WS, bool HP>
 __device__ __forceinline__ void stat_term(const FusedParams& p, float M, float Mt, float x, float t, float& z,
                                           float& s, float& zt, float& sx, float& st, float& zs) {
-    const float a = SOFTCAP ? fmaf(cap_r(x, p.kc2), -2.0f * p.cl, p.cl - M) : fmaf(x, p.K1, -M);
+    float a;
+    if (SOFTCAP) {
+        a = fmaf(cap_r(x, p.kc2), -2.0f * p.cl, p.cl - M);
+    } else {
+        a = fmaf(x, p.K1, -M);
+        if (HP) a = fmaf(x, p.K1l, a);
+    }
     const float ex = fast_exp2(a);
     z += ex;
     if (WS) s = fmaf(ex, a, s);
     if (TMODE != TM_NONE) {
-        const float u = fmaf(t, p.K2, -Mt);
+        float u = fmaf(t, p.K2, -Mt);
+        if (HP) u = fmaf(t, p.K2l, u);
         const float et = fast_exp2(u);
         zt += et;
         if (is_hinton(TMODE)) {
-            const float ad = a * p.beta;          // tempered student, shift M beta
+            const float ad = HP ? fmaf(a, p.beta_l, a * p.beta) : a * p.beta;   // tempered student, shift M beta
             const float ed = fast_exp2(ad);
             zs += ed;
             if (fkl_like(TMODE)) sx = fmaf(et, u - ad, sx);
@@ -546,26 +674,26 @@ __device__ __forceinline__ void stat_term(const FusedParams& p, float M, float M
 // ---------------------------------------------------------------------------
 // fused_kernel
 // ---------------------------------------------------------------------------
-// Bounded wait for the sibling chunks of a row (split-vocab variant only).
-constexpr uint32_t kSpinLimit = 1u << 20;
-
 
 // Waves per SIMD the register allocation must allow (the second
 // __launch_bounds__ argument): student-only slices of at most 10 vectors per
 // thread (8 with softcap) are held to 64 VGPRs, i.e. 8 waves per SIMD, so that
 // 32 waves (two 1024-thread or four 512-thread workgroups) share a CU; every
-// other instance is held to 128 VGPRs (4 waves per SIMD), which all fit.
-template <int BLOCK, int NVEC, int TMODE, bool SOFTCAP>
+// other instance is held to 128 VGPRs (4 waves per SIMD), which all fit. The
+// fp32 instances form their per-row coefficients in fp64 (HP) and take the
+// 128-VGPR budget too.
+template <typename T, int BLOCK, int NVEC, int TMODE, bool SOFTCAP>
 constexpr int min_waves_per_simd() {
-    return (TMODE == TM_NONE && NVEC <= (SOFTCAP ? 8 : 10)) ? 8 : 4;
+    return (!std::is_same<T, F32T>::value && TMODE == TM_NONE && NVEC <= (SOFTCAP ? 8 : 10)) ? 8 : 4;
 }
 
 template <typename T, int BLOCK, int NVEC, int TMODE, bool SOFTCAP>
-__global__ __launch_bounds__(BLOCK, (min_waves_per_simd<BLOCK, NVEC, TMODE, SOFTCAP>()))
+__global__ __launch_bounds__(BLOCK, (min_waves_per_simd<T, BLOCK, NVEC, TMODE, SOFTCAP>()))
 void fused_kernel(const FusedParams p) {
     constexpr int VEC = T::VEC;
     constexpr int ES = T::ESIZE;
     constexpr int NW = BLOCK / 64;
+    constexpr bool HP = std::is_same<T, F32T>::value;   // fp32: exact shifts, hi + lo constants
     static_assert(NW <= 16, "at most 16 waves per workgroup");
 
     __shared__ float s_rec[16][REC];
@@ -726,7 +854,21 @@ void fused_kernel(const FusedParams p) {
     // vector, the wave takes the true maximum and sums again. The entropy sum
     // S is formed only when the entropy metric is requested.
     float mx = kNegInf, mt = kNegInf;
-    if (tid < nv) {
+    if (HP) {
+        // fp32: the wave's exact maxima (its largest elements then sit at
+        // offset ~0, where the fp32 offsets are exact)
+#pragma unroll
+        for (int v = 0; v < NVEC; ++v) {
+            if (tid < nv - v * BLOCK) {
+                mx = T::vmax(mx, xs[v]);
+                if (TMODE != TM_NONE) mt = T::vmax(mt, ts[v]);
+            }
+        }
+        if (has_e) {
+            mx = fmaxf(mx, xe);
+            if (TMODE != TM_NONE) mt = fmaxf(mt, te);
+        }
+    } else if (tid < nv) {
         mx = T::vmax(mx, xs[0]);
         if (TMODE != TM_NONE) mt = T::vmax(mt, ts[0]);
     }
@@ -744,7 +886,7 @@ void fused_kernel(const FusedParams p) {
     // one term of every sum; the entropy term only when WS
     auto term = [&](auto want_s_tag, float x, float t, float& z, float& s, float& zt, float& sx, float& st,
                     float& zs) {
-        stat_term<TMODE, SOFTCAP, decltype(want_s_tag)::value>(p, M, Mt, x, t, z, s, zt, sx, st, zs);
+        stat_term<TMODE, SOFTCAP, decltype(want_s_tag)::value, HP>(p, M, Mt, x, t, z, s, zt, sx, st, zs);
     };
     auto accumulate = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st, float& zs) {
         term(std::true_type(), x, t, z, s, zt, sx, st, zs);
@@ -861,9 +1003,11 @@ void fused_kernel(const FusedParams p) {
             constexpr int NXW = xwords_used(TMODE);
             constexpr int POS_ZS = has_st(TMODE) ? 7 : 6;
             const uint64_t epoch = (uint64_t)p.ctrl[CTRL_EPOCH] << 32;
+            const uint32_t spin_limit = p.ctrl[CTRL_SPIN];
+            const bool held = (uint32_t)row == p.ctrl[CTRL_HOLD_ROW] && (uint32_t)c == p.ctrl[CTRL_HOLD_CHUNK];
             uint64_t* words = p.chunk_words + (int64_t)row * p.chunks * XWORDS;
-            if (lane == 0) {
-                uint64_t* mine = words + c * XWORDS;
+            uint64_t* mine = words + c * XWORDS;
+            if (lane == 0 && !held) {
                 const float f[XWORDS] = {wr.M, wr.Z, wr.S, wr.Mt, wr.Zt, wr.SX,
                                          has_st(TMODE) ? wr.St : wr.Zs, wr.Zs};
 #pragma unroll
@@ -876,16 +1020,28 @@ void fused_kernel(const FusedParams p) {
             const int lw = (lane / NXW) * XWORDS + lane % NXW;
             uint64_t w = 0;
             uint32_t spins = 0;
+            bool gave_up = false;
             while (true) {
                 if (lane < nwords) w = __hip_atomic_load(words + lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const bool ok = (lane >= nwords) || ((w & 0xffffffff00000000ull) == epoch);
                 if (__all(ok)) break;
                 __builtin_amdgcn_s_sleep(1);
-                if (++spins > kSpinLimit) {
-                    if (lane == 0)
-                        __hip_atomic_store(&p.ctrl[CTRL_ERROR], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (++spins > spin_limit) {
+                    gave_up = true;
                     break;
                 }
+            }
+            if (gave_up) {
+                // A sibling never published: this chunk's statistics become NaN
+                // (so its gradient slice and, for chunk 0, the row record are
+                // NaN), its words are republished as NaN for any sibling still
+                // polling, and the error word makes every scalar NaN.
+                if (lane == 0)
+                    __hip_atomic_store(&p.ctrl[CTRL_ERROR], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (lane < NXW)
+                    __hip_atomic_store(mine + lane, epoch | 0x7fc00000ull, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                w = epoch | 0x7fc00000ull;
             }
             if (lane < nwords) s_xw[lane] = __uint_as_float((uint32_t)w);
             // lane l of every 16-lane row holds chunk l's record (empty beyond C)
@@ -924,12 +1080,14 @@ void fused_kernel(const FusedParams p) {
     }   // pass 1
     if (p.grad == nullptr) return;
 
-    // ---- gradient coefficients (fp32, every thread) ----
-    Coefs kf = row_coefs<TMODE, SOFTCAP>(p, r, y, s_row[0], s_row[1], s_row[2]);
+    // ---- gradient coefficients (every thread; fp64 in the fp32 instances) ----
+    using CT = typename std::conditional<HP, double, float>::type;
+    CoefsFor<HP> kf = row_coefs<TMODE, SOFTCAP, HP>(p, r, y, s_row[0], s_row[1], s_row[2]);
     if (p.row_coef != nullptr && p.w_g != 0.f) {
         // GSPO: d(loss)/d(logp_t) = -coef_t / n_seg; d logp_t / d s_j = [j == y] - q_j
         const uint32_t n_seg = p.ctrl[CTRL_NSEG];
-        const float e = n_seg > 0u ? p.grad_scale * p.k * p.w_g * p.row_coef[row] / (float)n_seg : 0.f;
+        const CT e = n_seg > 0u ? (CT)p.grad_scale * (CT)p.k * (CT)p.w_g * (CT)p.row_coef[row] / (CT)n_seg
+                                : (CT)0;
         kf.alpha += e;
         kf.beta += e;
         if (TMODE == TM_RKL) kf.c0 += e;   // there c0 multiplies q (alpha is unused); in the
@@ -937,12 +1095,12 @@ void fused_kernel(const FusedParams p) {
     }
     if (p.load_mode && p.ctrl[CTRL_ERROR] != 0u) {
         // statistics or segments are not trustworthy: make the gradient say so
-        kf.alpha = kf.beta = kf.c0 = __builtin_nanf("");
+        kf.alpha = kf.beta = kf.c0 = (CT)__builtin_nanf("");
     }
-    auto grad_elem = [&](float x, float t, float lab) -> float {
-        return grad_one<TMODE, SOFTCAP>(p, kf, x, t, lab);
+    auto grad_elem = [&](float x, float t, CT lab) -> CT {
+        return grad_one<TMODE, SOFTCAP, HP>(p, kf, x, t, lab);
     };
-    const float beta = kf.beta;
+    const CT beta = kf.beta;
 
     if (STAGE_OLD && p.accumulate && nv > 0) {
         // slots past the slice re-read its last vector (in bounds, unused)
@@ -970,28 +1128,31 @@ void fused_kernel(const FusedParams p) {
 #pragma unroll
     for (int v = 0; v < NVEC; ++v) {
         if (tid < nv - v * BLOCK) {
-            float g[VEC];
+            CT gd[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
-                g[e] = grad_elem(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, 0.f);
+                gd[e] = grad_elem(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, (CT)0);
             if (tid == yv - v * BLOCK) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     if (e == ly)
-                        g[e] = grad_elem(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, beta);
+                        gd[e] = grad_elem(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, beta);
             }
             if (p.accumulate) {
                 const u32x4 old = STAGE_OLD ? s_old[v][tid] : ld_stream(gv + v * BLOCK + tid);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) g[e] = T::get(old, e) + g[e];
+                for (int e = 0; e < VEC; ++e) gd[e] = (CT)T::get(old, e) + gd[e];
             }
+            float g[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) g[e] = (float)gd[e];   // the one rounding
             st_stream(gv + v * BLOCK + tid, T::pack(g));
         }
     }
     if (has_e) {
-        float g = grad_elem(xe, te, (int64_t)eidx == y ? beta : 0.f);
-        if (p.accumulate) g = T::load1(grow, eidx) + g;
-        T::store1(grow, eidx, g);
+        CT g = grad_elem(xe, te, (int64_t)eidx == y ? beta : (CT)0);
+        if (p.accumulate) g = (CT)T::load1(grow, eidx) + g;
+        T::store1(grow, eidx, (float)g);
     }
 }
 
@@ -1015,6 +1176,7 @@ template <typename T, int TMODE, bool SOFTCAP>
 __global__ __launch_bounds__(kRowwiseBlock) void rowwise_kernel(const FusedParams p) {
     constexpr int NW = kRowwiseBlock / 64;
     constexpr int ES = T::ESIZE;
+    constexpr bool HP = std::is_same<T, F32T>::value;
     __shared__ float s_m[NW][2];
     __shared__ float s_rec[NW][8];
     __shared__ float s_fin[8];
@@ -1070,7 +1232,7 @@ __global__ __launch_bounds__(kRowwiseBlock) void rowwise_kernel(const FusedParam
         for (int64_t j = tid; j < V; j += kRowwiseBlock) {
             const float x = T::load1(xrow, j);
             const float t = TMODE != TM_NONE ? T::load1(trow, j) : 0.f;
-            stat_term<TMODE, SOFTCAP, true>(p, M, Mt, x, t, z, sv, zt, sx, st, zs);
+            stat_term<TMODE, SOFTCAP, true, HP>(p, M, Mt, x, t, z, sv, zt, sx, st, zs);
         }
         z = wave_sum(z);
         sv = wave_sum(sv);
@@ -1115,22 +1277,24 @@ __global__ __launch_bounds__(kRowwiseBlock) void rowwise_kernel(const FusedParam
     }
     if (grow == nullptr) return;
 
-    Coefs kf = row_coefs<TMODE, SOFTCAP>(p, r, y, xy, old, adv);
+    using CT = typename std::conditional<HP, double, float>::type;
+    CoefsFor<HP> kf = row_coefs<TMODE, SOFTCAP, HP>(p, r, y, xy, old, adv);
     if (p.row_coef != nullptr && p.w_g != 0.f) {
         // GSPO: the per-token coefficient of the segment step on the label column
         const uint32_t n_seg = p.ctrl[CTRL_NSEG];
-        const float e = n_seg > 0u ? p.grad_scale * p.k * p.w_g * p.row_coef[row] / (float)n_seg : 0.f;
+        const CT e = n_seg > 0u ? (CT)p.grad_scale * (CT)p.k * (CT)p.w_g * (CT)p.row_coef[row] / (CT)n_seg
+                                : (CT)0;
         kf.alpha += e;
         kf.beta += e;
         if (TMODE == TM_RKL) kf.c0 += e;
     }
-    if (p.load_mode && p.ctrl[CTRL_ERROR] != 0u) kf.alpha = kf.beta = kf.c0 = __builtin_nanf("");
+    if (p.load_mode && p.ctrl[CTRL_ERROR] != 0u) kf.alpha = kf.beta = kf.c0 = (CT)__builtin_nanf("");
     for (int64_t j = tid; j < V; j += kRowwiseBlock) {
         const float x = T::load1(xrow, j);
         const float t = TMODE != TM_NONE ? T::load1(trow, j) : 0.f;
-        float g = grad_one<TMODE, SOFTCAP>(p, kf, x, t, j == y ? kf.beta : 0.f);
-        if (p.accumulate) g = T::load1(grow, j) + g;
-        T::store1(grow, j, g);
+        CT g = grad_one<TMODE, SOFTCAP, HP>(p, kf, x, t, j == y ? kf.beta : (CT)0);
+        if (p.accumulate) g = (CT)T::load1(grow, j) + g;
+        T::store1(grow, j, (float)g);
     }
 }
 
@@ -1163,6 +1327,7 @@ __global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const Fus
     constexpr int ES = T::ESIZE;
     constexpr int NW = kStreamBlock / 64;
     constexpr int SU = TMODE == TM_NONE ? 4 : 2;
+    constexpr bool HP = std::is_same<T, F32T>::value;
     __shared__ float s_rec[16][8];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1243,7 +1408,7 @@ __global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const Fus
                 if ((b * SU + u) * kStreamBlock + tid < nbv) {
 #pragma unroll
                     for (int e = 0; e < VEC; ++e)
-                        stat_term<TMODE, SOFTCAP, true>(p, M, Mt, T::get(xa[u], e),
+                        stat_term<TMODE, SOFTCAP, true, HP>(p, M, Mt, T::get(xa[u], e),
                                                         TMODE != TM_NONE ? T::get(ta[u], e) : 0.f,
                                                         z, sv, zt, sx, st, zs);
                 }
@@ -1256,7 +1421,7 @@ __global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const Fus
                 }
             }
         }
-        if (has_e) stat_term<TMODE, SOFTCAP, true>(p, M, Mt, xe, te, z, sv, zt, sx, st, zs);
+        if (has_e) stat_term<TMODE, SOFTCAP, true, HP>(p, M, Mt, xe, te, z, sv, zt, sx, st, zs);
     }
     auto wave_sums = [&]() {
         z = wave_sum(z);
@@ -1291,10 +1456,10 @@ __global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const Fus
             u32x4 wt = {0u, 0u, 0u, 0u};
             if (TMODE != TM_NONE) wt = tv[i];
             for (int e = 0; e < VEC; ++e)
-                stat_term<TMODE, SOFTCAP, true>(p, M, Mt, T::get(w, e), TMODE != TM_NONE ? T::get(wt, e) : 0.f,
+                stat_term<TMODE, SOFTCAP, true, HP>(p, M, Mt, T::get(w, e), TMODE != TM_NONE ? T::get(wt, e) : 0.f,
                                                 z, sv, zt, sx, st, zs);
         }
-        if (has_e) stat_term<TMODE, SOFTCAP, true>(p, M, Mt, xe, te, z, sv, zt, sx, st, zs);
+        if (has_e) stat_term<TMODE, SOFTCAP, true, HP>(p, M, Mt, xe, te, z, sv, zt, sx, st, zs);
         wave_sums();
     }
     if (lane == 0) {

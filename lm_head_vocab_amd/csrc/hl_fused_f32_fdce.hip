@@ -1,6 +1,9 @@
 // Fused-kernel instances: dtype f32, distillation mode fdce.
 #include "hl_device.cuh"
 
+// fp32 teacher slices hold at most 8 vectors per tensor (the fp64 element path
+// of the fp32 instances needs the registers; see kF32TeacherNvec).
+
 namespace hl {
 
 FusedLauncher get_fused_f32_fdce(int block, int nvec, bool softcap) {
@@ -11,11 +14,8 @@ FusedLauncher get_fused_f32_fdce(int block, int nvec, bool softcap) {
     HL_FUSED_CASE(hl::F32T, 1024, 4, hl::TM_FDCE)
     HL_FUSED_CASE(hl::F32T, 1024, 6, hl::TM_FDCE)
     HL_FUSED_CASE(hl::F32T, 1024, 8, hl::TM_FDCE)
-    HL_FUSED_CASE(hl::F32T, 1024, 10, hl::TM_FDCE)
     HL_FUSED_CASE(hl::F32T, 512, 6, hl::TM_FDCE)
     HL_FUSED_CASE(hl::F32T, 512, 8, hl::TM_FDCE)
-    HL_FUSED_CASE(hl::F32T, 512, 9, hl::TM_FDCE)
-    HL_FUSED_CASE(hl::F32T, 512, 10, hl::TM_FDCE)
     return nullptr;
 }
 

@@ -34,10 +34,14 @@ struct hl_plan_s {
     size_t ws_bytes;
     bool ws_owned;
     bool ws_stale;      // the variant changed after a caller workspace was set
-    int64_t clean_rows; // rows whose split-vocab words are known zero or this plan's (-1: none)
+    bool ws_reset;      // the next call is the plan's first on ws: its control words are undefined
+    const void* last_ws;// workspace of the last call (the plan's, or the static one)
     int64_t last_rows;
     hipEvent_t ev_before;
     hipEvent_t ev_after;
+    uint32_t spin_limit;    // bound of the split-vocab wait (polls)
+    int64_t withhold_row;   // test hook: this row's chunk withhold_chunk does not publish (-1: none)
+    int withhold_chunk;
 };
 
 namespace {
@@ -47,6 +51,15 @@ thread_local char g_last_error[256] = "";
 hl_status hip_fail(const char* where, hipError_t e) {
     std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
     return HL_ERR_HIP;
+}
+
+// hi + lo split of a positive constant: hi is the float just below v (so
+// that lo = v - hi is > 0 even when v is a float), lo the rest rounded.
+void split_pos(double v, float& hi, float& lo) {
+    float h = (float)v;
+    if ((double)h >= v) h = std::nextafterf(h, 0.0f);
+    hi = h;
+    lo = (float)(v - (double)h);
 }
 
 constexpr uint32_t kDistillBits = HL_FKL | HL_RKL | HL_FDCE;
@@ -88,10 +101,18 @@ Layout layout_for(const hl_plan_s* p, int64_t n) {
     return L;
 }
 
-int round_up_to(const int* set, int n_set, int need) {
+// The smallest entry of set that is >= need and <= cap (-1: none).
+int round_up_to(const int* set, int n_set, int need, int cap = 1 << 30) {
     for (int i = 0; i < n_set; ++i)
-        if (set[i] >= need) return set[i];
+        if (set[i] >= need && set[i] <= cap) return set[i];
     return -1;
+}
+
+// Largest slice (16-byte vectors per thread per tensor) an instance of this
+// element type and mode holds.
+int nvec_cap(hl_dtype dt, int tmode) {
+    if (dt != HL_F32 || tmode == TM_NONE) return 1 << 30;
+    return is_hinton(tmode) ? kF32HintonNvec : kF32TeacherNvec;
 }
 
 typedef FusedLauncher (*Getter)(int, int, bool);
@@ -126,6 +147,7 @@ FusedLauncher lookup(hl_dtype dt, int tmode, int block, int nvec, bool softcap) 
 // teacher, so that a 1024-thread workgroup stays within 128 VGPRs.
 Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C, int block = 0) {
     const int vec = dt == HL_F32 ? 4 : 8;
+    const int cap = nvec_cap(dt, tmode);
     int64_t nvec_row = V / vec;
     if (nvec_row < 1) nvec_row = 1;
     const int64_t per = (nvec_row + C - 1) / C;
@@ -136,17 +158,18 @@ Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C, int block = 0) {
     }
     if (block == kMidBlock) {
         const int* set = tmode == TM_NONE ? kMidNvecStudent : kMidNvecTeacher;
-        const int n_set = 4;
         const int64_t need = (per + kMidBlock - 1) / kMidBlock;
-        if (need > set[n_set - 1]) return g;
-        return Geometry{C, kMidBlock, round_up_to(set, n_set, (int)need)};
+        if (need > (1 << 20)) return g;
+        const int nv = round_up_to(set, 4, (int)need, cap);
+        return nv < 0 ? g : Geometry{C, kMidBlock, nv};
     }
     if (block != 0 && block != kLargeBlock) return g;
     const int* set = tmode == TM_NONE ? kLargeNvecStudent : kLargeNvecTeacher;
     const int n_set = tmode == TM_NONE ? 10 : 5;
     const int64_t need = (per + kLargeBlock - 1) / kLargeBlock;
-    if (need > set[n_set - 1]) return g;
-    return Geometry{C, kLargeBlock, round_up_to(set, n_set, (int)need)};
+    if (need > (1 << 20)) return g;
+    const int nv = round_up_to(set, n_set, (int)need, cap);
+    return nv < 0 ? g : Geometry{C, kLargeBlock, nv};
 }
 
 // Automatic choice: the fewest chunks per row whose slice fits the register
@@ -189,7 +212,8 @@ hl_status choose(hl_plan_s* p) {
             // gradient comes from the fused kernel in load mode, which needs
             // no exchange, with as many 1024-thread chunks as the row needs.
             const int vec = p->dtype == HL_F32 ? 4 : 8;
-            const int nmax = p->tmode == TM_NONE ? kLargeNvecStudent[9] : kLargeNvecTeacher[4];
+            int nmax = p->tmode == TM_NONE ? kLargeNvecStudent[9] : kLargeNvecTeacher[4];
+            if (nmax > nvec_cap(p->dtype, p->tmode)) nmax = nvec_cap(p->dtype, p->tmode);
             const int64_t per_chunk = (int64_t)kLargeBlock * nmax;
             const int64_t nvec_row = p->V / vec;
             const int64_t C = (nvec_row + per_chunk - 1) / per_chunk;
@@ -224,197 +248,58 @@ void invalidate_workspace(hl_plan_s* p) {
     } else {
         p->ws_stale = true;
     }
-    p->clean_rows = -1;
 }
 
 }  // namespace
 
-extern "C" {
+namespace hl {
 
-hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags,
-                  const hl_weights* weights, float temperature, float eps,
-                  float logit_scale, float softcap) {
-    if (out == nullptr) return HL_ERR_INVALID_ARG;
-    *out = nullptr;
-    if (V < 1 || weights == nullptr) return HL_ERR_INVALID_ARG;
-    if (V > kMaxRowElements) return HL_ERR_UNSUPPORTED;
-    if (dtype != HL_F32 && dtype != HL_BF16 && dtype != HL_F16) return HL_ERR_INVALID_ARG;
-    if ((loss_flags & ~kKnownBits) != 0u || (loss_flags & kLossBits) == 0u) return HL_ERR_INVALID_ARG;
-    const uint32_t dbits = loss_flags & kDistillBits;
-    if (dbits & (dbits - 1u)) return HL_ERR_INVALID_ARG;   // at most one distillation loss
-    const bool distill = dbits != 0u;
-    if ((loss_flags & HL_HINTON) && !distill) return HL_ERR_INVALID_ARG;   // the mode tempers distillation
-    if (distill && !(finite(temperature) && temperature > 0.f)) return HL_ERR_INVALID_ARG;
-    if ((loss_flags & kPolicyBits) == kPolicyBits) return HL_ERR_INVALID_ARG;   // one policy loss
-    if ((loss_flags & kPolicyBits) && !(finite(eps) && eps > 0.f && eps < 1.f)) return HL_ERR_INVALID_ARG;
-    if (!(finite(logit_scale) && logit_scale > 0.f)) return HL_ERR_INVALID_ARG;
-    if (!(finite(softcap) && softcap >= 0.f)) return HL_ERR_INVALID_ARG;
-    const hl_weights& w = *weights;
-    if (!(finite(w.ce) && finite(w.z) && finite(w.distill) && finite(w.grpo) &&
-          finite(w.grad_scale) && finite(w.divisor)))
-        return HL_ERR_INVALID_ARG;
+void set_last_error(const char* msg) { std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg); }
 
-    hl_plan_s* p = new (std::nothrow) hl_plan_s;
-    if (p == nullptr) return HL_ERR_INVALID_ARG;
-    std::memset(p, 0, sizeof(*p));
-    p->V = V;
-    p->dtype = dtype;
-    p->flags = loss_flags;
-    p->w = w;
-    p->temperature = distill ? temperature : 1.f;
-    p->eps = eps;
-    p->logit_scale = logit_scale;
-    p->softcap = softcap;
-    p->tmode = (loss_flags & HL_FKL) ? TM_FKL
-             : (loss_flags & HL_RKL) ? TM_RKL
-             : (loss_flags & HL_FDCE) ? TM_FDCE : TM_NONE;
-    if (loss_flags & HL_HINTON) p->tmode += TM_FKL_H - TM_FKL;
-    const hl_status st = choose(p);
-    if (st != HL_OK) {
-        delete p;
-        return st;
-    }
-    *out = p;
-    return HL_OK;
-}
+size_t call_workspace_bytes(hl_plan_t plan, int64_t n_rows) { return layout_for(plan, n_rows).total; }
 
-void hl_plan_destroy(hl_plan_t plan) {
-    if (plan == nullptr) return;
-    if (plan->ws_owned && plan->ws) (void)hipFree(plan->ws);
-    delete plan;
-}
-
-size_t hl_workspace_bytes(hl_plan_t plan, int64_t n_rows) {
-    if (plan == nullptr || n_rows < 0) return 0;
-    return layout_for(plan, n_rows).total;
-}
-
-hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t bytes) {
-    if (plan == nullptr || dev_workspace == nullptr) return HL_ERR_INVALID_ARG;
-    if ((reinterpret_cast<uintptr_t>(dev_workspace) & 255u) != 0) return HL_ERR_INVALID_ARG;
-    if (plan->ws_owned && plan->ws) (void)hipFree(plan->ws);
-    plan->ws = dev_workspace;
-    plan->ws_bytes = bytes;
-    plan->ws_owned = false;
-    plan->ws_stale = false;
-    plan->clean_rows = -1;
-    return HL_OK;
-}
-
-hl_status hl_plan_set_chunks(hl_plan_t plan, int chunks) {
-    if (plan == nullptr || chunks < 0 || chunks > kMaxChunks) return HL_ERR_INVALID_ARG;
-    const int prev = plan->forced_chunks, prev_b = plan->forced_block;
-    const Geometry prev_geo = plan->geo;
-    const FusedLauncher prev_fn = plan->fused;
-    plan->forced_chunks = chunks;
-    plan->forced_block = 0;
-    const hl_status st = choose(plan);
-    if (st != HL_OK) {
-        plan->forced_chunks = prev;
-        plan->forced_block = prev_b;
-        plan->geo = prev_geo;
-        plan->fused = prev_fn;
-    } else {
-        invalidate_workspace(plan);
-    }
-    return st;
-}
-
-hl_status hl_plan_set_variant(hl_plan_t plan, int chunks, int block) {
-    if (plan == nullptr || chunks < 0 || chunks > kMaxChunks) return HL_ERR_INVALID_ARG;
-    if (block != 0 && block != kSmallBlock && block != kMidBlock && block != kLargeBlock) return HL_ERR_INVALID_ARG;
-    if (block != 0 && chunks == 0) return HL_ERR_INVALID_ARG;
-    const int prev_c = plan->forced_chunks, prev_b = plan->forced_block;
-    const Geometry prev_geo = plan->geo;
-    const FusedLauncher prev_fn = plan->fused;
-    plan->forced_chunks = chunks;
-    plan->forced_block = block;
-    const hl_status st = choose(plan);
-    if (st != HL_OK) {
-        plan->forced_chunks = prev_c;
-        plan->forced_block = prev_b;
-        plan->geo = prev_geo;
-        plan->fused = prev_fn;
-    } else {
-        invalidate_workspace(plan);
-    }
-    return st;
-}
-
-hl_status hl_plan_describe(hl_plan_t plan, int* chunks, int* block, int* vec_per_thread) {
-    if (plan == nullptr) return HL_ERR_INVALID_ARG;
-    if (chunks) *chunks = plan->geo.chunks;
-    if (block) *block = plan->geo.block;
-    if (vec_per_thread) *vec_per_thread = plan->geo.nvec;
-    return HL_OK;
-}
-
-hl_status hl_plan_set_timing_events(hl_plan_t plan, hipEvent_t before, hipEvent_t after) {
-    if (plan == nullptr) return HL_ERR_INVALID_ARG;
-    plan->ev_before = before;
-    plan->ev_after = after;
-    return HL_OK;
-}
-
-const float* hl_row_values(hl_plan_t plan) {
-    if (plan == nullptr || plan->ws == nullptr) return nullptr;
-    const Layout L = layout_for(plan, plan->last_rows);
-    return reinterpret_cast<const float*>(static_cast<const char*>(plan->ws) + L.rows);
-}
-
-hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits,
-                              const int64_t* labels, const uint8_t* mask,
-                              const void* teacher_logits, const float* old_logprobs,
-                              const float* advantages, void* grad_out,
-                              float* scalars_out, hipStream_t stream) {
-    return hl_forward_backward_segments(plan, n_rows, logits, labels, mask, teacher_logits, old_logprobs,
-                                        advantages, nullptr, 0, grad_out, scalars_out, stream);
-}
-
-hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const void* logits,
-                                       const int64_t* labels, const uint8_t* mask,
-                                       const void* teacher_logits, const float* old_logprobs,
-                                       const float* advantages, const int32_t* seq_offsets,
-                                       int64_t n_segments, void* grad_out,
-                                       float* scalars_out, hipStream_t stream) {
-    if (plan == nullptr || n_rows < 0 || scalars_out == nullptr) return HL_ERR_INVALID_ARG;
-    if (n_rows > 0 && logits == nullptr) return HL_ERR_INVALID_ARG;
+hl_status check_call(hl_plan_t plan, const CallArgs& a) {
+    if (plan == nullptr || a.n_rows < 0 || a.scalars == nullptr) return HL_ERR_INVALID_ARG;
+    const int64_t n_rows = a.n_rows;
+    if (n_rows > 0 && a.logits == nullptr) return HL_ERR_INVALID_ARG;
     const uint32_t f = plan->flags;
-    const bool gspo = (f & HL_GSPO) != 0u;
-    if (gspo) {
-        if (n_rows > 0 && seq_offsets == nullptr) return HL_ERR_MISSING_INPUT;
-        if (n_segments < 0 || n_segments > n_rows || (n_rows > 0 && n_segments < 1)) return HL_ERR_INVALID_ARG;
+    if (f & HL_GSPO) {
+        if (n_rows > 0 && a.seq_offsets == nullptr) return HL_ERR_MISSING_INPUT;
+        if (a.n_segments < 0 || a.n_segments > n_rows || (n_rows > 0 && a.n_segments < 1)) return HL_ERR_INVALID_ARG;
     }
     if (n_rows > 0) {
-        if ((f & (HL_CE | kPolicyBits)) && labels == nullptr) return HL_ERR_MISSING_INPUT;
-        if ((f & kDistillBits) && teacher_logits == nullptr) return HL_ERR_MISSING_INPUT;
-        if ((f & kPolicyBits) && (old_logprobs == nullptr || advantages == nullptr)) return HL_ERR_MISSING_INPUT;
+        if ((f & (HL_CE | kPolicyBits)) && a.labels == nullptr) return HL_ERR_MISSING_INPUT;
+        if ((f & kDistillBits) && a.teacher == nullptr) return HL_ERR_MISSING_INPUT;
+        if ((f & kPolicyBits) && (a.old_logprobs == nullptr || a.advantages == nullptr)) return HL_ERR_MISSING_INPUT;
         const size_t es = elem_size(plan->dtype);
-        if (!elem_aligned(logits, es)) return HL_ERR_INVALID_ARG;
-        if (plan->tmode != TM_NONE && !elem_aligned(teacher_logits, es)) return HL_ERR_INVALID_ARG;
-        if (grad_out != nullptr && !elem_aligned(grad_out, es)) return HL_ERR_INVALID_ARG;
+        if (!elem_aligned(a.logits, es)) return HL_ERR_INVALID_ARG;
+        if (plan->tmode != TM_NONE && !elem_aligned(a.teacher, es)) return HL_ERR_INVALID_ARG;
+        if (a.grad != nullptr && !elem_aligned(a.grad, es)) return HL_ERR_INVALID_ARG;
         if ((uint64_t)(n_rows + 7) * (uint64_t)plan->geo.chunks > 0x7fffffffull) return HL_ERR_UNSUPPORTED;
     }
+    return HL_OK;
+}
 
+// Enqueue the kernels of a checked call on the workspace `wsv` (at least
+// call_workspace_bytes(plan, n_rows), 256-byte aligned).
+hl_status enqueue_call(hl_plan_t plan, const CallArgs& a, void* wsv, bool reset, hipStream_t stream) {
+    const int64_t n_rows = a.n_rows;
+    const void* logits = a.logits;
+    const int64_t* labels = a.labels;
+    const uint8_t* mask = a.mask;
+    const void* teacher_logits = a.teacher;
+    const float* old_logprobs = a.old_logprobs;
+    const float* advantages = a.advantages;
+    const int32_t* seq_offsets = a.seq_offsets;
+    const int64_t n_segments = a.n_segments;
+    void* grad_out = a.grad;
+    float* scalars_out = a.scalars;
+    const uint32_t f = plan->flags;
+    const bool gspo = (f & HL_GSPO) != 0u;
     const Layout L = layout_for(plan, n_rows);
-    if (plan->ws_stale) return HL_ERR_WORKSPACE;
-    if (plan->ws == nullptr || plan->ws_bytes < L.total) {
-        if (plan->ws != nullptr && !plan->ws_owned) return HL_ERR_WORKSPACE;
-        if (plan->ws_owned && plan->ws) {
-            (void)hipFree(plan->ws);
-            plan->ws = nullptr;
-            plan->ws_bytes = 0;
-        }
-        void* mem = nullptr;
-        hipError_t me = hipMalloc(&mem, L.total);
-        if (me != hipSuccess) return hip_fail("hipMalloc(workspace)", me);
-        plan->ws = mem;
-        plan->ws_bytes = L.total;
-        plan->ws_owned = true;
-        plan->clean_rows = -1;
-    }
+    plan->last_ws = wsv;
     plan->last_rows = n_rows;
-    char* ws = static_cast<char*>(plan->ws);
+    char* ws = static_cast<char*>(wsv);
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
     uint64_t* chunk_words = reinterpret_cast<uint64_t*>(ws + L.chunk_rec);
     float* row_rec = reinterpret_cast<float*>(ws + L.row_rec);
@@ -428,12 +313,13 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
     cp.ctrl = ctrl;
     cp.n_rows = n_rows;
     cp.V = plan->V;
-    // The split-vocab words of rows [0, clean_rows) hold zeros or this plan's
-    // own records (older epochs). Anything else (a new workspace, or a region
-    // another call's layout used for other data) is zero-filled by the count
-    // kernel first, and the epoch restarts.
-    const bool fresh = CX > 1 && plan->clean_rows < n_rows;
-    cp.fresh = fresh ? 1 : 0;
+    // The count kernel bumps the workspace's epoch and zero-fills this call's
+    // split-vocab words where the workspace may hold anything but such words
+    // (its control words decide; `reset` when they are undefined).
+    cp.reset = reset ? 1 : 0;
+    cp.spin_limit = plan->spin_limit;
+    cp.hold_row = plan->withhold_row < 0 ? 0xffffffffu : (uint32_t)plan->withhold_row;
+    cp.hold_chunk = plan->withhold_row < 0 ? 0xffffffffu : (uint32_t)plan->withhold_chunk;
     cp.vec = (labels != nullptr && aligned16(labels) && (mask == nullptr || aligned16(mask))) ? 1 : 0;
     cp.fill = chunk_words;
     cp.fill_words = CX > 1 ? n_rows * CX * XWORDS : 0;
@@ -462,11 +348,16 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
         fp.rows_per_xcd = (int)((n_rows + 7) / 8);
         fp.accumulate = (f & HL_ACCUMULATE) ? 1 : 0;
         fp.flags = f;
-        const float log2e = 1.44269504088896340736f;
+        constexpr double kLog2eD = 1.4426950408889634074;
         fp.k = plan->logit_scale;
-        fp.K1 = plan->logit_scale * log2e;
-        fp.K2 = log2e / plan->temperature;
-        fp.beta = (f & HL_HINTON) ? 1.0f / plan->temperature : 1.0f;
+        split_pos((double)plan->logit_scale * kLog2eD, fp.K1, fp.K1l);
+        split_pos(kLog2eD / (double)plan->temperature, fp.K2, fp.K2l);
+        if (f & HL_HINTON) {
+            split_pos(1.0 / (double)plan->temperature, fp.beta, fp.beta_l);
+        } else {
+            fp.beta = 1.0f;
+            fp.beta_l = 0.0f;
+        }
         fp.tau = plan->temperature;
         fp.cap = plan->softcap;
         fp.kc = plan->softcap > 0.f ? plan->logit_scale / plan->softcap : 0.f;
@@ -568,9 +459,195 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
     rp.divisor = plan->w.divisor;
     e = launch_reduce(rp, stream);
     if (e != hipSuccess) return hip_fail("reduce kernel launch", e);
-    // this call's other regions may have written past its own record region
-    plan->clean_rows = fresh ? n_rows : (plan->clean_rows < n_rows ? plan->clean_rows : n_rows);
     return HL_OK;
+}
+
+}  // namespace hl
+
+extern "C" {
+
+hl_status hl_plan(hl_plan_t* out, int64_t V, hl_dtype dtype, uint32_t loss_flags,
+                  const hl_weights* weights, float temperature, float eps,
+                  float logit_scale, float softcap) {
+    if (out == nullptr) return HL_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (V < 1 || weights == nullptr) return HL_ERR_INVALID_ARG;
+    if (V > kMaxRowElements) return HL_ERR_UNSUPPORTED;
+    if (dtype != HL_F32 && dtype != HL_BF16 && dtype != HL_F16) return HL_ERR_INVALID_ARG;
+    if ((loss_flags & ~kKnownBits) != 0u || (loss_flags & kLossBits) == 0u) return HL_ERR_INVALID_ARG;
+    const uint32_t dbits = loss_flags & kDistillBits;
+    if (dbits & (dbits - 1u)) return HL_ERR_INVALID_ARG;   // at most one distillation loss
+    const bool distill = dbits != 0u;
+    if ((loss_flags & HL_HINTON) && !distill) return HL_ERR_INVALID_ARG;   // the mode tempers distillation
+    if (distill && !(finite(temperature) && temperature > 0.f)) return HL_ERR_INVALID_ARG;
+    if ((loss_flags & kPolicyBits) == kPolicyBits) return HL_ERR_INVALID_ARG;   // one policy loss
+    if ((loss_flags & kPolicyBits) && !(finite(eps) && eps > 0.f && eps < 1.f)) return HL_ERR_INVALID_ARG;
+    if (!(finite(logit_scale) && logit_scale > 0.f)) return HL_ERR_INVALID_ARG;
+    if (!(finite(softcap) && softcap >= 0.f)) return HL_ERR_INVALID_ARG;
+    const hl_weights& w = *weights;
+    if (!(finite(w.ce) && finite(w.z) && finite(w.distill) && finite(w.grpo) &&
+          finite(w.grad_scale) && finite(w.divisor)))
+        return HL_ERR_INVALID_ARG;
+
+    hl_plan_s* p = new (std::nothrow) hl_plan_s;
+    if (p == nullptr) return HL_ERR_INVALID_ARG;
+    std::memset(p, 0, sizeof(*p));
+    p->V = V;
+    p->dtype = dtype;
+    p->flags = loss_flags;
+    p->w = w;
+    p->temperature = distill ? temperature : 1.f;
+    p->eps = eps;
+    p->logit_scale = logit_scale;
+    p->softcap = softcap;
+    p->spin_limit = kSpinLimit;
+    p->withhold_row = -1;
+    p->withhold_chunk = -1;
+    p->tmode = (loss_flags & HL_FKL) ? TM_FKL
+             : (loss_flags & HL_RKL) ? TM_RKL
+             : (loss_flags & HL_FDCE) ? TM_FDCE : TM_NONE;
+    if (loss_flags & HL_HINTON) p->tmode += TM_FKL_H - TM_FKL;
+    const hl_status st = choose(p);
+    if (st != HL_OK) {
+        delete p;
+        return st;
+    }
+    *out = p;
+    return HL_OK;
+}
+
+void hl_plan_destroy(hl_plan_t plan) {
+    if (plan == nullptr) return;
+    if (plan->ws_owned && plan->ws) (void)hipFree(plan->ws);
+    delete plan;
+}
+
+size_t hl_workspace_bytes(hl_plan_t plan, int64_t n_rows) {
+    if (plan == nullptr || n_rows < 0) return 0;
+    return layout_for(plan, n_rows).total;
+}
+
+hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t bytes) {
+    if (plan == nullptr || dev_workspace == nullptr) return HL_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(dev_workspace) & 255u) != 0) return HL_ERR_INVALID_ARG;
+    if (plan->ws_owned && plan->ws) (void)hipFree(plan->ws);
+    plan->ws = dev_workspace;
+    plan->ws_bytes = bytes;
+    plan->ws_owned = false;
+    plan->ws_stale = false;
+    plan->ws_reset = true;
+    return HL_OK;
+}
+
+hl_status hl_plan_set_chunks(hl_plan_t plan, int chunks) {
+    if (plan == nullptr || chunks < 0 || chunks > kMaxChunks) return HL_ERR_INVALID_ARG;
+    const int prev = plan->forced_chunks, prev_b = plan->forced_block;
+    const Geometry prev_geo = plan->geo;
+    const FusedLauncher prev_fn = plan->fused;
+    plan->forced_chunks = chunks;
+    plan->forced_block = 0;
+    const hl_status st = choose(plan);
+    if (st != HL_OK) {
+        plan->forced_chunks = prev;
+        plan->forced_block = prev_b;
+        plan->geo = prev_geo;
+        plan->fused = prev_fn;
+    } else {
+        invalidate_workspace(plan);
+    }
+    return st;
+}
+
+hl_status hl_plan_set_variant(hl_plan_t plan, int chunks, int block) {
+    if (plan == nullptr || chunks < 0 || chunks > kMaxChunks) return HL_ERR_INVALID_ARG;
+    if (block != 0 && block != kSmallBlock && block != kMidBlock && block != kLargeBlock) return HL_ERR_INVALID_ARG;
+    if (block != 0 && chunks == 0) return HL_ERR_INVALID_ARG;
+    const int prev_c = plan->forced_chunks, prev_b = plan->forced_block;
+    const Geometry prev_geo = plan->geo;
+    const FusedLauncher prev_fn = plan->fused;
+    plan->forced_chunks = chunks;
+    plan->forced_block = block;
+    const hl_status st = choose(plan);
+    if (st != HL_OK) {
+        plan->forced_chunks = prev_c;
+        plan->forced_block = prev_b;
+        plan->geo = prev_geo;
+        plan->fused = prev_fn;
+    } else {
+        invalidate_workspace(plan);
+    }
+    return st;
+}
+
+hl_status hl_plan_describe(hl_plan_t plan, int* chunks, int* block, int* vec_per_thread) {
+    if (plan == nullptr) return HL_ERR_INVALID_ARG;
+    if (chunks) *chunks = plan->geo.chunks;
+    if (block) *block = plan->geo.block;
+    if (vec_per_thread) *vec_per_thread = plan->geo.nvec;
+    return HL_OK;
+}
+
+hl_status hl_plan_set_timing_events(hl_plan_t plan, hipEvent_t before, hipEvent_t after) {
+    if (plan == nullptr) return HL_ERR_INVALID_ARG;
+    plan->ev_before = before;
+    plan->ev_after = after;
+    return HL_OK;
+}
+
+hl_status hl_plan_set_exchange_test(hl_plan_t plan, uint32_t spin_limit, int64_t withhold_row,
+                                    int withhold_chunk) {
+    if (plan == nullptr || spin_limit < 1 || withhold_row >= 0xffffffffLL) return HL_ERR_INVALID_ARG;
+    plan->spin_limit = spin_limit;
+    plan->withhold_row = withhold_row < 0 ? -1 : withhold_row;
+    plan->withhold_chunk = withhold_row < 0 ? -1 : withhold_chunk;
+    return HL_OK;
+}
+
+const float* hl_row_values(hl_plan_t plan) {
+    if (plan == nullptr || plan->last_ws == nullptr) return nullptr;
+    const Layout L = layout_for(plan, plan->last_rows);
+    return reinterpret_cast<const float*>(static_cast<const char*>(plan->last_ws) + L.rows);
+}
+
+hl_status hl_forward_backward(hl_plan_t plan, int64_t n_rows, const void* logits,
+                              const int64_t* labels, const uint8_t* mask,
+                              const void* teacher_logits, const float* old_logprobs,
+                              const float* advantages, void* grad_out,
+                              float* scalars_out, hipStream_t stream) {
+    return hl_forward_backward_segments(plan, n_rows, logits, labels, mask, teacher_logits, old_logprobs,
+                                        advantages, nullptr, 0, grad_out, scalars_out, stream);
+}
+
+hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const void* logits,
+                                       const int64_t* labels, const uint8_t* mask,
+                                       const void* teacher_logits, const float* old_logprobs,
+                                       const float* advantages, const int32_t* seq_offsets,
+                                       int64_t n_segments, void* grad_out,
+                                       float* scalars_out, hipStream_t stream) {
+    const CallArgs a{n_rows, logits, labels, mask, teacher_logits, old_logprobs, advantages,
+                     seq_offsets, n_segments, grad_out, scalars_out};
+    hl_status st = check_call(plan, a);
+    if (st != HL_OK) return st;
+    const size_t need = call_workspace_bytes(plan, n_rows);
+    if (plan->ws_stale) return HL_ERR_WORKSPACE;
+    if (plan->ws == nullptr || plan->ws_bytes < need) {
+        if (plan->ws != nullptr && !plan->ws_owned) return HL_ERR_WORKSPACE;
+        if (plan->ws_owned && plan->ws) {
+            (void)hipFree(plan->ws);
+            plan->ws = nullptr;
+            plan->ws_bytes = 0;
+        }
+        void* mem = nullptr;
+        hipError_t me = hipMalloc(&mem, need);
+        if (me != hipSuccess) return hip_fail("hipMalloc(workspace)", me);
+        plan->ws = mem;
+        plan->ws_bytes = need;
+        plan->ws_owned = true;
+        plan->ws_reset = true;
+    }
+    st = enqueue_call(plan, a, plan->ws, plan->ws_reset, stream);
+    if (st == HL_OK) plan->ws_reset = false;
+    return st;
 }
 
 const char* hl_last_error(void) { return g_last_error; }

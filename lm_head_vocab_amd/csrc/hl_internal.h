@@ -49,9 +49,17 @@ enum RecField : int { R_M = 0, R_Z, R_S, R_MT, R_ZT, R_SX, R_ST, R_XY, R_VALID, 
 
 // Control words at the start of the workspace. CTRL_NSEG counts the GSPO
 // segments that hold a valid row. CTRL_ERROR: 1 = a split-vocab row never saw
-// all of its chunks, 2 = malformed segment offsets.
+// all of its chunks, 2 = malformed segment offsets. CTRL_EPOCH tags the
+// split-vocab words of the current call; CTRL_CLEAN_LO/HI (a 64-bit count)
+// is how many leading split-vocab words are known to hold zeros or words of
+// earlier epochs (both belong to the workspace, whichever plan calls).
+// CTRL_SPIN, CTRL_HOLD_ROW, CTRL_HOLD_CHUNK: the bound of the split-vocab
+// wait and the test hook of a withheld chunk, written by the count kernel
+// and read by the exchange where it needs them (as kernel arguments they
+// would stay live in scalar registers through the whole fused kernel).
 enum Ctrl : int {
     CTRL_NVALID = 0, CTRL_NBAD = 1, CTRL_EPOCH = 2, CTRL_ERROR = 3, CTRL_DONE = 4, CTRL_NSEG = 5,
+    CTRL_CLEAN_LO = 6, CTRL_CLEAN_HI = 7, CTRL_SPIN = 8, CTRL_HOLD_ROW = 9, CTRL_HOLD_CHUNK = 10,
     NCTRL = 64
 };
 
@@ -94,9 +102,13 @@ struct FusedParams {
     int accumulate;
     uint32_t flags;
     float k;          // logit scale
-    float K1;         // k * log2(e)
-    float K2;         // log2(e) / temperature
+    float K1;         // k * log2(e), rounded toward zero
+    float K2;         // log2(e) / temperature, rounded toward zero
     float beta;       // 1 / temperature for the tempered distillation student (Hinton modes), else 1
+    // Low parts (fp32 instances): K1 + K1l, K2 + K2l and beta + beta_l are the
+    // constants to about 2^-48 relative; every low part is > 0, so a -Inf
+    // logit still gives a -Inf exponent (never -Inf + Inf).
+    float K1l, K2l, beta_l;
     float tau;        // temperature (the Hinton gradient carries tau)
     float cap;        // softcap c (0 = off)
     float kc;         // k / c
@@ -108,18 +120,28 @@ struct FusedParams {
     float eps;
 };
 
+// Default bound of the split-vocab wait, in polls.
+constexpr uint32_t kSpinLimit = 1u << 20;
+
 struct CountParams {
     const int64_t* labels;
     const uint8_t* mask;
     uint32_t* ctrl;
     int64_t n_rows;
     int64_t V;
-    // First call on a new workspace: every workgroup zero-fills its stripe of
-    // the split-vocab words and workgroup 0 restarts the epoch at 1.
-    int fresh;
-    uint64_t* fill;
-    int64_t fill_words;
+    // First call of a plan on a workspace: its control words may hold
+    // anything, so the epoch restarts at 1 and the call's split-vocab words
+    // are zero-filled whatever CTRL_CLEAN says.
+    int reset;
+    uint64_t* fill;        // the call's split-vocab words
+    int64_t fill_words;    // their number (0 without a chunk exchange); even
     int vec;   // labels (and mask, if any) 16-byte aligned: the tiled load path
+    // Bounded wait of the split-vocab exchange (polls), and a test hook: the
+    // chunk hold_chunk of row hold_row does not publish its statistics
+    // (hold_row 0xffffffff: none), so that every chunk of that row gives up.
+    uint32_t spin_limit;
+    uint32_t hold_row;
+    uint32_t hold_chunk;
 };
 
 constexpr int kReduceBlock = 256;   // rows per reduction workgroup
@@ -195,9 +217,37 @@ FusedLauncher get_stream_f32(int tmode, bool softcap);
 FusedLauncher get_stream_bf16(int tmode, bool softcap);
 FusedLauncher get_stream_f16(int tmode, bool softcap);
 
-hipError_t launch_count(const CountParams& p, hipStream_t s);  // grid grows when p.fresh
+hipError_t launch_count(const CountParams& p, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_seam(const SeamParams& p, hipStream_t s);
+
+}  // namespace hl
+
+#include "headloss.h"
+
+namespace hl {
+
+// Host side (hl_host.cpp): one call's arguments (those of
+// hl_forward_backward_segments), its checks, its workspace size, and the
+// enqueue of its kernels on a given workspace. `reset`: the workspace's
+// control words are undefined (a plan's first call on it).
+struct CallArgs {
+    int64_t n_rows;
+    const void* logits;
+    const int64_t* labels;
+    const uint8_t* mask;
+    const void* teacher;
+    const float* old_logprobs;
+    const float* advantages;
+    const int32_t* seq_offsets;
+    int64_t n_segments;
+    void* grad;
+    float* scalars;
+};
+hl_status check_call(hl_plan_t plan, const CallArgs& a);
+size_t call_workspace_bytes(hl_plan_t plan, int64_t n_rows);
+hl_status enqueue_call(hl_plan_t plan, const CallArgs& a, void* ws, bool reset, hipStream_t stream);
+void set_last_error(const char* msg);
 
 // Threads per workgroup of the row-wise kernel (one workgroup per row).
 constexpr int kRowwiseBlock = 256;
@@ -213,5 +263,10 @@ constexpr int kMidNvecStudent[] = {10, 12, 16, 20};
 constexpr int kMidNvecTeacher[] = {6, 8, 9, 10};
 constexpr int kLargeNvecStudent[] = {2, 4, 6, 8, 10, 12, 14, 16, 18, 20};
 constexpr int kLargeNvecTeacher[] = {2, 4, 6, 8, 10};
+// fp32 slices with a teacher hold at most this many vectors per tensor (the
+// fp64 element path of the fp32 instances needs the registers): 8, or 4 in
+// the Hinton modes (three exponentials per element).
+constexpr int kF32TeacherNvec = 8;
+constexpr int kF32HintonNvec = 4;
 
 }  // namespace hl

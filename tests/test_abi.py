@@ -260,3 +260,46 @@ def test_binding_marshalling_errors_without_gpu():
         hl.Plan(64, torch.bfloat16, hl.FKL | hl.RKL)
     with pytest.raises(ValueError):
         hl.Plan(64, torch.int8, hl.CE)
+
+
+def test_layout_without_an_instance_is_refused_and_the_plan_kept():
+    # 6 chunks of 256 threads x 4 vectors hold 49152 bf16 elements: no instance serves V = 60013
+    st, h = _plan(V=60013, flags=hl.CE | hl.ZLOSS)
+    assert st == 0
+    c, b = ctypes.c_int(), ctypes.c_int()
+    lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), None)
+    before = (c.value, b.value)
+    assert lib.hl_plan_set_variant(h, 6, 256) == hl.HL_ERR_UNSUPPORTED
+    lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), None)
+    assert (c.value, b.value) == before
+    assert lib.hl_plan_set_variant(h, 8, 256) == hl.HL_OK
+    lib.hl_plan_destroy(h)
+
+
+def test_fp32_teacher_slices_respect_their_register_cap():
+    # fp32 instances evaluate gradient elements in fp64: teacher slices hold at
+    # most 8 vectors per tensor, 4 in the Hinton modes
+    for extra, cap in ((0, 8), (hl.HINTON, 4)):
+        for V in (20011, 60000, 151936, 300007):
+            st, h = _plan(V=V, flags=hl.CE | hl.FKL | extra, dtype=hl.HL_F32, w=Weights(1, 0, 1, 0, 1, 0), tau=2.0)
+            assert st == 0, (V, extra)
+            n = ctypes.c_int()
+            assert lib.hl_plan_describe(h, None, None, ctypes.byref(n)) == 0
+            assert n.value <= cap, (V, extra, n.value)
+            for chunks in range(1, 10):
+                if lib.hl_plan_set_chunks(h, chunks) == hl.HL_OK:
+                    lib.hl_plan_describe(h, None, None, ctypes.byref(n))
+                    assert n.value <= cap, (V, extra, chunks, n.value)
+            lib.hl_plan_destroy(h)
+
+
+def test_exchange_test_hook_arguments():
+    st, h = _plan(V=20000, flags=hl.CE | hl.RKL, w=Weights(1, 0, 1, 0, 1, 0))
+    assert st == 0
+    hook = lib.hl_plan_set_exchange_test
+    assert hook(None, 64, 0, 0) == hl.HL_ERR_INVALID_ARG
+    assert hook(h, 0, 0, 0) == hl.HL_ERR_INVALID_ARG            # the wait needs at least one poll
+    assert hook(h, 64, 1 << 32, 0) == hl.HL_ERR_INVALID_ARG     # rows are 32-bit there
+    assert hook(h, 64, 3, 1) == hl.HL_OK
+    assert hook(h, 1 << 20, -1, -1) == hl.HL_OK                  # back to the default
+    lib.hl_plan_destroy(h)

@@ -113,7 +113,8 @@ def test_unaligned_bases_match_the_oracle(case, layout):
                              to_np(inp.get("old_logprobs")), to_np(inp.get("advantages")))
     valid, _ = oracle.row_validity(N, V, y, to_np(inp["mask"]))
     boundary = _grpo_boundary_rows(spec, inp) & valid
-    assert_scalars(spec, sc, ref_sc, dtype, vals, valid, skip=("CLIPFRAC",) if boundary.any() else ())
+    assert_scalars(spec, sc, ref_sc, dtype, vals, valid, skip=("CLIPFRAC",) if boundary.any() else (),
+                   x=to_np(inp["logits"]))
     gk = g.detach().cpu()
     keep = ~boundary
     grad_check(gk[torch.from_numpy(keep)], ref_g[keep], dtype, labels=y[keep])

@@ -132,7 +132,7 @@ def _check(spec, inp, dtype, chunks=0, grad_mode=None):
     sc, g = _run(plan, inp, grad_mode)
     ref_sc, ref_g, vals, valid, seam = _oracle(spec, inp, want_grad=grad_mode != "none")
     boundary, any_boundary = _boundary_rows(spec, seam, valid) if N else (np.zeros(0, bool), False)
-    assert_scalars(spec, sc, ref_sc, dtype, _scalar_vals(vals, seam) if N else None, valid,
+    assert_scalars(spec, sc, ref_sc, dtype, _scalar_vals(vals, seam) if N else None, valid, x=to_np(inp["logits"]),
                    skip=("CLIPFRAC",) if any_boundary else ())
     if not any_boundary:
         ns = seam["n_seg"]

@@ -92,7 +92,7 @@ def _to_dev(inp):
     return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
 
 
-def _check_small(spec, inp, dtype, chunks=0, grad_mode=None, f32_abs=None, skip_scalars=()):
+def _check_small(spec, inp, dtype, chunks=0, grad_mode=None, skip_scalars=()):
     grad_mode = grad_mode or ("accumulate" if spec.has(ACC) else "overwrite")
     plan = make_plan(spec, TDT[dtype], chunks)
     say(f"[gpu] N={inp['logits'].shape[0]} V={spec.V} {dtype} flags={spec.flags:#x} "
@@ -107,7 +107,7 @@ def _check_small(spec, inp, dtype, chunks=0, grad_mode=None, f32_abs=None, skip_
                                    to_np(inp["mask"]))
     boundary = _grpo_boundary_rows(spec, inp) & valid
     assert_scalars(spec, sc, ref_sc, dtype, vals, valid,
-                   skip=tuple(skip_scalars) + (("CLIPFRAC",) if boundary.any() else ()))
+                   skip=tuple(skip_scalars) + (("CLIPFRAC",) if boundary.any() else ()), x=to_np(inp["logits"]))
     if spec.has(GRPO) and not boundary.any():
         n = ref_sc[SLOT["N_VALID"]] if spec.divisor <= 0 else spec.divisor
         assert round(sc[SLOT["CLIPFRAC"]] * n) == round(ref_sc[SLOT["CLIPFRAC"]] * n)
@@ -116,8 +116,7 @@ def _check_small(spec, inp, dtype, chunks=0, grad_mode=None, f32_abs=None, skip_
     gk = g.detach().cpu()
     keep = ~boundary
     metrics = grad_check(gk[torch.from_numpy(keep)], ref_g[keep], dtype,
-                         labels=to_np(inp["labels"])[keep] if inp["labels"] is not None else None,
-                         f32_abs=f32_abs)
+                         labels=to_np(inp["labels"])[keep] if inp["labels"] is not None else None)
     # masked rows: +0.0 in overwrite mode, bit-identical existing values in accumulate mode
     inval = torch.from_numpy(~valid)
     if grad_mode == "overwrite":
@@ -205,8 +204,11 @@ def test_forward_only_streaming(dtype, combo, shape):
 @pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "all_fkl", "ce_fkl", "all_fdce"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_split_vocab_variant(dtype, combo, chunks):
-    # forced chunking exercises the cross-workgroup combine at small sizes
-    for V, N in ((20011, 7), (70000, 5)):
+    # forced chunking exercises the cross-workgroup combine at small sizes;
+    # fp32 teacher slices hold at most 8 vectors per tensor, so the wider
+    # fp32 rows are 60000 elements (two chunks of 1024 x 8 x 4)
+    wide = 60000 if dtype == "f32" else 70000
+    for V, N in ((20011, 7), (wide, 5)):
         spec, inp = _small(dtype, combo, N, V, seed=chunks * 100 + N, softcap=15.0, scale=0.8)
         _check_small(spec, inp, dtype, chunks=chunks)
 
@@ -224,18 +226,16 @@ def test_split_vocab_short_rows(dtype, combo, V, chunks):
     _check_small(spec, inp, dtype, chunks=chunks)
 
 
-@pytest.mark.parametrize("variant", [(2, 512), (4, 512), (3, 1024), (1, 1024), (6, 256)])
+@pytest.mark.parametrize("variant", [(2, 512), (4, 512), (3, 1024), (1, 1024), (8, 256)])
 @pytest.mark.parametrize("combo", ["ce_z", "all_rkl", "grpo_z_ent", "ce_fkl"])
 def test_forced_variants(combo, variant):
-    """Every (chunks, threads per workgroup) layout gives the same answer."""
+    """Every (chunks, threads per workgroup) layout gives the same answer
+    (each of these layouts has an instance at V = 60013; a layout without
+    one is refused on the host, tested in test_abi)."""
     chunks, block = variant
     spec, inp = _small("bf16", combo, 6, 60013, seed=31 + chunks, softcap=12.0, scale=0.9, mask_frac=0.2)
     plan = make_plan(spec, torch.bfloat16)
-    try:
-        plan.set_variant(chunks, block)
-    except hl.HeadLossError as e:
-        assert e.status == hl.HL_ERR_UNSUPPORTED
-        pytest.skip(f"no instance for {variant} at V={spec.V}")
+    plan.set_variant(chunks, block)
     say(f"[gpu] variant {variant} -> {plan.describe()}")
     sc, g = run_hip(plan, _to_dev(inp), "overwrite")
     ref_sc, ref_g, _ = run_oracle(spec, inp)
@@ -326,8 +326,11 @@ def test_split_vocab_accumulate_and_masking():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_hinton_split_vocab_and_temperatures(dtype, combo, chunks, tau):
     """The tempered student sums travel through the split-vocab exchange (up
-    to 8 chunks, the cap of the 8-statistic from-distribution mode)."""
-    for V, N in ((20011, 7), (70000, 5)):
+    to 8 chunks, the cap of the 8-statistic from-distribution mode). fp32
+    Hinton slices hold at most 4 vectors per tensor: the wider fp32 rows are
+    30011 elements (two chunks of 1024 x 4 x 4)."""
+    wide = 30011 if dtype == "f32" else 70000
+    for V, N in ((20011, 7), (wide, 5)):
         spec, inp = _small(dtype, combo, N, V, seed=chunks * 10 + N, softcap=15.0, scale=0.8,
                            temperature=tau, mask_frac=0.2)
         _check_small(spec, inp, dtype, chunks=chunks)
@@ -383,11 +386,9 @@ def test_outlier_logits(dtype, combo, chunks, mode):
         inp["teacher"] = t.to(TDT[dtype])
     if spec.has(GRPO):
         inp["old_logprobs"] = oracle_old_logprobs(spec, inp["logits"], inp["labels"], inp["old_noise"])
-    # fp32: the exponent argument x k log2(e) - lse2 is a difference of two
-    # numbers near |x k log2 e|, so its rounding error (about 2 ulps of that
-    # magnitude) makes each softmax entry's relative error up to
-    # 2 ln2 |x k log2 e| 2^-24; the absolute gate scales with it and with the
-    # largest gradient entry (1e-6 is the gate for ordinary logit ranges)
+    # fp32 gradient: the plain 1e-6 absolute gate (the fp32 instances carry
+    # k log2(e) and the log-partitions as hi + lo pairs and shift by the exact
+    # wave maxima, so an outlier's exponent keeps its low bits).
     #
     # Entropy: these rows are nearly one-hot, so the exact entropy is ~1e-7
     # nats and the fp32 record's Z sits at 1 + O(1e-9); each rounding of Z
@@ -395,11 +396,10 @@ def test_outlier_logits(dtype, combo, chunks, mode):
     # ~20 merges, so the entropy is checked to 2e-6 nats absolute instead of
     # relative to its near-zero value.
     ref_sc, ref_g, _ = run_oracle(spec, inp)
-    xmax = float(inp["logits"].float().abs().max()) * spec.logit_scale * 1.4427
-    f32_abs = max(1e-6, 2 * 0.6931 * xmax * 2.0 ** -23 * float(np.max(np.abs(ref_g))))
     gm = None if mode == "gradient" else "none"
-    _, sc, _ = _check_small(spec, inp, dtype, chunks=chunks, grad_mode=gm, f32_abs=f32_abs,
-                            skip_scalars=("ENTROPY",))
+    _, sc, met = _check_small(spec, inp, dtype, chunks=chunks, grad_mode=gm, skip_scalars=("ENTROPY",))
+    if met is not None and "max_abs" in met:
+        say(f"[f32-err] outlier max_abs={met['max_abs']:.3e} max|g|={float(np.max(np.abs(ref_g))):.3e}")
     e = SLOT["ENTROPY"]
     assert abs(sc[e] - ref_sc[e]) <= 2e-6 + TOL[dtype]["scalar_rel"] * abs(ref_sc[e]), (sc[e], ref_sc[e])
     spec_c, inp_c = _small(dtype, combo, N, V, seed=71 + chunks, softcap=30.0, scale=0.5)
@@ -408,8 +408,9 @@ def test_outlier_logits(dtype, combo, chunks, mode):
     if spec_c.has(GRPO):
         inp_c["old_logprobs"] = oracle_old_logprobs(spec_c, inp_c["logits"], inp_c["labels"], inp_c["old_noise"])
     ref_sc, ref_c, _ = run_oracle(spec_c, inp_c)
-    _, sc, _ = _check_small(spec_c, inp_c, dtype, chunks=chunks, grad_mode=gm, skip_scalars=("ENTROPY",),
-                            f32_abs=max(1e-6, 2 * 0.6931 * 30 * 1.4427 * 2.0 ** -23 * float(np.max(np.abs(ref_c)))))
+    _, sc, met = _check_small(spec_c, inp_c, dtype, chunks=chunks, grad_mode=gm, skip_scalars=("ENTROPY",))
+    if met is not None and "max_abs" in met:
+        say(f"[f32-err] outlier softcap max_abs={met['max_abs']:.3e} max|g|={float(np.max(np.abs(ref_c))):.3e}")
     assert abs(sc[e] - ref_sc[e]) <= 2e-6 + TOL[dtype]["scalar_rel"] * abs(ref_sc[e]), (sc[e], ref_sc[e])
 
 

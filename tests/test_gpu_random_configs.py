@@ -14,26 +14,21 @@ bf16: scalars 1e-4 relative, gradient rms-relative 4e-3 over the tensor and
 over its non-label entries; fp16: 1e-3); masked rows must be +0.0 or
 untouched.
 
-Two configurations the fixed absolute gates do not fit, read the same way
-as the outlier test reads very large logits. The shared statistics are fp32
-numbers of magnitude up to L2 = log2(e) (S + max |lse|), so every
-softmax entry and the policy ratio carry a relative error of a few ulps of
-L2: with one or a few rows and scales above 1 the gradient entries are of
-order 1, and the fp32 gradient gate becomes max(1e-6, 4 L2 2^-23 max |g|).
-A scalar whose exact value is 0 because a row is degenerate (V = 1: CE,
-new log-prob and every KL are 0) is computed from logits of magnitude
-S = max |s| (with a softcap c, max(max |s|, c): the element path forms
-s log2 e as c log2 e - 2 c log2 e r, within a few ulps of c log2 e), so it
-may differ from 0 by a few ulps of that: each slot is accepted within its
-relative gate or within 4 ulps of S times the weight sum; S also replaces
-max |s| in L2 above. On one-element rows (V = 1) every gradient term but
-the z-loss's cancels exactly (q = 1), and fp32 leaves q within a few ulps of
-L2 of 1: their gradient is checked per element to the output rounding
-(2^-7 relative) plus 4 ulps of L2 times grad_scale k (1 + sum of weights)
-/ n. fp16 stores magnitudes below 2^-14 as subnormals 2^-24 apart (a
-z-loss-only plan with a small weight puts its whole gradient there): the
-fp16 rms bounds add that spacing, rms(g - ref) <= 1e-3 rms(ref) + 2^-24,
-over the tensor and over its non-label entries.
+One configuration the fixed gates do not fit, a reading stated here: rows of
+one element (V = 1). There the exact CE, new log-prob and every KL are 0 and
+every gradient term but the z-loss's cancels exactly (q = 1), while the
+kernel forms them from fp32 statistics of magnitude S = max |s| (with a
+softcap c, max(max |s|, c): the element path forms s log2 e as
+c log2 e - 2 c log2 e r, within a few ulps of c log2 e). On such cases a
+scalar slot is accepted within its relative gate or within 4 ulps of S
+times the weight sum, and the gradient per element within the output
+rounding (2^-7 relative) plus 4 ulps of L2 = log2(e) (S + max |lse|) times
+grad_scale k (1 + sum of weights) / n; the test prints the measured error.
+Every other fp32 case uses the plain gates. fp16 stores magnitudes below
+2^-14 as subnormals 2^-24 apart (a z-loss-only plan with a small weight puts
+its whole gradient there): the fp16 rms bounds add that spacing,
+rms(g - ref) <= 1e-3 rms(ref) + 2^-24, over the tensor and over its
+non-label entries.
 """
 
 import numpy as np
@@ -42,7 +37,8 @@ import torch
 
 import oracle
 import workloads
-from gpu_support import (TOL, grad_check, make_plan, oracle_old_logprobs, say, scalar_errors, spec_from, to_np)
+from gpu_support import (TOL, assert_scalars, degenerate_allowance, grad_check, make_plan, oracle_old_logprobs,
+                         say, scalar_errors, spec_from, to_np)
 from oracle import SLOT
 
 pytestmark = pytest.mark.gpu
@@ -188,25 +184,24 @@ def test_random_configuration(i):
     wsum = 1.0 + sum(abs(v) for k, v in c["w"].items() if k != "grad_scale")
     rel = TOL[dtype]["scalar_rel"]
     errs = scalar_errors(spec, got, ref_sc, vals, valid)
-    for name in ("N_VALID", "N_BADLABEL"):
-        assert got[SLOT[name]] == ref_sc[SLOT[name]], name
+    allow = degenerate_allowance(spec, to_np(inp["logits"])[valid] if valid.any() else None)
     for name, e in errs.items():
-        if name in ("N_VALID", "N_BADLABEL") or (name == "CLIPFRAC" and boundary.any()):
-            continue
-        i_s = SLOT[name]
-        assert e <= rel or abs(got[i_s] - ref_sc[i_s]) <= 4 * 2.0 ** -23 * smax * wsum, \
-            (name, got[i_s], ref_sc[i_s], e)
+        if e > rel and name not in ("N_VALID", "N_BADLABEL"):
+            say(f"[scalar-v1] case {i} {name} got={got[SLOT[name]]!r} ref={ref_sc[SLOT[name]]!r} "
+                f"abs={abs(got[SLOT[name]] - ref_sc[SLOT[name]]):.3e} allowance={allow:.3e} V={V}")
+    assert_scalars(spec, got, ref_sc, dtype, vals, valid, skip=("CLIPFRAC",) if boundary.any() else (),
+                   x=to_np(inp["logits"])[valid] if valid.any() else None)
     if grad is None:
         return
     gk = grad.detach().cpu()
     keep_rows = ~boundary
     l2 = 1.4427 * (smax + lmax)
-    f32_abs = max(1e-6, 4 * l2 * 2.0 ** -23 * float(np.max(np.abs(ref_g)))) if ref_g.size else 1e-6
     if V == 1:
         n = max(1, int(valid.sum()))
         floor = 4 * l2 * 2.0 ** -23 * c["w"]["grad_scale"] * c["scale"] * wsum / n
         gd = to_np(gk[torch.from_numpy(keep_rows)])
         rd = ref_g[keep_rows]
+        say(f"[v1-grad] case {i} max_abs={float(np.max(np.abs(gd - rd))) if gd.size else 0.0:.3e} floor={floor:.3e}")
         assert np.all(np.abs(gd - rd) <= 2.0 ** -7 * np.abs(rd) + floor), (np.max(np.abs(gd - rd)), floor)
     elif dtype == "f16":
         gd = to_np(gk[torch.from_numpy(keep_rows)])
@@ -221,7 +216,10 @@ def test_random_configuration(i):
                 err = float(np.sqrt(np.mean((gd[sel] - rd[sel]) ** 2)))
                 assert err <= tol * float(np.sqrt(np.mean(rd[sel] ** 2))) + 2.0 ** -24, (err, float(np.abs(rd[sel]).max()))
     else:
-        grad_check(gk[torch.from_numpy(keep_rows)], ref_g[keep_rows], dtype, labels=y[keep_rows], f32_abs=f32_abs)
+        met = grad_check(gk[torch.from_numpy(keep_rows)], ref_g[keep_rows], dtype, labels=y[keep_rows])
+        if "max_abs" in met:
+            say(f"[f32-err] case {i} max_abs={met['max_abs']:.3e} "
+                f"max|g|={float(np.max(np.abs(ref_g))) if ref_g.size else 0.0:.3e}")
     inval = torch.from_numpy(~valid)
     if c["mode"] == "overwrite":
         assert torch.equal(gk[inval].view(INT_VIEW[dtype]), torch.zeros_like(gk[inval]).view(INT_VIEW[dtype]))
