@@ -263,13 +263,46 @@ hl_status hl_forward_backward_segments(hl_plan_t plan, int64_t n_rows, const voi
                                        int64_t n_segments, void* grad_out,
                                        float* scalars_out, hipStream_t stream);
 
+/* Size of the library's static per-GPU workspace used by
+ * hl_forward_backward_noalloc. */
+#define HL_STATIC_WORKSPACE_BYTES (32u * 1024u * 1024u)
+
+/*
+ * hl_forward_backward_noalloc - hl_forward_backward_segments for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The call makes no device allocation
+ * and no allocating library call: its workspace is a fixed device array of
+ * HL_STATIC_WORKSPACE_BYTES inside the library, one per GPU, held from the
+ * first such call on that GPU until the process ends (the current device's
+ * copy is used; the stream must belong to that device). Arguments, results,
+ * asynchrony and kernels are those of hl_forward_backward_segments
+ * (seq_offsets may be NULL and n_segments 0 for plans without HL_GSPO), and
+ * the plan's own workspace, if any, is not touched; hl_row_values then points
+ * into the static array. Every call on one GPU, from any plan, shares that
+ * GPU's array and leaves its contents for the next call (each call clears
+ * what must start at zero itself): calls that overlap in time on one GPU
+ * race and must not be issued. Errors: those of
+ * hl_forward_backward_segments, plus HL_ERR_WORKSPACE when the call needs
+ * more than HL_STATIC_WORKSPACE_BYTES (hl_workspace_bytes(plan, n_rows) tells
+ * in advance; hl_last_error names the sizes), HL_ERR_UNSUPPORTED for a device
+ * index above 63, HL_ERR_HIP if the array's address cannot be obtained.
+ */
+hl_status hl_forward_backward_noalloc(hl_plan_t plan, int64_t n_rows, const void* logits,
+                                      const int64_t* labels, const uint8_t* mask,
+                                      const void* teacher_logits, const float* old_logprobs,
+                                      const float* advantages, const int32_t* seq_offsets,
+                                      int64_t n_segments, void* grad_out, float* scalars_out,
+                                      hipStream_t stream);
+
 /* Device pointer to the per-row values of the plan's last call: float
  * [n_rows, HL_NUM_ROW_COLS] inside the workspace (masked rows are all 0,
  * HL_R_VALID is 1 for counted rows; HL_R_ENTROPY is 0 unless HL_ENTROPY is
  * requested; with HL_GSPO the policy columns hold the row's segment values). Valid until the next call with the plan
  * or a workspace change. These are the per-token values the batch means of
  * #549 Loss coverage are taken over (new_logprobs, entropy, ratio, ...).
- * Returns NULL when the plan has no workspace yet. */
+ * Returns NULL before the plan's first call. The values live in the
+ * workspace the call used (the plan's, or the static one of
+ * hl_forward_backward_noalloc). */
 const float* hl_row_values(hl_plan_t plan);
 
 /* Override the number of vocabulary chunks per row (0 = automatic). More than
@@ -310,7 +343,9 @@ hl_status hl_plan_set_exchange_test(hl_plan_t plan, uint32_t spin_limit, int64_t
                                     int withhold_chunk);
 
 /* Text of the last HIP failure seen by this thread (which call, the HIP
- * error string and code), or "" if none. Valid until the next failing call. */
+ * error string and code), or of the last workspace-size refusal of
+ * hl_forward_backward_noalloc, or "" if none. Valid until the next failing
+ * call. */
 const char* hl_last_error(void);
 
 /* Static text for a status code. */

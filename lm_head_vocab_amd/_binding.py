@@ -102,6 +102,8 @@ def load_library(path: str | None = None):
     lib.hl_forward_backward.restype = ctypes.c_int
     lib.hl_forward_backward_segments.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp]
     lib.hl_forward_backward_segments.restype = ctypes.c_int
+    lib.hl_forward_backward_noalloc.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp]
+    lib.hl_forward_backward_noalloc.restype = ctypes.c_int
     lib.hl_row_values.argtypes = [vp]
     lib.hl_row_values.restype = vp
     lib.hl_plan_set_chunks.argtypes = [vp, ctypes.c_int]
@@ -239,7 +241,10 @@ class Plan:
         return ctypes.c_void_p(t.data_ptr())
 
     def __call__(self, logits, labels=None, mask=None, teacher=None, old_logprobs=None,
-                 advantages=None, grad=None, scalars=None, stream=None, seq_offsets=None):
+                 advantages=None, grad=None, scalars=None, stream=None, seq_offsets=None,
+                 noalloc=False):
+        """noalloc: run hl_forward_backward_noalloc (the library's static
+        per-GPU workspace; no device allocation by the call itself)."""
         torch = _torch()
         if logits.dim() != 2 or logits.shape[1] != self.V:
             raise ValueError(f"logits must be [N, {self.V}], got {tuple(logits.shape)}")
@@ -260,9 +265,22 @@ class Plan:
         if scalars is None:
             scalars = torch.empty(NUM_SCALARS, dtype=torch.float32, device=dev)
         sp = self._ptr(scalars, "scalars", torch.float32, (NUM_SCALARS,))
-        self._ensure_workspace(n, dev)
         if stream is None:
             stream = torch.cuda.current_stream(dev)
+        if noalloc:
+            op, n_seg = None, 0
+            if seq_offsets is not None:
+                if seq_offsets.dim() != 1 or seq_offsets.numel() < 1:
+                    raise ValueError("seq_offsets must be a 1-D int32 tensor of n_segments + 1 offsets")
+                op, n_seg = self._ptr(seq_offsets, "seq_offsets", torch.int32), seq_offsets.numel() - 1
+            st = self._lib.hl_forward_backward_noalloc(
+                self._h, n, *args[:6], op, n_seg, args[6], sp, ctypes.c_void_p(stream.cuda_stream))
+            _check("hl_forward_backward_noalloc", st)
+            self._last_rows = n
+            self._last_static = True
+            return scalars
+        self._ensure_workspace(n, dev)
+        self._last_static = False
         if seq_offsets is None:
             st = self._lib.hl_forward_backward(self._h, n, *args, sp, ctypes.c_void_p(stream.cuda_stream))
             _check("hl_forward_backward", st)
@@ -281,6 +299,9 @@ class Plan:
         """float32 [n_rows, 12] view of the per-row values of the last call."""
         torch = _torch()
         ptr = self._lib.hl_row_values(self._h)
+        if getattr(self, "_last_static", False):
+            raise RuntimeError("the last call used the static workspace (hl_forward_backward_noalloc); "
+                               "its per-row values are at the device pointer hl_row_values returns")
         if not ptr or self._ws is None:
             raise RuntimeError("no call has been made with this plan yet")
         off = ptr - self._ws.data_ptr()

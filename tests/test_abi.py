@@ -303,3 +303,20 @@ def test_exchange_test_hook_arguments():
     assert hook(h, 64, 3, 1) == hl.HL_OK
     assert hook(h, 1 << 20, -1, -1) == hl.HL_OK                  # back to the default
     lib.hl_plan_destroy(h)
+
+
+def test_noalloc_checks_before_any_hip_call():
+    # argument checks and the static-workspace size limit are host checks
+    st, h = _plan(V=151936, flags=hl.CE | hl.FKL, w=Weights(1, 0, 1, 0, 1, 0), tau=2.0)
+    assert st == 0
+    fake = VP(4096)
+    na = lib.hl_forward_backward_noalloc
+    assert na(None, 4, fake, fake, None, fake, None, None, None, 0, fake, fake, None) == hl.HL_ERR_INVALID_ARG
+    assert na(h, 4, fake, fake, None, None, None, None, None, 0, fake, fake, None) == hl.HL_ERR_MISSING_INPUT
+    n = 1
+    while lib.hl_workspace_bytes(h, n) <= 32 * 1024 * 1024:
+        n *= 2
+    assert na(h, n, fake, fake, None, fake, None, None, None, 0, fake, fake, None) == hl.HL_ERR_WORKSPACE
+    msg = lib.hl_last_error().decode()
+    assert "HL_STATIC_WORKSPACE_BYTES" in msg and str(n) in msg
+    lib.hl_plan_destroy(h)
