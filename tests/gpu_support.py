@@ -34,6 +34,20 @@ ROW_KEY = {"CE": "ce", "Z": "z", "DISTILL": "distill", "GRPO": "grpo", "NEWLOGP"
            "KL_OLD_NEW": "k3", "ADV_MEAN": "adv", "ENTROPY": "entropy"}
 ZERO_CAPABLE = ("DISTILL", "GRPO", "KL_OLD_NEW", "ADV_MEAN")
 NEAR_ZERO_FLOOR = 1e-2
+# per-row value columns whose values can be exactly 0 (the same reading, row by row)
+ZERO_CAPABLE_ROWS = ("fkl", "rkl", "fdce", "grpo", "k3", "adv")
+
+
+def row_value_scale(key, ref):
+    """Scale of each per-row value of column `key` (ref: the oracle's values of
+    the valid rows): max(|value|, 1e-2 * mean |value| of the column), and the
+    near-zero floor for columns whose values can be exactly 0."""
+    ref = np.asarray(ref, dtype=np.float64)
+    col = 1e-2 * float(np.mean(np.abs(ref))) if ref.size else 0.0
+    sc = np.maximum(np.abs(ref), col)
+    if key in ZERO_CAPABLE_ROWS:
+        sc = np.maximum(sc, NEAR_ZERO_FLOOR)
+    return sc
 
 
 def degenerate_allowance(spec, x) -> float:

@@ -37,6 +37,7 @@ HAND = {
     "ce_fdce_bf16": 2 * 2 * 151936 + 2 * 151936 + 8,
     "ce_fkl_hinton_bf16": 2 * 2 * 151936 + 2 * 151936 + 8,
     "grpo_z_ent_bf16": 2 * 151936 + 2 * 151936 + 8 + 1 + 8,
+    "ce_z_grpo_ent_bf16": 2 * 151936 + 2 * 151936 + 8 + 1 + 8,
     "gspo_z_ent_bf16": 2 * 2 * 151936 + 2 * 151936 + 8 + 1 + 8,
     "all_combined_bf16": 2 * 2 * 256000 + 2 * 2 * 256000 + 8 + 8,
 }
@@ -74,16 +75,19 @@ def test_metrics_only_calls_read_each_valid_row_once():
 
 
 def test_headline_launch_bytes_match_the_design_figure():
-    # 16384 tokens, 5% of them masked in the generated batch: 15534 valid rows
+    # 16384 tokens, 5% of them masked in the generated batch: 15534 valid rows; the default
+    # line runs the loss set the metric names on the GRPO configuration's inputs
     w = workloads.WORKLOADS[workloads.HEADLINE]
-    assert w.name == "grpo_z_ent_bf16"
+    assert w.name == "ce_z_grpo_ent_bf16"
+    assert "+".join(bench.LOSS_NAMES[b] for b in bench.LOSS_NAMES if w.flags & b) == "CE+z+GRPO+entropy"
+    assert workloads.seed_for(w.name) == workloads.seed_for("grpo_z_ent_bf16")
     assert workloads.algorithmic_bytes(w, n_valid_rows=15534) == 9699265024
 
 
 def test_source_hash_is_stable_and_stored_traffic_needs_it():
     h = bench.source_hash()
     assert h == bench.source_hash() and len(h) == 16 and int(h, 16) >= 0
-    w = workloads.WORKLOADS[workloads.HEADLINE]
+    w = workloads.WORKLOADS["grpo_z_ent_bf16"]
     assert bench.stored_traffic(w, "0" * 16) is None
     path = os.path.join(ROOT, "profiles", f"fused_kernel_{w.name}_pmc.json")
     with open(path) as f:

@@ -311,70 +311,3 @@ def test_gspo_empty_batch_and_all_masked():
     assert torch.all(sc.cpu() == 0)
     spec, inp = _case("bf16", "all_gspo_rkl", 10, 777, seed=1, ignore_frac=1.0)
     _check(spec, inp, "bf16")
-
-
-# ---------------------------------------------------------------------------
-# The GSPO benchmark configuration at full size
-# ---------------------------------------------------------------------------
-def test_gspo_full_config_sampled_segments():
-    name = "gspo_z_ent_bf16"
-    w = workloads.WORKLOADS[name]
-    say(f"[gpu] generate {name} N={w.N} V={w.V}")
-    inp = workloads.generate(w, DEV)
-    spec = spec_from(w.V, w.flags, dict(ce=0.0, z=w.weights["z"], grpo=w.weights["grpo"]), eps=w.eps)
-    inp["old_logprobs"] = torch_old_logprobs(spec, inp["logits"], inp["labels"], inp["old_noise"])
-    plan = make_plan(spec, torch.bfloat16)
-    grad = torch.empty_like(inp["logits"])
-    say(f"[gpu] run {name} plan={plan.describe()}")
-    sc = plan(inp["logits"], labels=inp["labels"], mask=inp["mask"], old_logprobs=inp["old_logprobs"],
-              advantages=inp["advantages"], grad=grad, seq_offsets=inp["seq_offsets"]).cpu().double().numpy()
-    torch.cuda.synchronize()
-    rv = plan.row_values().cpu().double().numpy()
-    N = w.N
-    offs = inp["seq_offsets"].cpu().numpy().astype(np.int64)
-    labels = to_np(inp["labels"]).astype(np.int64)
-    mask = to_np(inp["mask"])
-    valid, _ = oracle.row_validity(N, w.V, labels, mask)
-    assert sc[SLOT["N_VALID"]] == int(valid.sum())
-    inval = torch.from_numpy(~valid).to(DEV)
-    assert torch.count_nonzero(grad[inval].view(torch.int16)).item() == 0
-    # property: the policy slots are the means over segments of the per-token
-    # segment columns (read at each segment's first valid row)
-    S = len(offs) - 1
-    firsts = [offs[i] + int(np.argmax(valid[offs[i]:offs[i + 1]])) for i in range(S) if valid[offs[i]:offs[i + 1]].any()]
-    for slot, col in (("GRPO", 3), ("RATIO", 5), ("CLIPFRAC", 6), ("KL_OLD_NEW", 7), ("ADV_MEAN", 8)):
-        expect = rv[firsts, col].mean()
-        assert abs(sc[SLOT[slot]] - expect) <= 2e-6 * max(1.0, abs(expect)), (slot, sc[SLOT[slot]], expect)
-    # two whole segments against the oracle (their coefficients depend on
-    # every row of the segment), gradient on a spread of their rows
-    n_seg = len(firsts)
-    for i in (0, S - 1):
-        r0, r1 = int(offs[i]), int(offs[i + 1])
-        rows = np.arange(r0, r1)
-        sub = {k: (v[r0:r1].cpu() if isinstance(v, torch.Tensor) and v.dim() >= 1 and v.shape[0] == N else v)
-               for k, v in inp.items()}
-        x = to_np(sub["logits"])
-        say(f"[gpu] oracle on segment {i} rows [{r0}, {r1})")
-        logp = np.empty(len(rows))
-        for c0 in range(0, len(rows), 32):
-            logp[c0:c0 + 32] = oracle.row_values(spec, x[c0:c0 + 32], labels[r0:r1][c0:c0 + 32])["logp"]
-        seam = oracle.gspo_seam(spec, logp, to_np(sub["old_logprobs"]), to_np(sub["advantages"]),
-                                valid[rows], [0, len(rows)], n_seg_total=n_seg)
-        near = abs(seam["ratio"][0] - (1 + spec.eps)) < 1e-5 or abs(seam["ratio"][0] - (1 - spec.eps)) < 1e-5
-        tol = TOL["bf16"]["scalar_rel"]
-        first = r0 + int(np.argmax(valid[rows]))
-        for key, col in (("loss", 3), ("ratio", 5), ("k3", 7), ("adv", 8)):
-            ref = seam[key][0]
-            scale = max(abs(ref), 1e-3 if key in ("loss", "k3") else 1e-2)
-            assert abs(rv[first, col] - ref) / scale <= tol, (key, rv[first, col], ref)
-        if near:
-            continue
-        assert (rv[first, 6] != 0) == bool(seam["clipped"][0])
-        pick = np.unique(np.concatenate([[0, len(rows) - 1], np.linspace(0, len(rows) - 1, 12).astype(int)]))
-        n = float(valid.sum())
-        _, _, _, ref_g = oracle.rows_forward_backward(
-            spec, x[pick], n, labels=labels[r0:r1][pick], mask=mask[r0:r1][pick],
-            old_logprobs=to_np(sub["old_logprobs"])[pick], advantages=to_np(sub["advantages"])[pick],
-            gspo_dlogp=seam["dlogp"][pick])
-        gk = grad[torch.from_numpy(rows[pick]).to(DEV)].cpu()
-        grad_check(gk, ref_g, "bf16", labels=labels[r0:r1][pick])
