@@ -66,77 +66,86 @@ def plan_kwargs(w):
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle, as it stands, on a bounded sample of rows
 # ---------------------------------------------------------------------------
-def cpu_baseline(w, budget_s: float, threads: int):
+_SAMPLE = None   # (spec, flags, N, x, inputs): set before the worker processes fork
+
+
+def _oracle_rows(bounds):
+    """One task of the CPU baseline: the oracle's forward+backward on rows
+    [r0, r1) of the sample (GSPO: those rows as one segment)."""
+    import oracle
+
+    spec, flags, N, x, d = _SAMPLE
+    r0, r1 = bounds
+    sub = {key: (v[r0:r1] if v is not None else None) for key, v in d.items()}
+    if flags & oracle.GSPO:
+        oracle.forward_backward(spec, x[r0:r1], seq_offsets=[0, r1 - r0], **sub)
+    else:
+        oracle.rows_forward_backward(spec, x[r0:r1], float(N), **sub)
+    return r1 - r0
+
+
+def cpu_baseline(w, budget_s: float, workers: int):
+    import multiprocessing as mp
+
     import numpy as np
-    from concurrent.futures import ThreadPoolExecutor
 
     import oracle
 
+    global _SAMPLE
     spec = oracle.Spec(V=w.V, flags=w.flags, w_ce=w.weights.get("ce", 1.0), w_z=w.weights.get("z", 0.0),
                        w_distill=w.weights.get("distill", 0.0), w_grpo=w.weights.get("grpo", 0.0),
                        grad_scale=w.weights.get("grad_scale", 1.0), temperature=w.temperature,
                        eps=w.eps, logit_scale=w.logit_scale, softcap=w.softcap)
     rows_per_task = 2
-
-    def sample(n_rows, seed):
-        inp = workloads.generate(w, "cpu", seed=seed, n_rows=n_rows)
-        x = inp["logits"].double().numpy()
-        y = inp["labels"].numpy() if inp["labels"] is not None else None
-        d = dict(labels=y, mask=inp["mask"].numpy() if inp["mask"] is not None else None,
-                 teacher=inp["teacher"].double().numpy() if inp["teacher"] is not None else None,
-                 advantages=inp["advantages"].double().numpy() if inp["advantages"] is not None else None,
-                 grad_in=inp["grad_init"].double().numpy() if inp["grad_init"] is not None else None)
-        if w.flags & (oracle.GRPO | oracle.GSPO):
-            d["old_logprobs"] = oracle.row_values(spec, x, y)["logp"] + inp["old_noise"].double().numpy()
-        return x, d
-
-    def task(args):
-        x, d = args
-        if w.flags & oracle.GSPO:
-            # the rows of one task form one segment (GSPO's coefficients need whole segments)
-            oracle.forward_backward(spec, x, seq_offsets=[0, x.shape[0]], **d)
-        else:
-            oracle.rows_forward_backward(spec, x, float(w.N), **d)
-
-    def split(x, d, k):
-        out = []
-        for r0 in range(0, x.shape[0], k):
-            sl = slice(r0, r0 + k)
-            out.append((x[sl], {key: (v[sl] if v is not None else None) for key, v in d.items()}))
-        return out
-
-    # a fixed sample of rows, processed in rounds until the time budget is spent
-    n_rows = 4 * threads * rows_per_task
-    x, d = sample(n_rows, seed=workloads.seed_for(w.name, 8))
-    tasks = split(x, d, rows_per_task)
-    log(f"cpu baseline: oracle on {n_rows}-row sample x V={w.V}, {threads} threads, ~{budget_s:.0f} s")
+    n_rows = 4 * workers * rows_per_task
+    inp = workloads.generate(w, "cpu", seed=workloads.seed_for(w.name, 8), n_rows=n_rows)
+    x = inp["logits"].double().numpy()
+    y = inp["labels"].numpy() if inp["labels"] is not None else None
+    d = dict(labels=y, mask=inp["mask"].numpy() if inp["mask"] is not None else None,
+             teacher=inp["teacher"].double().numpy() if inp["teacher"] is not None else None,
+             advantages=inp["advantages"].double().numpy() if inp["advantages"] is not None else None,
+             grad_in=inp["grad_init"].double().numpy() if inp["grad_init"] is not None else None,
+             old_logprobs=None)
+    if w.flags & (oracle.GRPO | oracle.GSPO):
+        d["old_logprobs"] = oracle.row_values(spec, x, y)["logp"] + inp["old_noise"].double().numpy()
+    _SAMPLE = (spec, w.flags, w.N, x, d)
+    tasks = [(r0, r0 + rows_per_task) for r0 in range(0, n_rows, rows_per_task)]
+    log(f"cpu baseline: oracle on a {n_rows}-row sample x V={w.V}, {workers} worker processes, ~{budget_s:.0f} s")
     done = 0
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=threads) as ex:
+    # fork: the workers inherit the sample; nothing has touched the GPU yet
+    with mp.get_context("fork").Pool(processes=workers) as pool:
+        t0 = time.perf_counter()
         while True:
-            list(ex.map(task, tasks))
-            done += n_rows
+            done += sum(pool.map(_oracle_rows, tasks, chunksize=1))
             dt = time.perf_counter() - t0
             if dt >= budget_s:
                 break
-    n_rows = done
-    return {"value": n_rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_rows} row evaluations of a {4 * threads * rows_per_task}-row host-drawn sample of "
-                      f"{w.name} (V={w.V}, same recipe), full forward+backward in numpy fp64, "
-                      f"{threads} threads, {dt:.1f} s"}
+    _SAMPLE = None
+    return {"value": done / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "workers": workers, "host_cores": os.cpu_count(),
+            "cpus_available": len(os.sched_getaffinity(0)),
+            "sample": f"{done} row evaluations of a {n_rows}-row host-drawn sample of {w.name} (V={w.V}, same "
+                      f"recipe), full forward+backward in numpy fp64, {workers} worker processes "
+                      f"(host reports {os.cpu_count()} cores; the pool is capped at the 16-CPU share of one "
+                      f"GPU), {dt:.1f} s"}
 
 
 # ---------------------------------------------------------------------------
 # GPU measurement
 # ---------------------------------------------------------------------------
-def stored_traffic(w, src_hash, with_grad=True):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources; else None."""
+def traffic_file(w, with_grad=True):
+    """The committed counter summary of a workload's timed kernel(s)."""
     if with_grad:
         tag = "fused_seam" if w.flags & workloads.GSPO else FUSED_KERNEL
     else:
         tag = "stream_seam" if w.flags & workloads.GSPO else "stream_stats"
-    path = os.path.join(ROOT, "profiles", f"{tag}_{w.name}_pmc.json")
+    return f"profiles/{tag}_{w.name}_pmc.json"
+
+
+def stored_traffic(w, src_hash, with_grad=True):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, traffic_file(w, with_grad))
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -170,8 +179,8 @@ def main(argv=None):
     # The host baseline runs before anything touches the GPU.
     cpu = None
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
-        cpu = cpu_baseline(w, args.cpu_seconds, threads)
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        cpu = cpu_baseline(w, args.cpu_seconds, workers)
         log(f"cpu baseline {cpu['value']:.1f} tokens/s")
 
     import torch
@@ -298,8 +307,13 @@ def main(argv=None):
     achieved = algo_bytes / (kernel_avg * 1e-3) / 1e9
     src_hash = source_hash()
     traffic = stored_traffic(w, src_hash, with_grad=not args.no_grad)
+    tfile = traffic_file(w, with_grad=not args.no_grad)
+    traffic_source = (f"{tfile}: rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, copy-calibrated, taken on "
+                      f"these kernel sources (hash {src_hash}); not measured in this run"
+                      if traffic is not None else
+                      f"null: no counter summary for kernel source hash {src_hash} ({tfile})")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic, "traffic_source": traffic_source,
                 "kernel": ((GSPO_KERNELS if w.flags & workloads.GSPO else FUSED_KERNEL) if not args.no_grad else
                            (GSPO_FWD_KERNELS if w.flags & workloads.GSPO else STREAM_KERNEL)),
                 "kernel_ms_avg": round(kernel_avg, 5),
