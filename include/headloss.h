@@ -312,8 +312,13 @@ const float* hl_row_values(hl_plan_t plan);
  * releases a library-owned workspace; a caller-owned one must be set again
  * with hl_plan_set_workspace before the next call (HL_ERR_WORKSPACE until
  * then). Errors: HL_ERR_INVALID_ARG (chunks < 0 or > 9),
- * HL_ERR_UNSUPPORTED (no variant fits V with that many chunks, or more than
- * 8 chunks with HL_FDCE | HL_HINTON, whose chunks exchange 8 statistics). */
+ * HL_ERR_UNSUPPORTED (no variant fits V with that many chunks, or more
+ * chunks than the exchange serves: one wave polls all of a row's exchanged
+ * words, at most 64, and a chunk exchanges 3 statistics without a teacher,
+ * 6 with one, one more with HL_FDCE and one more with HL_HINTON; HL_F32 plans
+ * add the low parts of their 1 to 3 normalizers. So at most 8 chunks with
+ * HL_FDCE | HL_HINTON, and for HL_F32 plans 9 / 8 / 7 / 6 / 5 chunks without a
+ * teacher / forward or reverse KL / FDCE / Hinton KL / Hinton FDCE). */
 hl_status hl_plan_set_chunks(hl_plan_t plan, int chunks);
 
 /* Tuning form of hl_plan_set_chunks that also fixes the threads per

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kSeamBlock) void seam_kernel(const SeamParams p) {
     for (int64_t t = o0 + lane; t < o1; t += 64) {
         const float* rec = p.row_rec + t * REC;
         if (rec[R_VALID] != 0.f) {
-            const double lse = ((double)rec[R_M] + log2((double)rec[R_Z])) * LN2;
+            const double lse = ((double)rec[R_M] + log2((double)rec[R_Z] + (double)rec[R_ZL])) * LN2;
             const double xy = rec[R_XY];
             const double sy = p.cap > 0.f ? (double)p.cap * tanh((double)p.k * xy / (double)p.cap)
                                           : (double)p.k * xy;
@@ -207,18 +207,18 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(const ReduceParams
         const float old_r = grpo_in ? p.old_logprobs[r] : 0.f;
         const int64_t sid = (f & F_GSPO) ? (int64_t)p.seg_of_row[r] : -1;
         if (rec[R_VALID] != 0.f) {
-            const double Z = rec[R_Z];
+            const double Z = (double)rec[R_Z] + (double)rec[R_ZL];   // hi + lo (lo = 0 below fp32)
             const double l2Z = log2(Z);
             const double lse = ((double)rec[R_M] + l2Z) * LN2;
             v[RC_Z] = lse * lse;
             if (f & F_ENT) v[RC_ENT] = LN2 * (l2Z - (double)rec[R_S] / Z);   // S is formed only then
             if (f & F_DISTILL) {
-                const double Zt = rec[R_ZT];
+                const double Zt = (double)rec[R_ZT] + (double)rec[R_ZTL];
                 const double l2Zt = log2(Zt);
                 // the distillation student: the shared softmax, or the tempered
                 // one (Hinton mode; its shift is M / tau), whose value carries tau^2
                 const bool hinton = (f & F_HINTON) != 0u;
-                const double Zd = hinton ? (double)rec[R_ZS] : Z;
+                const double Zd = hinton ? (double)rec[R_ZS] + (double)rec[R_ZSL] : Z;
                 const double l2Zd = hinton ? log2(Zd) : l2Z;
                 const double sc = hinton ? (double)p.tau * (double)p.tau : 1.0;
                 if (f & F_RKL) {

@@ -166,6 +166,28 @@ __device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) { __builtin_nontemp
 
 __device__ __forceinline__ float fast_exp2(float a) { return __builtin_amdgcn_exp2f(a); }
 
+// 2^a in fp64: 2^a = 2^n 2^u with n = rint(a), |u| <= 1/2, and 2^u = e^(u ln 2)
+// from the Taylor series of the exponential to degree 8 (remainder below
+// 2^-32 relative, ample for a result that is rounded to fp32). Branch-free:
+// arguments below -1100 (-Inf included) are clamped there and give 0 from
+// the final scaling; a NaN argument gives NaN.
+__device__ __forceinline__ double exp2_hp(double a) {
+    constexpr double LN2 = 0.69314718055994530942;
+    a = a < -1100.0 ? -1100.0 : a;
+    const double n = rint(a);
+    const double v = (a - n) * LN2;
+    double e = 1.0 / 40320.0;
+    e = fma(e, v, 1.0 / 5040.0);
+    e = fma(e, v, 1.0 / 720.0);
+    e = fma(e, v, 1.0 / 120.0);
+    e = fma(e, v, 1.0 / 24.0);
+    e = fma(e, v, 1.0 / 6.0);
+    e = fma(e, v, 0.5);
+    e = fma(e, v, 1.0);
+    e = fma(e, v, 1.0);
+    return ldexp(e, (int)n);
+}
+
 // tanh from its definition: the odd Taylor polynomial (coefficients
 // 2^(2n) (2^(2n)-1) B_2n / (2n)!, terms z .. z^9) for |z| < 0.25, where the
 // truncation error is below 1e-8 relative and the fp32 result within 1.2e-7,
@@ -254,6 +276,54 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __fadd_rn(q.a, q.b);
 }
 
+// The same butterfly in fp64 (the fp32 instances' normalizer sums): each
+// step moves the two 32-bit halves.
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double pair_sum_d16(double v) {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)__double2loint(v), (uint32_t)__double2loint(v), false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)__double2hiint(v), (uint32_t)__double2hiint(v), false, false);
+    return __dadd_rn(__hiloint2double((int)hi[0], (int)lo[0]), __hiloint2double((int)hi[1], (int)lo[1]));
+}
+__device__ __forceinline__ double pair_sum_d32(double v) {
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)__double2loint(v), (uint32_t)__double2loint(v), false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)__double2hiint(v), (uint32_t)__double2hiint(v), false, false);
+    return __dadd_rn(__hiloint2double((int)hi[0], (int)lo[0]), __hiloint2double((int)hi[1], (int)lo[1]));
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+    v = __dadd_rn(v, dpp_d<DPP_XOR1>(v));
+    v = __dadd_rn(v, dpp_d<DPP_XOR2>(v));
+    v = __dadd_rn(v, dpp_d<DPP_HALF_MIRROR>(v));
+    v = __dadd_rn(v, dpp_d<DPP_MIRROR>(v));
+    v = pair_sum_d16(v);
+    return pair_sum_d32(v);
+}
+
+// An fp64 value as a hi + lo pair of floats.
+__device__ __forceinline__ void split_hl(double v, float& hi, float& lo) {
+    hi = (float)v;
+    lo = (float)(v - (double)hi);
+}
+
+// 2^d for a shift difference d. The fp32 instances (HP) use integer shifts,
+// so d is an integer (exact: both shifts are integers below 2^24 in
+// magnitude, or the factor is 0 anyway) and the factor an exact power of
+// two; -Inf and NaN (an empty side) give 0.
+template <bool HP>
+__device__ __forceinline__ float shift_int(float m) {
+    if constexpr (HP) return ceilf(m);
+    else return m;
+}
+template <bool HP>
+__device__ __forceinline__ float pow2_of(float d) {
+    if constexpr (HP) return ldexpf(1.0f, (int)fmaxf(d, -1000.0f));
+    else return fast_exp2(d);
+}
+
 // ---------------------------------------------------------------------------
 // Softmax-statistics record and its merge (the max-rescaling combine of an
 // online softmax). Written with non-contracted operations so that
@@ -261,19 +331,24 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ---------------------------------------------------------------------------
 struct Rec {
     float M, Z, S, Mt, Zt, SX, St, Zs;
+    float Zl, Ztl, Zsl;   // low parts of Z, Zt, Zs (fp32 instances; 0 otherwise)
 };
 
-__device__ __forceinline__ Rec rec_empty() { return Rec{kNegInf, 0.f, 0.f, kNegInf, 0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ Rec rec_empty() {
+    return Rec{kNegInf, 0.f, 0.f, kNegInf, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+}
 
 // Merge two records (beta = 1 / tau, used by the tempered student sums of the
 // Hinton modes, whose offsets move by beta times the student's shift change).
-template <int TMODE>
-__device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b, float beta) {
+// HP (the fp32 instances): the shifts are integers and the normalizers Z, Zt,
+// Zs are merged in fp64 from their hi + lo parts (betad = 1 / tau in fp64).
+template <int TMODE, bool HP = false>
+__device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b, float beta, double betad = 1.0) {
     const bool ea = (a.Z == 0.f), eb = (b.Z == 0.f);
     Rec r;
     const float M = fmaxf(a.M, b.M);
     const float da = __fsub_rn(a.M, M), db = __fsub_rn(b.M, M);
-    const float fa = fast_exp2(da), fb = fast_exp2(db);
+    const float fa = pow2_of<HP>(da), fb = pow2_of<HP>(db);
     r.M = M;
     r.Z = __fadd_rn(__fmul_rn(a.Z, fa), __fmul_rn(b.Z, fb));
     r.S = __fadd_rn(__fmul_rn(fa, __fadd_rn(a.S, __fmul_rn(da, a.Z))),
@@ -281,7 +356,7 @@ __device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b, float beta)
     if (TMODE != TM_NONE) {
         const float Mt = fmaxf(a.Mt, b.Mt);
         const float dta = __fsub_rn(a.Mt, Mt), dtb = __fsub_rn(b.Mt, Mt);
-        const float fta = fast_exp2(dta), ftb = fast_exp2(dtb);
+        const float fta = pow2_of<HP>(dta), ftb = pow2_of<HP>(dtb);
         r.Mt = Mt;
         r.Zt = __fadd_rn(__fmul_rn(a.Zt, fta), __fmul_rn(b.Zt, ftb));
         r.Zs = 0.f;
@@ -316,13 +391,28 @@ __device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b, float beta)
     } else {
         r.Mt = 0.f; r.Zt = 0.f; r.SX = 0.f; r.St = 0.f; r.Zs = 0.f;
     }
+    r.Zl = 0.f; r.Ztl = 0.f; r.Zsl = 0.f;
+    if constexpr (HP) {
+        // integer shifts: each side is rescaled exactly, the sum rounded once
+        // in fp64; the tempered sums move by d / tau, an fp64 exponential
+        split_hl((double)a.Z * fa + (double)a.Zl * fa + ((double)b.Z * fb + (double)b.Zl * fb), r.Z, r.Zl);
+        if (TMODE != TM_NONE) {
+            const double fta = pow2_of<HP>(__fsub_rn(a.Mt, r.Mt)), ftb = pow2_of<HP>(__fsub_rn(b.Mt, r.Mt));
+            split_hl((double)a.Zt * fta + (double)a.Ztl * fta + ((double)b.Zt * ftb + (double)b.Ztl * ftb), r.Zt,
+                     r.Ztl);
+            if (is_hinton(TMODE)) {
+                const double fsa = exp2_hp((double)da * betad), fsb = exp2_hp((double)db * betad);
+                split_hl(((double)a.Zs + (double)a.Zsl) * fsa + ((double)b.Zs + (double)b.Zsl) * fsb, r.Zs, r.Zsl);
+            }
+        }
+    }
     if (ea) r = b;
     if (eb) r = a;
     return r;
 }
 
-template <int CTRL, int TMODE>
-__device__ __forceinline__ Rec rec_dpp_step(const Rec& a, float beta) {
+template <int CTRL, int TMODE, bool HP = false>
+__device__ __forceinline__ Rec rec_dpp_step(const Rec& a, float beta, double betad = 1.0) {
     Rec b;
     b.M = dpp<CTRL>(a.M);
     b.Z = dpp<CTRL>(a.Z);
@@ -336,19 +426,25 @@ __device__ __forceinline__ Rec rec_dpp_step(const Rec& a, float beta) {
     } else {
         b.Mt = 0.f; b.Zt = 0.f; b.SX = 0.f; b.St = 0.f; b.Zs = 0.f;
     }
-    return rec_merge<TMODE>(a, b, beta);
+    b.Zl = 0.f; b.Ztl = 0.f; b.Zsl = 0.f;
+    if constexpr (HP) {
+        b.Zl = dpp<CTRL>(a.Zl);
+        if (TMODE != TM_NONE) b.Ztl = dpp<CTRL>(a.Ztl);
+        if (is_hinton(TMODE)) b.Zsl = dpp<CTRL>(a.Zsl);
+    }
+    return rec_merge<TMODE, HP>(a, b, beta, betad);
 }
 
 // Merge the records held by lanes 0..n-1 of every 16-lane row (lanes n..15
 // hold empty records); all lanes end with the same result. A step whose
 // partners are all empty is skipped: merging with an empty record returns
 // the other one unchanged, so the result is the same for any n.
-template <int TMODE>
-__device__ __forceinline__ Rec rec_reduce16(Rec r, float beta, int n) {
-    if (n > 1) r = rec_dpp_step<DPP_XOR1, TMODE>(r, beta);
-    if (n > 2) r = rec_dpp_step<DPP_XOR2, TMODE>(r, beta);
-    if (n > 4) r = rec_dpp_step<DPP_HALF_MIRROR, TMODE>(r, beta);
-    if (n > 8) r = rec_dpp_step<DPP_MIRROR, TMODE>(r, beta);
+template <int TMODE, bool HP = false>
+__device__ __forceinline__ Rec rec_reduce16(Rec r, float beta, int n, double betad = 1.0) {
+    if (n > 1) r = rec_dpp_step<DPP_XOR1, TMODE, HP>(r, beta, betad);
+    if (n > 2) r = rec_dpp_step<DPP_XOR2, TMODE, HP>(r, beta, betad);
+    if (n > 4) r = rec_dpp_step<DPP_HALF_MIRROR, TMODE, HP>(r, beta, betad);
+    if (n > 8) r = rec_dpp_step<DPP_MIRROR, TMODE, HP>(r, beta, betad);
     return r;
 }
 
@@ -485,7 +581,7 @@ __device__ __forceinline__ CoefsD row_coefs_hp(const FusedParams& p, const Rec& 
     constexpr double LN2 = 0.69314718055994530942;
     const uint32_t f = p.flags;
     CoefsD k;
-    const double l2Z = log2((double)r.Z);
+    const double l2Z = log2((double)r.Z + (double)r.Zl);
     const double B2 = (double)r.M + l2Z;
     const double lse = B2 * LN2;
     k.sB = (SOFTCAP ? (double)p.cl : 0.0) - B2;
@@ -494,14 +590,16 @@ __device__ __forceinline__ CoefsD row_coefs_hp(const FusedParams& p, const Rec& 
     k.cd = 0.0;
     double kl = 0.0;
     if (TMODE != TM_NONE) {
-        const double l2Zt = log2((double)r.Zt);
+        const double Ztd = (double)r.Zt + (double)r.Ztl;
+        const double l2Zt = log2(Ztd);
         k.sBt = -((double)r.Mt + l2Zt);
         if (is_hinton(TMODE)) {
-            const double l2Zs = log2((double)r.Zs);
-            k.cd = l2Z * ((double)p.beta + (double)p.beta_l) - l2Zs;
-            if (base_mode(TMODE) == TM_RKL) kl = LN2 * ((double)r.SX / (double)r.Zs - l2Zs + l2Zt);
+            const double Zsd = (double)r.Zs + (double)r.Zsl;
+            const double l2Zs = log2(Zsd);
+            k.cd = l2Z * p.betad - l2Zs;
+            if (base_mode(TMODE) == TM_RKL) kl = LN2 * ((double)r.SX / Zsd - l2Zs + l2Zt);
         } else if (TMODE == TM_RKL) {
-            kl = LN2 * ((double)r.SX / (double)r.Z - l2Z + l2Zt);
+            kl = LN2 * ((double)r.SX / ((double)r.Z + (double)r.Zl) - l2Z + l2Zt);
         }
     }
     double a_g = 0.0;
@@ -549,26 +647,6 @@ __device__ __forceinline__ CoefsFor<HP> row_coefs(const FusedParams& p, const Re
     else return row_coefs_fast<TMODE, SOFTCAP>(p, r, y, xy, old, adv);
 }
 
-// 2^a in fp64: 2^a = 2^n 2^u with n = rint(a), |u| <= 1/2, and 2^u = e^(u ln 2)
-// from the Taylor series of the exponential to degree 8 (remainder below
-// 2^-32 relative, ample for a result that is rounded to fp32). A NaN
-// argument gives NaN, -Inf and arguments far below the fp64 range give 0.
-__device__ __forceinline__ double exp2_hp(double a) {
-    constexpr double LN2 = 0.69314718055994530942;
-    if (!(a > -1070.0)) return a != a ? a : 0.0;
-    const double n = rint(a);
-    const double v = (a - n) * LN2;
-    double e = 1.0 / 40320.0;
-    e = fma(e, v, 1.0 / 5040.0);
-    e = fma(e, v, 1.0 / 720.0);
-    e = fma(e, v, 1.0 / 120.0);
-    e = fma(e, v, 1.0 / 24.0);
-    e = fma(e, v, 1.0 / 6.0);
-    e = fma(e, v, 0.5);
-    e = fma(e, v, 1.0);
-    e = fma(e, v, 1.0);
-    return ldexp(e, (int)n);
-}
 
 // Gradient of one element; lab = the label-column coefficient at the label,
 // else 0. The fp32 instances (HP) compute in fp64 and return the unrounded
@@ -584,14 +662,14 @@ grad_one(const FusedParams& p, const CoefsFor<HP>& k, float x, float t,
             aq = fma(r, -2.0 * (double)p.cl, k.sB);
             cf = r * (4.0 - 4.0 * r);
         } else {
-            aq = fma((double)x, (double)p.K1 + (double)p.K1l, k.sB);
+            aq = fma((double)x, p.K1d, k.sB);
         }
         const double q = exp2_hp(aq);
         double up = 0.0;              // log2 of the teacher's softmax entry
-        if (TMODE != TM_NONE) up = fma((double)t, (double)p.K2 + (double)p.K2l, k.sBt);
+        if (TMODE != TM_NONE) up = fma((double)t, p.K2d, k.sBt);
         double g;
         if (is_hinton(TMODE)) {
-            const double aqd = fma(aq, (double)p.beta + (double)p.beta_l, k.cd);
+            const double aqd = fma(aq, p.betad, k.cd);
             const double qd = exp2_hp(aqd);
             if (fkl_like(TMODE)) g = k.alpha * q + k.gq * qd - k.gam * exp2_hp(up) - lab;
             else g = k.alpha * q + qd * (k.rho2 * (aqd - up) + k.c0) - lab;
@@ -637,37 +715,60 @@ grad_one(const FusedParams& p, const CoefsFor<HP>& k, float x, float t,
 // when WS: the entropy sum), Zt += 2^u, the distillation cross sum SX (and
 // St = sum 2^u u, Zs = sum 2^(a / tau) in the modes that need them), with
 // a = s log2(e) - M the student's and u = t log2(e) / tau - Mt the teacher's
-// offset (HP: with the low parts of the constants).
-template <int TMODE, bool SOFTCAP, bool WS, bool HP>
-__device__ __forceinline__ void stat_term(const FusedParams& p, float M, float Mt, float x, float t, float& z,
-                                          float& s, float& zt, float& sx, float& st, float& zs) {
-    float a;
-    if (SOFTCAP) {
-        a = fmaf(cap_r(x, p.kc2), -2.0f * p.cl, p.cl - M);
-    } else {
-        a = fmaf(x, p.K1, -M);
-        if (HP) a = fmaf(x, p.K1l, a);
-    }
-    const float ex = fast_exp2(a);
-    z += ex;
-    if (WS) s = fmaf(ex, a, s);
-    if (TMODE != TM_NONE) {
-        float u = fmaf(t, p.K2, -Mt);
-        if (HP) u = fmaf(t, p.K2l, u);
-        const float et = fast_exp2(u);
-        zt += et;
-        if (is_hinton(TMODE)) {
-            const float ad = HP ? fmaf(a, p.beta_l, a * p.beta) : a * p.beta;   // tempered student, shift M beta
-            const float ed = fast_exp2(ad);
-            zs += ed;
-            if (fkl_like(TMODE)) sx = fmaf(et, u - ad, sx);
-            else sx = fmaf(ed, ad - u, sx);
-        } else if (fkl_like(TMODE)) {
-            sx = fmaf(et, u - a, sx);
-        } else {
-            sx = fmaf(ex, a - u, sx);
+// offset. HP (the fp32 instances): the offsets with the low parts of the
+// constants in fp64, the normalizer terms from the fp64 exp2, and Z, Zt, Zs
+// accumulated in fp64 (A = double); S, SX, St stay fp32 sums.
+template <int TMODE, bool SOFTCAP, bool WS, bool HP, typename A>
+__device__ __forceinline__ void stat_term(const FusedParams& p, float M, float Mt, float x, float t, A& z,
+                                          float& s, A& zt, float& sx, float& st, A& zs) {
+    if constexpr (HP) {
+        const double ad = SOFTCAP ? fma((double)cap_r(x, p.kc2), -2.0 * (double)p.cl, (double)p.cl - (double)M)
+                                  : fma((double)x, p.K1d, -(double)M);
+        const double exd = exp2_hp(ad);
+        z += exd;
+        const float a = (float)ad, ex = (float)exd;
+        if (WS) s = fmaf(ex, a, s);
+        if (TMODE != TM_NONE) {
+            const double ud = fma((double)t, p.K2d, -(double)Mt);
+            const double etd = exp2_hp(ud);
+            zt += etd;
+            const float u = (float)ud, et = (float)etd;
+            if (is_hinton(TMODE)) {
+                const double add = ad * p.betad;   // tempered student, shift M beta
+                const double edd = exp2_hp(add);
+                zs += edd;
+                const float ad32 = (float)add, ed = (float)edd;
+                if (fkl_like(TMODE)) sx = fmaf(et, u - ad32, sx);
+                else sx = fmaf(ed, ad32 - u, sx);
+            } else if (fkl_like(TMODE)) {
+                sx = fmaf(et, u - a, sx);
+            } else {
+                sx = fmaf(ex, a - u, sx);
+            }
+            if (has_st(TMODE)) st = fmaf(et, u, st);
         }
-        if (has_st(TMODE)) st = fmaf(et, u, st);
+    } else {
+        const float a = SOFTCAP ? fmaf(cap_r(x, p.kc2), -2.0f * p.cl, p.cl - M) : fmaf(x, p.K1, -M);
+        const float ex = fast_exp2(a);
+        z += ex;
+        if (WS) s = fmaf(ex, a, s);
+        if (TMODE != TM_NONE) {
+            const float u = fmaf(t, p.K2, -Mt);
+            const float et = fast_exp2(u);
+            zt += et;
+            if (is_hinton(TMODE)) {
+                const float ad = a * p.beta;          // tempered student, shift M beta
+                const float ed = fast_exp2(ad);
+                zs += ed;
+                if (fkl_like(TMODE)) sx = fmaf(et, u - ad, sx);
+                else sx = fmaf(ed, ad - u, sx);
+            } else if (fkl_like(TMODE)) {
+                sx = fmaf(et, u - a, sx);
+            } else {
+                sx = fmaf(ex, a - u, sx);
+            }
+            if (has_st(TMODE)) st = fmaf(et, u, st);
+        }
     }
 }
 
@@ -843,6 +944,7 @@ void fused_kernel(const FusedParams p) {
         r.M = s_lrec[R_M]; r.Z = s_lrec[R_Z]; r.S = s_lrec[R_S];
         r.Mt = s_lrec[R_MT]; r.Zt = s_lrec[R_ZT]; r.SX = s_lrec[R_SX]; r.St = s_lrec[R_ST];
         r.Zs = s_lrec[R_ZS];
+        r.Zl = s_lrec[R_ZL]; r.Ztl = s_lrec[R_ZTL]; r.Zsl = s_lrec[R_ZSL];
     } else {
     // ---- pass 1: sums relative to a provisional wave shift, log2 domain ----
     // The shift is the wave's maximum over its first vector, not the row
@@ -875,47 +977,64 @@ void fused_kernel(const FusedParams p) {
     const float mx0 = wave_max(mx);
     const float mt0 = TMODE != TM_NONE ? wave_max(mt) : 0.f;
     auto shift_of = [&](float m) -> float {
-        return SOFTCAP ? (p.cap * hl_tanh(m * p.kc)) * kLog2e : m * p.K1;
+        return shift_int<HP>(SOFTCAP ? (p.cap * hl_tanh(m * p.kc)) * kLog2e : m * p.K1);
     };
     float M = shift_of(mx0);
-    float Mt = TMODE != TM_NONE ? mt0 * p.K2 : 0.f;
+    float Mt = TMODE != TM_NONE ? shift_int<HP>(mt0 * p.K2) : 0.f;
     const bool early = mx0 != kNegInf && (TMODE == TM_NONE || mt0 != kNegInf);
     const bool want_s = (p.flags & F_ENT) != 0u;
 
+    // normalizer accumulators: fp64 in the fp32 instances
+    using Acc = typename std::conditional<HP, double, float>::type;
     float Z = 0.f, S = 0.f, Zt = 0.f, SX = 0.f, St = 0.f, Zs = 0.f;
+    float Zl = 0.f, Ztl = 0.f, Zsl = 0.f;
     // one term of every sum; the entropy term only when WS
-    auto term = [&](auto want_s_tag, float x, float t, float& z, float& s, float& zt, float& sx, float& st,
-                    float& zs) {
+    auto term = [&](auto want_s_tag, float x, float t, Acc& z, float& s, Acc& zt, float& sx, float& st,
+                    Acc& zs) {
         stat_term<TMODE, SOFTCAP, decltype(want_s_tag)::value, HP>(p, M, Mt, x, t, z, s, zt, sx, st, zs);
     };
-    auto accumulate = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st, float& zs) {
+    auto accumulate = [&](float x, float t, Acc& z, float& s, Acc& zt, float& sx, float& st, Acc& zs) {
         term(std::true_type(), x, t, z, s, zt, sx, st, zs);
     };
-    auto wave_sums = [&](bool ws, float z0, float s0, float zt0, float sx0, float st0, float zs0) {
-        Z = wave_sum(z0);
-        if (ws) S = wave_sum(s0);
-        if (TMODE != TM_NONE) {
-            Zt = wave_sum(zt0);
-            SX = wave_sum(sx0);
+    auto wave_sums = [&](bool ws, Acc z0, float s0, Acc zt0, float sx0, float st0, Acc zs0) {
+        if constexpr (HP) {
+            split_hl(wave_sum_d(z0), Z, Zl);
+            if (TMODE != TM_NONE) split_hl(wave_sum_d(zt0), Zt, Ztl);
+            if (is_hinton(TMODE)) split_hl(wave_sum_d(zs0), Zs, Zsl);
+        } else {
+            Z = wave_sum(z0);
+            if (TMODE != TM_NONE) Zt = wave_sum(zt0);
+            if (is_hinton(TMODE)) Zs = wave_sum(zs0);
         }
+        if (ws) S = wave_sum(s0);
+        if (TMODE != TM_NONE) SX = wave_sum(sx0);
         if (has_st(TMODE)) St = wave_sum(st0);
-        if (is_hinton(TMODE)) Zs = wave_sum(zs0);
     };
     // one call site per variant (below), so the slice stays in registers
     auto sweep = [&](auto want_s_tag) __attribute__((always_inline)) {
         constexpr bool WS = decltype(want_s_tag)::value;
-        auto acc = [&](float x, float t, float& z, float& s, float& zt, float& sx, float& st, float& zs) {
+        auto acc = [&](float x, float t, Acc& z, float& s, Acc& zt, float& sx, float& st, Acc& zs) {
             term(want_s_tag, x, t, z, s, zt, sx, st, zs);
         };
-        float z0 = 0.f, s0 = 0.f, zt0 = 0.f, sx0 = 0.f, st0 = 0.f, zs0 = 0.f;
+        Acc z0 = 0, zt0 = 0, zs0 = 0;
+        float s0 = 0.f, sx0 = 0.f, st0 = 0.f;
 #pragma unroll
         for (int v = 0; v < NVEC; ++v) {
             if (tid < nv - v * BLOCK) {
-                float z = 0.f, s = 0.f, zt = 0.f, sx = 0.f, st = 0.f, zs = 0.f;
+                if constexpr (HP) {
+                    // fp64 sums: straight into the thread's totals
 #pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    acc(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z, s, zt, sx, st, zs);
-                z0 += z; s0 += s; zt0 += zt; sx0 += sx; st0 += st; zs0 += zs;
+                    for (int e = 0; e < VEC; ++e)
+                        acc(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z0, s0, zt0, sx0, st0,
+                            zs0);
+                } else {
+                    Acc z = 0, zt = 0, zs = 0;
+                    float s = 0.f, sx = 0.f, st = 0.f;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        acc(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z, s, zt, sx, st, zs);
+                    z0 += z; s0 += s; zt0 += zt; sx0 += sx; st0 += st; zs0 += zs;
+                }
             }
         }
         if (has_e) acc(xe, te, z0, s0, zt0, sx0, st0, zs0);
@@ -942,8 +1061,9 @@ void fused_kernel(const FusedParams p) {
             if (TMODE != TM_NONE) mt = fmaxf(mt, te);
         }
         M = shift_of(wave_max(mx));
-        if (TMODE != TM_NONE) Mt = wave_max(mt) * p.K2;
-        float z0 = 0.f, s0 = 0.f, zt0 = 0.f, sx0 = 0.f, st0 = 0.f, zs0 = 0.f;
+        if (TMODE != TM_NONE) Mt = shift_int<HP>(wave_max(mt) * p.K2);
+        Acc z0 = 0, zt0 = 0, zs0 = 0;
+        float s0 = 0.f, sx0 = 0.f, st0 = 0.f;
         for (int i = tid; i < nv; i += BLOCK) {
             const u32x4 w = xv[i];
             u32x4 wt = {0u, 0u, 0u, 0u};
@@ -963,6 +1083,11 @@ void fused_kernel(const FusedParams p) {
         s_rec[wave][5] = SX;
         s_rec[wave][6] = St;
         s_rec[wave][7] = Zs;
+        if (HP) {
+            s_rec[wave][8] = Zl;
+            s_rec[wave][9] = Ztl;
+            s_rec[wave][10] = Zsl;
+        }
     }
     __syncthreads();
 
@@ -993,23 +1118,34 @@ void fused_kernel(const FusedParams p) {
                     if (has_st(TMODE)) wr.St = s_rec[w][6];
                     if (is_hinton(TMODE)) wr.Zs = s_rec[w][7];
                 }
+                if (HP) {
+                    wr.Zl = s_rec[w][8];
+                    if (TMODE != TM_NONE) wr.Ztl = s_rec[w][9];
+                    if (is_hinton(TMODE)) wr.Zsl = s_rec[w][10];
+                }
                 if (wr.Z == 0.f) wr = rec_empty();
             }
-            wr = rec_reduce16<TMODE>(wr, p.beta, NW);
+            wr = rec_reduce16<TMODE, HP>(wr, p.beta, NW, p.betad);
         }
         if (p.chunks > 1) {
             // statistics this mode exchanges: M, Z, S (+ Mt, Zt, SX (+ St) (+ Zs)),
-            // packed in that order
-            constexpr int NXW = xwords_used(TMODE);
+            // packed in that order, then (fp32 instances) Zl (+ Ztl (+ Zsl))
+            constexpr int NX0 = xwords_used(TMODE);
+            constexpr int NXW = xwords_used(TMODE, HP);
+            constexpr int XS = xwords_stride(HP);
             constexpr int POS_ZS = has_st(TMODE) ? 7 : 6;
             const uint64_t epoch = (uint64_t)p.ctrl[CTRL_EPOCH] << 32;
             const uint32_t spin_limit = p.ctrl[CTRL_SPIN];
             const bool held = (uint32_t)row == p.ctrl[CTRL_HOLD_ROW] && (uint32_t)c == p.ctrl[CTRL_HOLD_CHUNK];
-            uint64_t* words = p.chunk_words + (int64_t)row * p.chunks * XWORDS;
-            uint64_t* mine = words + c * XWORDS;
+            uint64_t* words = p.chunk_words + (int64_t)row * p.chunks * XS;
+            uint64_t* mine = words + c * XS;
             if (lane == 0 && !held) {
-                const float f[XWORDS] = {wr.M, wr.Z, wr.S, wr.Mt, wr.Zt, wr.SX,
-                                         has_st(TMODE) ? wr.St : wr.Zs, wr.Zs};
+                float f[XS] = {wr.M, wr.Z, wr.S, wr.Mt, wr.Zt, wr.SX, has_st(TMODE) ? wr.St : wr.Zs, wr.Zs};
+                if (HP) {
+                    f[NX0] = wr.Zl;
+                    if (TMODE != TM_NONE) f[NX0 + 1] = wr.Ztl;
+                    if (is_hinton(TMODE)) f[NX0 + 2] = wr.Zsl;
+                }
 #pragma unroll
                 for (int i = 0; i < NXW; ++i)
                     __hip_atomic_store(mine + i, epoch | __float_as_uint(f[i]), __ATOMIC_RELAXED,
@@ -1017,7 +1153,7 @@ void fused_kernel(const FusedParams p) {
             }
             // lane l polls word (l % NXW) of chunk (l / NXW)
             const int nwords = p.chunks * NXW;
-            const int lw = (lane / NXW) * XWORDS + lane % NXW;
+            const int lw = (lane / NXW) * XS + lane % NXW;
             uint64_t w = 0;
             uint32_t spins = 0;
             bool gave_up = false;
@@ -1054,14 +1190,22 @@ void fused_kernel(const FusedParams p) {
                     if (has_st(TMODE)) cr.St = s_xw[l * NXW + 6];
                     if (is_hinton(TMODE)) cr.Zs = s_xw[l * NXW + POS_ZS];
                 }
+                if (HP) {
+                    cr.Zl = s_xw[l * NXW + NX0];
+                    if (TMODE != TM_NONE) cr.Ztl = s_xw[l * NXW + NX0 + 1];
+                    if (is_hinton(TMODE)) cr.Zsl = s_xw[l * NXW + NX0 + 2];
+                }
                 if (cr.Z == 0.f) cr = rec_empty();
             }
-            wr = rec_reduce16<TMODE>(cr, p.beta, p.chunks);
+            wr = rec_reduce16<TMODE, HP>(cr, p.beta, p.chunks, p.betad);
         }
         if (lane == 0) {
             s_fin[0] = wr.M; s_fin[1] = wr.Z; s_fin[2] = wr.S;
             s_fin[3] = wr.Mt; s_fin[4] = wr.Zt; s_fin[5] = wr.SX; s_fin[6] = wr.St;
             s_fin[7] = wr.Zs;
+            if (HP) {
+                s_fin[8] = wr.Zl; s_fin[9] = wr.Ztl; s_fin[10] = wr.Zsl;
+            }
             // per-row record for the batch reduction (s_row[0] was written by
             // this thread)
             if (c == 0) {
@@ -1071,12 +1215,19 @@ void fused_kernel(const FusedParams p) {
                 out[R_ZS] = wr.Zs;
                 out[R_XY] = s_row[0];
                 out[R_VALID] = 1.0f;
+                out[R_ZL] = HP ? wr.Zl : 0.f;
+                out[R_ZTL] = HP ? wr.Ztl : 0.f;
+                out[R_ZSL] = HP ? wr.Zsl : 0.f;
             }
         }
     }
     __syncthreads();
     r.M = s_fin[0]; r.Z = s_fin[1]; r.S = s_fin[2];
     r.Mt = s_fin[3]; r.Zt = s_fin[4]; r.SX = s_fin[5]; r.St = s_fin[6]; r.Zs = s_fin[7];
+    r.Zl = 0.f; r.Ztl = 0.f; r.Zsl = 0.f;
+    if (HP) {
+        r.Zl = s_fin[8]; r.Ztl = s_fin[9]; r.Zsl = s_fin[10];
+    }
     }   // pass 1
     if (p.grad == nullptr) return;
 
@@ -1178,8 +1329,8 @@ __global__ __launch_bounds__(kRowwiseBlock) void rowwise_kernel(const FusedParam
     constexpr int ES = T::ESIZE;
     constexpr bool HP = std::is_same<T, F32T>::value;
     __shared__ float s_m[NW][2];
-    __shared__ float s_rec[NW][8];
-    __shared__ float s_fin[8];
+    __shared__ float s_rec[NW][11];
+    __shared__ float s_fin[11];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -1207,6 +1358,7 @@ __global__ __launch_bounds__(kRowwiseBlock) void rowwise_kernel(const FusedParam
         const float* rec = p.row_rec + row * REC;
         r.M = rec[R_M]; r.Z = rec[R_Z]; r.S = rec[R_S];
         r.Mt = rec[R_MT]; r.Zt = rec[R_ZT]; r.SX = rec[R_SX]; r.St = rec[R_ST]; r.Zs = rec[R_ZS];
+        r.Zl = rec[R_ZL]; r.Ztl = rec[R_ZTL]; r.Zsl = rec[R_ZSL];
     } else {
         float mx = kNegInf, mt = kNegInf;
         for (int64_t j = tid; j < V; j += kRowwiseBlock) {
@@ -1226,25 +1378,33 @@ __global__ __launch_bounds__(kRowwiseBlock) void rowwise_kernel(const FusedParam
             mx = fmaxf(mx, s_m[w][0]);
             mt = fmaxf(mt, s_m[w][1]);
         }
-        const float M = SOFTCAP ? (p.cap * hl_tanh(mx * p.kc)) * kLog2e : mx * p.K1;
-        const float Mt = TMODE != TM_NONE ? mt * p.K2 : 0.f;
-        float z = 0.f, sv = 0.f, zt = 0.f, sx = 0.f, st = 0.f, zs = 0.f;
+        const float M = shift_int<HP>(SOFTCAP ? (p.cap * hl_tanh(mx * p.kc)) * kLog2e : mx * p.K1);
+        const float Mt = TMODE != TM_NONE ? shift_int<HP>(mt * p.K2) : 0.f;
+        using Acc = typename std::conditional<HP, double, float>::type;
+        Acc z = 0, zt = 0, zs = 0;
+        float sv = 0.f, sx = 0.f, st = 0.f;
         for (int64_t j = tid; j < V; j += kRowwiseBlock) {
             const float x = T::load1(xrow, j);
             const float t = TMODE != TM_NONE ? T::load1(trow, j) : 0.f;
             stat_term<TMODE, SOFTCAP, true, HP>(p, M, Mt, x, t, z, sv, zt, sx, st, zs);
         }
-        z = wave_sum(z);
-        sv = wave_sum(sv);
-        if (TMODE != TM_NONE) {
-            zt = wave_sum(zt);
-            sx = wave_sum(sx);
+        float zh = 0.f, zl = 0.f, zth = 0.f, ztl = 0.f, zsh = 0.f, zsl = 0.f;
+        if constexpr (HP) {
+            split_hl(wave_sum_d(z), zh, zl);
+            if (TMODE != TM_NONE) split_hl(wave_sum_d(zt), zth, ztl);
+            if (is_hinton(TMODE)) split_hl(wave_sum_d(zs), zsh, zsl);
+        } else {
+            zh = wave_sum(z);
+            if (TMODE != TM_NONE) zth = wave_sum(zt);
+            if (is_hinton(TMODE)) zsh = wave_sum(zs);
         }
+        sv = wave_sum(sv);
+        if (TMODE != TM_NONE) sx = wave_sum(sx);
         if (has_st(TMODE)) st = wave_sum(st);
-        if (is_hinton(TMODE)) zs = wave_sum(zs);
         if (lane == 0) {
-            s_rec[wave][0] = M; s_rec[wave][1] = z; s_rec[wave][2] = sv; s_rec[wave][3] = Mt;
-            s_rec[wave][4] = zt; s_rec[wave][5] = sx; s_rec[wave][6] = st; s_rec[wave][7] = zs;
+            s_rec[wave][0] = M; s_rec[wave][1] = zh; s_rec[wave][2] = sv; s_rec[wave][3] = Mt;
+            s_rec[wave][4] = zth; s_rec[wave][5] = sx; s_rec[wave][6] = st; s_rec[wave][7] = zsh;
+            s_rec[wave][8] = zl; s_rec[wave][9] = ztl; s_rec[wave][10] = zsl;
         }
         __syncthreads();
         if (tid == 0) {
@@ -1259,21 +1419,25 @@ __global__ __launch_bounds__(kRowwiseBlock) void rowwise_kernel(const FusedParam
                 } else {
                     b.Mt = 0.f; b.Zt = 0.f; b.SX = 0.f; b.St = 0.f; b.Zs = 0.f;
                 }
+                b.Zl = s_rec[w][8]; b.Ztl = s_rec[w][9]; b.Zsl = s_rec[w][10];
                 if (b.Z == 0.f) b = rec_empty();
-                acc = rec_merge<TMODE>(acc, b, p.beta);
+                acc = rec_merge<TMODE, HP>(acc, b, p.beta, p.betad);
             }
             s_fin[0] = acc.M; s_fin[1] = acc.Z; s_fin[2] = acc.S; s_fin[3] = acc.Mt;
             s_fin[4] = acc.Zt; s_fin[5] = acc.SX; s_fin[6] = acc.St; s_fin[7] = acc.Zs;
+            s_fin[8] = acc.Zl; s_fin[9] = acc.Ztl; s_fin[10] = acc.Zsl;
             float* out = p.row_rec + row * REC;
             out[R_M] = acc.M; out[R_Z] = acc.Z; out[R_S] = acc.S;
             out[R_MT] = acc.Mt; out[R_ZT] = acc.Zt; out[R_SX] = acc.SX; out[R_ST] = acc.St;
             out[R_ZS] = acc.Zs;
             out[R_XY] = xy;
             out[R_VALID] = 1.0f;
+            out[R_ZL] = acc.Zl; out[R_ZTL] = acc.Ztl; out[R_ZSL] = acc.Zsl;
         }
         __syncthreads();
         r.M = s_fin[0]; r.Z = s_fin[1]; r.S = s_fin[2]; r.Mt = s_fin[3];
         r.Zt = s_fin[4]; r.SX = s_fin[5]; r.St = s_fin[6]; r.Zs = s_fin[7];
+        r.Zl = s_fin[8]; r.Ztl = s_fin[9]; r.Zsl = s_fin[10];
     }
     if (grow == nullptr) return;
 
@@ -1318,17 +1482,19 @@ hipError_t launch_rowwise(const FusedParams& p, dim3 grid, hipStream_t s) {
 // order. Same record format as the fused kernel.
 // ---------------------------------------------------------------------------
 // Batches of 4 vectors (2 per tensor with a teacher) keep two double-buffered
-// batches within 64 VGPRs, so two 1024-thread workgroups share a CU.
+// batches within 64 VGPRs, so two 1024-thread workgroups share a CU (the fp32
+// instances, whose normalizer sums run in fp64, take 128 VGPRs and one).
 constexpr int kStreamBlock = 1024;
 
 template <typename T, int TMODE, bool SOFTCAP>
-__global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const FusedParams p) {
+__global__ __launch_bounds__(kStreamBlock, (std::is_same<T, F32T>::value ? 4 : 8)) void stream_stats_kernel(
+    const FusedParams p) {
     constexpr int VEC = T::VEC;
     constexpr int ES = T::ESIZE;
     constexpr int NW = kStreamBlock / 64;
     constexpr int SU = TMODE == TM_NONE ? 4 : 2;
     constexpr bool HP = std::is_same<T, F32T>::value;
-    __shared__ float s_rec[16][8];
+    __shared__ float s_rec[16][11];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -1393,12 +1559,14 @@ __global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const Fus
     const float mx0 = wave_max(mx);
     const float mt0 = TMODE != TM_NONE ? wave_max(mt) : 0.f;
     auto shift_of = [&](float m) -> float {
-        return SOFTCAP ? (p.cap * hl_tanh(m * p.kc)) * kLog2e : m * p.K1;
+        return shift_int<HP>(SOFTCAP ? (p.cap * hl_tanh(m * p.kc)) * kLog2e : m * p.K1);
     };
     float M = shift_of(mx0);
-    float Mt = TMODE != TM_NONE ? mt0 * p.K2 : 0.f;
+    float Mt = TMODE != TM_NONE ? shift_int<HP>(mt0 * p.K2) : 0.f;
     const bool early = mx0 != kNegInf && (TMODE == TM_NONE || mt0 != kNegInf);
-    float z = 0.f, sv = 0.f, zt = 0.f, sx = 0.f, st = 0.f, zs = 0.f;
+    using Acc = typename std::conditional<HP, double, float>::type;
+    Acc z = 0, zt = 0, zs = 0;
+    float sv = 0.f, sx = 0.f, st = 0.f;
     if (early) {
         for (int64_t b = 0; b < nbatch; ++b) {
             u32x4 xn[SU], tn[TMODE != TM_NONE ? SU : 1];
@@ -1423,20 +1591,25 @@ __global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const Fus
         }
         if (has_e) stat_term<TMODE, SOFTCAP, true, HP>(p, M, Mt, xe, te, z, sv, zt, sx, st, zs);
     }
+    float zh = 0.f, zl = 0.f, zth = 0.f, ztl = 0.f, zsh = 0.f, zsl = 0.f;
     auto wave_sums = [&]() {
-        z = wave_sum(z);
-        sv = wave_sum(sv);
-        if (TMODE != TM_NONE) {
-            zt = wave_sum(zt);
-            sx = wave_sum(sx);
+        if constexpr (HP) {
+            split_hl(wave_sum_d(z), zh, zl);
+            if (TMODE != TM_NONE) split_hl(wave_sum_d(zt), zth, ztl);
+            if (is_hinton(TMODE)) split_hl(wave_sum_d(zs), zsh, zsl);
+        } else {
+            zh = wave_sum(z);
+            if (TMODE != TM_NONE) zth = wave_sum(zt);
+            if (is_hinton(TMODE)) zsh = wave_sum(zs);
         }
+        sv = wave_sum(sv);
+        if (TMODE != TM_NONE) sx = wave_sum(sx);
         if (has_st(TMODE)) st = wave_sum(st);
-        if (is_hinton(TMODE)) zs = wave_sum(zs);
     };
     wave_sums();
     constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
-    if (!early || !(z <= kSumLimit) || (TMODE != TM_NONE && !(zt <= kSumLimit)) ||
-        (is_hinton(TMODE) && !(zs <= kSumLimit))) {
+    if (!early || !(zh <= kSumLimit) || (TMODE != TM_NONE && !(zth <= kSumLimit)) ||
+        (is_hinton(TMODE) && !(zsh <= kSumLimit))) {
         // rare: the true maxima of the wave's vectors, then the sums again
         mx = kNegInf;
         mt = kNegInf;
@@ -1449,8 +1622,9 @@ __global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const Fus
             if (TMODE != TM_NONE) mt = fmaxf(mt, te);
         }
         M = shift_of(wave_max(mx));
-        if (TMODE != TM_NONE) Mt = wave_max(mt) * p.K2;
-        z = sv = zt = sx = st = zs = 0.f;
+        if (TMODE != TM_NONE) Mt = shift_int<HP>(wave_max(mt) * p.K2);
+        z = zt = zs = 0;
+        sv = sx = st = 0.f;
         for (int64_t i = tid; i < nbv; i += kStreamBlock) {
             const u32x4 w = xv[i];
             u32x4 wt = {0u, 0u, 0u, 0u};
@@ -1463,8 +1637,11 @@ __global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const Fus
         wave_sums();
     }
     if (lane == 0) {
-        s_rec[wave][0] = M; s_rec[wave][1] = z; s_rec[wave][2] = sv; s_rec[wave][3] = Mt;
-        s_rec[wave][4] = zt; s_rec[wave][5] = sx; s_rec[wave][6] = st; s_rec[wave][7] = zs;
+        s_rec[wave][0] = M; s_rec[wave][1] = zh; s_rec[wave][2] = sv; s_rec[wave][3] = Mt;
+        s_rec[wave][4] = zth; s_rec[wave][5] = sx; s_rec[wave][6] = st; s_rec[wave][7] = zsh;
+        if (HP) {
+            s_rec[wave][8] = zl; s_rec[wave][9] = ztl; s_rec[wave][10] = zsl;
+        }
     }
     __syncthreads();
     if (wave == 0) {
@@ -1481,9 +1658,14 @@ __global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const Fus
                 if (has_st(TMODE)) wr.St = s_rec[w][6];
                 if (is_hinton(TMODE)) wr.Zs = s_rec[w][7];
             }
+            if (HP) {
+                wr.Zl = s_rec[w][8];
+                if (TMODE != TM_NONE) wr.Ztl = s_rec[w][9];
+                if (is_hinton(TMODE)) wr.Zsl = s_rec[w][10];
+            }
             if (wr.Z == 0.f) wr = rec_empty();
         }
-        wr = rec_reduce16<TMODE>(wr, p.beta, NW);
+        wr = rec_reduce16<TMODE, HP>(wr, p.beta, NW, p.betad);
         if (lane == 0) {
             float* out = p.row_rec + row * REC;
             out[R_M] = wr.M; out[R_Z] = wr.Z; out[R_S] = wr.S;
@@ -1491,6 +1673,9 @@ __global__ __launch_bounds__(kStreamBlock, 8) void stream_stats_kernel(const Fus
             out[R_ZS] = wr.Zs;
             out[R_XY] = T::from_raw(xy_b);
             out[R_VALID] = 1.0f;
+            out[R_ZL] = HP ? wr.Zl : 0.f;
+            out[R_ZTL] = HP ? wr.Ztl : 0.f;
+            out[R_ZSL] = HP ? wr.Zsl : 0.f;
         }
     }
 }

@@ -53,15 +53,6 @@ hl_status hip_fail(const char* where, hipError_t e) {
     return HL_ERR_HIP;
 }
 
-// hi + lo split of a positive constant: hi is the float just below v (so
-// that lo = v - hi is > 0 even when v is a float), lo the rest rounded.
-void split_pos(double v, float& hi, float& lo) {
-    float h = (float)v;
-    if ((double)h >= v) h = std::nextafterf(h, 0.0f);
-    hi = h;
-    lo = (float)(v - (double)h);
-}
-
 constexpr uint32_t kDistillBits = HL_FKL | HL_RKL | HL_FDCE;
 constexpr uint32_t kPolicyBits = HL_GRPO | HL_GSPO;
 constexpr uint32_t kLossBits = HL_CE | HL_ZLOSS | kDistillBits | kPolicyBits | HL_ENTROPY;
@@ -88,7 +79,8 @@ Layout layout_for(const hl_plan_s* p, int64_t n) {
     const size_t N = n > 0 ? (size_t)n : 0;
     L.ctrl = 0;
     L.chunk_rec = align256(NCTRL * sizeof(uint32_t));
-    const size_t rec_bytes = exchange_chunks(p) > 1 ? N * p->geo.chunks * XWORDS * sizeof(uint64_t) : 0;
+    const size_t rec_bytes =
+        exchange_chunks(p) > 1 ? N * p->geo.chunks * xwords_stride(p->dtype == HL_F32) * sizeof(uint64_t) : 0;
     L.row_rec = L.chunk_rec + align256(rec_bytes);
     L.rows = L.row_rec + align256(N * REC * sizeof(float));
     L.partials = L.rows + align256(N * NCOL * sizeof(float));
@@ -179,7 +171,7 @@ Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C, int block = 0) {
 // threads and at most 10 + 10 vectors (about 113 VGPRs). Short rows use one
 // 256-thread workgroup.
 hl_status choose(hl_plan_s* p) {
-    const int max_chunks = max_chunks_for(p->tmode);
+    const int max_chunks = max_chunks_for(p->tmode, p->dtype == HL_F32);
     if (p->forced_chunks > max_chunks) return HL_ERR_UNSUPPORTED;
     if (p->forced_chunks > 0) {
         Geometry g = geometry_for(p->V, p->dtype, p->tmode, p->forced_chunks, p->forced_block);
@@ -322,7 +314,7 @@ hl_status enqueue_call(hl_plan_t plan, const CallArgs& a, void* wsv, bool reset,
     cp.hold_chunk = plan->withhold_row < 0 ? 0xffffffffu : (uint32_t)plan->withhold_chunk;
     cp.vec = (labels != nullptr && aligned16(labels) && (mask == nullptr || aligned16(mask))) ? 1 : 0;
     cp.fill = chunk_words;
-    cp.fill_words = CX > 1 ? n_rows * CX * XWORDS : 0;
+    cp.fill_words = CX > 1 ? n_rows * CX * xwords_stride(plan->dtype == HL_F32) : 0;
     hipError_t e = launch_count(cp, stream);
     if (e != hipSuccess) return hip_fail("count kernel launch", e);
 
@@ -350,14 +342,12 @@ hl_status enqueue_call(hl_plan_t plan, const CallArgs& a, void* wsv, bool reset,
         fp.flags = f;
         constexpr double kLog2eD = 1.4426950408889634074;
         fp.k = plan->logit_scale;
-        split_pos((double)plan->logit_scale * kLog2eD, fp.K1, fp.K1l);
-        split_pos(kLog2eD / (double)plan->temperature, fp.K2, fp.K2l);
-        if (f & HL_HINTON) {
-            split_pos(1.0 / (double)plan->temperature, fp.beta, fp.beta_l);
-        } else {
-            fp.beta = 1.0f;
-            fp.beta_l = 0.0f;
-        }
+        fp.K1d = (double)plan->logit_scale * kLog2eD;
+        fp.K2d = kLog2eD / (double)plan->temperature;
+        fp.betad = (f & HL_HINTON) ? 1.0 / (double)plan->temperature : 1.0;
+        fp.K1 = (float)fp.K1d;
+        fp.K2 = (float)fp.K2d;
+        fp.beta = (float)fp.betad;
         fp.tau = plan->temperature;
         fp.cap = plan->softcap;
         fp.kc = plan->softcap > 0.f ? plan->logit_scale / plan->softcap : 0.f;

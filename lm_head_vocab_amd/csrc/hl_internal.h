@@ -18,8 +18,12 @@ constexpr int base_mode(int t) { return is_hinton(t) ? t - 3 : t; }
 constexpr bool fkl_like(int t) { return base_mode(t) == TM_FKL || base_mode(t) == TM_FDCE; }
 // Modes that carry the teacher entropy sum St.
 constexpr bool has_st(int t) { return base_mode(t) == TM_FDCE; }
-// Statistics a chunk publishes: M, Z, S (+ Mt, Zt, SX (+ St) (+ Zs)).
-constexpr int xwords_used(int t) { return t == TM_NONE ? 3 : 6 + (has_st(t) ? 1 : 0) + (is_hinton(t) ? 1 : 0); }
+// Statistics a chunk publishes: M, Z, S (+ Mt, Zt, SX (+ St) (+ Zs)); the fp32
+// instances (hp) also carry the low parts of the normalizers Z (+ Zt (+ Zs)).
+constexpr int xwords_used(int t, bool hp = false) {
+    return (t == TM_NONE ? 3 : 6 + (has_st(t) ? 1 : 0) + (is_hinton(t) ? 1 : 0)) +
+           (hp ? (t == TM_NONE ? 1 : (is_hinton(t) ? 3 : 2)) : 0);
+}
 
 // Loss bits (same values as the public HL_* flags).
 enum : uint32_t {
@@ -43,9 +47,12 @@ constexpr int NSCALARS = 13;
 //   St = sum 2^(U_j - Mt) (U_j - Mt), the teacher entropy sum (FDCE only).
 //   Zs = sum 2^((A_j - M) b), b = 1 / tau: the tempered student's sum
 //        (Hinton modes only; its shift is M b).
+//   Zl, Ztl, Zsl: the fp32 instances keep the normalizers Z, Zt, Zs as
+//        hi + lo pairs (sums and merges in fp64, carried as two floats);
+//        0 in every other instance.
 // The per-row record written by the fused kernel adds the raw label logit
 // and a valid flag.
-enum RecField : int { R_M = 0, R_Z, R_S, R_MT, R_ZT, R_SX, R_ST, R_XY, R_VALID, R_ZS, REC };
+enum RecField : int { R_M = 0, R_Z, R_S, R_MT, R_ZT, R_SX, R_ST, R_XY, R_VALID, R_ZS, R_ZL, R_ZTL, R_ZSL, REC };
 
 // Control words at the start of the workspace. CTRL_NSEG counts the GSPO
 // segments that hold a valid row. CTRL_ERROR: 1 = a split-vocab row never saw
@@ -68,13 +75,19 @@ enum Ctrl : int {
 // act * A * s / n_i, and the valid-token count n_i.
 enum SegField : int { SG_LOSS = 0, SG_RATIO, SG_CLIP, SG_K3, SG_ADV, SG_NONEMPTY, SG_DERIV, SG_COUNT, SEGREC };
 
-// Split-vocab exchange: each chunk publishes up to 8 statistics as 64-bit
-// words (float bits low, call epoch high), XWORDS apart. One wave polls all
-// of a row's words, so a mode allows at most 64 / xwords_used chunks.
+// Split-vocab exchange: each chunk publishes its statistics as 64-bit words
+// (float bits low, call epoch high), XWORDS apart (XWORDS_HP in the fp32
+// instances, up to 11 words). One wave polls all of a row's words, so a mode
+// allows at most 64 / xwords_used chunks.
 constexpr int XWORDS = 8;
+constexpr int XWORDS_HP = 16;
+constexpr int xwords_stride(bool hp) { return hp ? XWORDS_HP : XWORDS; }
 constexpr int kMaxChunks = 9;
-constexpr int max_chunks_for(int t) { return 64 / xwords_used(t) < kMaxChunks ? 64 / xwords_used(t) : kMaxChunks; }
+constexpr int max_chunks_for(int t, bool hp = false) {
+    return 64 / xwords_used(t, hp) < kMaxChunks ? 64 / xwords_used(t, hp) : kMaxChunks;
+}
 static_assert(kMaxChunks * xwords_used(TM_FDCE) <= 64, "one wave polls every exchanged word of a row");
+static_assert(xwords_used(TM_FDCE_H, true) <= XWORDS_HP && xwords_used(TM_FDCE_H) <= XWORDS, "words per chunk");
 
 struct Geometry {
     int chunks;      // workgroups per row
@@ -91,7 +104,7 @@ struct FusedParams {
     const float* advantages;
     void* grad;
     float* row_rec;           // [N, REC]
-    uint64_t* chunk_words;    // [N, C, XWORDS]
+    uint64_t* chunk_words;    // [N, C, XWORDS] (XWORDS_HP in the fp32 instances)
     uint32_t* ctrl;           // [NCTRL]
     const float* row_coef;    // [N] GSPO label-column coefficient per row, or nullptr
     int load_mode;            // 1: statistics from row_rec (second launch of a GSPO call)
@@ -102,13 +115,10 @@ struct FusedParams {
     int accumulate;
     uint32_t flags;
     float k;          // logit scale
-    float K1;         // k * log2(e), rounded toward zero
-    float K2;         // log2(e) / temperature, rounded toward zero
+    float K1;         // k * log2(e)
+    float K2;         // log2(e) / temperature
     float beta;       // 1 / temperature for the tempered distillation student (Hinton modes), else 1
-    // Low parts (fp32 instances): K1 + K1l, K2 + K2l and beta + beta_l are the
-    // constants to about 2^-48 relative; every low part is > 0, so a -Inf
-    // logit still gives a -Inf exponent (never -Inf + Inf).
-    float K1l, K2l, beta_l;
+    double K1d, K2d, betad;   // the same three in fp64 (used by the fp32 instances)
     float tau;        // temperature (the Hinton gradient carries tau)
     float cap;        // softcap c (0 = off)
     float kc;         // k / c

@@ -73,13 +73,36 @@ def to_np(t):
     return None if t is None else t.detach().to("cpu", torch.float64).numpy()
 
 
+def _f32(v) -> float:
+    return float(np.float32(v))
+
+
 def spec_from(V, flags, w=None, **kw) -> oracle.Spec:
+    """The oracle's Spec for a plan. The C ABI takes every hyper-parameter
+    (weights, scale, divisor, temperature, eps, logit scale, softcap) as fp32,
+    so the plan holds their fp32 roundings; the oracle is evaluated at those
+    same values (at the unrounded ones a weight of 1.44 alone moves an fp32
+    gradient entry of magnitude 8 by 1.3e-6)."""
     w = w or {}
-    return oracle.Spec(V=V, flags=flags, w_ce=w.get("ce", 1.0), w_z=w.get("z", 0.0),
-                       w_distill=w.get("distill", 0.0), w_grpo=w.get("grpo", 0.0),
-                       grad_scale=w.get("grad_scale", 1.0), divisor=w.get("divisor", 0.0),
-                       temperature=kw.get("temperature", 1.0), eps=kw.get("eps", 0.2),
-                       logit_scale=kw.get("logit_scale", 1.0), softcap=kw.get("softcap", 0.0))
+    return oracle.Spec(V=V, flags=flags, w_ce=_f32(w.get("ce", 1.0)), w_z=_f32(w.get("z", 0.0)),
+                       w_distill=_f32(w.get("distill", 0.0)), w_grpo=_f32(w.get("grpo", 0.0)),
+                       grad_scale=_f32(w.get("grad_scale", 1.0)), divisor=_f32(w.get("divisor", 0.0)),
+                       temperature=_f32(kw.get("temperature", 1.0)), eps=_f32(kw.get("eps", 0.2)),
+                       logit_scale=_f32(kw.get("logit_scale", 1.0)), softcap=_f32(kw.get("softcap", 0.0)))
+
+
+def max_chunks(dtype: str, spec: oracle.Spec) -> int:
+    """Chunks per row the split-vocab exchange allows (the documented rule of
+    hl_plan_set_chunks): one wave polls every exchanged word of a row, at most
+    64, and a chunk exchanges 3 statistics student-only, 6 with a teacher,
+    one more for FDCE and one more for Hinton; fp32 plans also exchange the
+    low parts of their one to three normalizers. Never more than 9."""
+    teacher = bool(spec.flags & (oracle.FKL | oracle.RKL | oracle.FDCE))
+    hinton = teacher and spec.has(oracle.HINTON)
+    words = 3 if not teacher else 6 + int(spec.has(oracle.FDCE)) + int(hinton)
+    if dtype == "f32":
+        words += 1 if not teacher else (3 if hinton else 2)
+    return min(9, 64 // words)
 
 
 def make_plan(spec: oracle.Spec, dtype, chunks: int = 0) -> hl.Plan:
@@ -189,14 +212,6 @@ def assert_scalars(spec, got, ref, dtype, vals=None, valid=None, skip=(), x=None
     assert not bad, f"scalar errors above {rel}: {bad}\n got={got}\n ref={ref}"
 
 
-# fp32 gradient entries larger than F32_BIG in magnitude (a reading): 1e-6
-# absolute is less than two fp32 ulps there (ulp(4) = 4.8e-7), below what a
-# result normalised by fp32 softmax sums can hold (the sums carry about an
-# ulp themselves, the output rounding half an ulp), so such entries are held
-# to two ulps, 2^-22 relative. Every other fp32 entry: 1e-6 absolute.
-F32_BIG = 4.0
-
-
 def grad_check(got, ref, dtype, labels=None, valid=None, base=None):
     """Compare a gradient tensor with the oracle's. Returns a dict of metrics."""
     g = to_np(got)
@@ -205,12 +220,8 @@ def grad_check(got, ref, dtype, labels=None, valid=None, base=None):
     if dtype == "f32":
         d = np.abs(g - r)
         out["max_abs"] = float(np.max(d)) if g.size else 0.0
-        big = np.abs(r) > F32_BIG
-        if big.any():
-            out["max_rel_big"] = float(np.max(d[big] / np.abs(r[big])))
-            say(f"[f32-big] {int(big.sum())} entries above {F32_BIG}: max rel {out['max_rel_big']:.3e}")
-            assert out["max_rel_big"] <= 2.0 ** -22, out
-        assert (float(np.max(d[~big])) if (~big).any() else 0.0) <= TOL["f32"]["grad_abs"], out
+        out["max_ref"] = float(np.max(np.abs(r))) if r.size else 0.0
+        assert out["max_abs"] <= TOL["f32"]["grad_abs"], out
         return out
     diff = g - r
     den = np.sqrt(np.mean(r * r)) if r.size else 0.0

@@ -131,10 +131,10 @@ void enqueue_paths() {
     CHECK(g_last_count.fill_words == N * c * hl::XWORDS || c == 1);
     CHECK(hl_forward_backward(p, N, x, y, nullptr, t, old, adv, g, sc, nullptr) == HL_OK);
     CHECK(g_last_count.reset == 0);
-    // hi/lo constants: every low part > 0, hi + lo = the constant
-    CHECK(g_last_fused.K1l > 0.0f && g_last_fused.K2l > 0.0f);
-    CHECK(std::fabs(((double)g_last_fused.K1 + (double)g_last_fused.K1l) - 1.4426950408889634) < 1e-13);
-    CHECK(std::fabs(((double)g_last_fused.K2 + (double)g_last_fused.K2l) - 1.4426950408889634 / 2.0) < 1e-13);
+    // the exponent constants in fp64 and their fp32 roundings
+    CHECK(std::fabs(g_last_fused.K1d - 1.4426950408889634) < 1e-15);
+    CHECK(std::fabs(g_last_fused.K2d - 1.4426950408889634 / 2.0) < 1e-15);
+    CHECK(g_last_fused.K1 == (float)g_last_fused.K1d && g_last_fused.K2 == (float)g_last_fused.K2d);
     // the test hook reaches the count kernel's parameters
     CHECK(hl_plan_set_exchange_test(p, 64, 7, 1) == HL_OK);
     CHECK(hl_forward_backward(p, N, x, y, nullptr, t, old, adv, g, sc, nullptr) == HL_OK);

@@ -226,6 +226,22 @@ def test_hinton_plans_and_the_eight_statistic_chunk_cap():
         lib.hl_plan_destroy(h)
 
 
+def test_fp32_chunk_caps():
+    """fp32 plans also exchange the low parts of their normalizers (Z; + Zt
+    with a teacher; + Zs with Hinton), so their chunk caps are 64 // words:
+    9 student-only, 8 forward / reverse KL, 7 FDCE, 6 Hinton KL, 5 Hinton
+    FDCE."""
+    cases = [(hl.CE, 9), (hl.CE | hl.FKL, 8), (hl.CE | hl.RKL, 8), (hl.CE | hl.FDCE, 7),
+             (hl.CE | hl.FKL | hl.HINTON, 6), (hl.CE | hl.RKL | hl.HINTON, 6), (hl.CE | hl.FDCE | hl.HINTON, 5)]
+    for flags, cap in cases:
+        st, h = _plan(V=20011, dtype=hl.HL_F32, flags=flags, w=Weights(1, 0, 1, 0, 1, 0), tau=2.0)
+        assert st == hl.HL_OK
+        assert lib.hl_plan_set_chunks(h, cap) == hl.HL_OK, (flags, cap)
+        if cap < 9:
+            assert lib.hl_plan_set_chunks(h, cap + 1) == hl.HL_ERR_UNSUPPORTED, (flags, cap)
+        lib.hl_plan_destroy(h)
+
+
 def test_segment_call_host_checks_enqueue_nothing():
     st, h = _plan(V=64, flags=hl.CE | hl.GSPO | hl.RKL, w=Weights(1, 0, 1, 1, 1, 0))
     assert st == 0

@@ -43,7 +43,8 @@ def _expect_row_failed(plan, sc, g, row, n_valid, dtype_int):
 
 
 @pytest.mark.parametrize("case", [("bf16", "ce_fkl", 60013, 4), ("bf16", "grpo_z_ent", 151936, 2),
-                                  ("f32", "all_rkl", 30011, 3), ("bf16", "all_fdce_h", 20011, 8)],
+                                  ("f32", "all_rkl", 30011, 3), ("bf16", "all_fdce_h", 20011, 8),
+                                  ("f32", "all_fdce_h", 20011, 5)],
                          ids=lambda c: f"{c[0]}-{c[1]}-{c[3]}chunks")
 def test_withheld_chunk_gives_nan_then_recovers(case):
     dtype, combo, V, chunks = case

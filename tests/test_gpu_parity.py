@@ -21,7 +21,7 @@ import torch
 import lm_head_vocab_amd as hl
 import oracle
 import workloads
-from gpu_support import (TOL, assert_scalars, grad_check, make_plan, oracle_old_logprobs,
+from gpu_support import (TOL, assert_scalars, grad_check, make_plan, max_chunks, oracle_old_logprobs,
                          run_hip, run_oracle, say, spec_from, to_np, torch_old_logprobs)
 from oracle import SLOT
 
@@ -204,11 +204,12 @@ def test_forward_only_streaming(dtype, combo, shape):
 def test_split_vocab_variant(dtype, combo, chunks):
     # forced chunking exercises the cross-workgroup combine at small sizes;
     # fp32 teacher slices hold at most 8 vectors per tensor, so the wider
-    # fp32 rows are 60000 elements (two chunks of 1024 x 8 x 4)
+    # fp32 rows are 60000 elements (two chunks of 1024 x 8 x 4); a count above
+    # what the mode's exchange allows is taken at that maximum
     wide = 60000 if dtype == "f32" else 70000
     for V, N in ((20011, 7), (wide, 5)):
         spec, inp = _small(dtype, combo, N, V, seed=chunks * 100 + N, softcap=15.0, scale=0.8)
-        _check_small(spec, inp, dtype, chunks=chunks)
+        _check_small(spec, inp, dtype, chunks=min(chunks, max_chunks(dtype, spec)))
 
 
 @pytest.mark.parametrize("chunks", [2, 4, 8])
@@ -221,7 +222,7 @@ def test_split_vocab_short_rows(dtype, combo, V, chunks):
     discarded), head and tail elements sit with chunk 0, and every row still
     merges all of its chunks."""
     spec, inp = _small(dtype, combo, 9, V, seed=V * 10 + chunks, mask_frac=0.2, softcap=6.0, scale=0.9)
-    _check_small(spec, inp, dtype, chunks=chunks)
+    _check_small(spec, inp, dtype, chunks=min(chunks, max_chunks(dtype, spec)))
 
 
 @pytest.mark.parametrize("variant", [(2, 512), (4, 512), (3, 1024), (1, 1024), (8, 256)])
@@ -324,14 +325,15 @@ def test_split_vocab_accumulate_and_masking():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_hinton_split_vocab_and_temperatures(dtype, combo, chunks, tau):
     """The tempered student sums travel through the split-vocab exchange (up
-    to 8 chunks, the cap of the 8-statistic from-distribution mode). fp32
-    Hinton slices hold at most 4 vectors per tensor: the wider fp32 rows are
-    30011 elements (two chunks of 1024 x 4 x 4)."""
+    to 8 chunks, the cap of the 8-statistic from-distribution mode; fp32
+    plans, which also exchange the normalizers' low parts, up to their own
+    caps). fp32 Hinton slices hold at most 4 vectors per tensor: the wider
+    fp32 rows are 30011 elements (two chunks of 1024 x 4 x 4)."""
     wide = 30011 if dtype == "f32" else 70000
     for V, N in ((20011, 7), (wide, 5)):
         spec, inp = _small(dtype, combo, N, V, seed=chunks * 10 + N, softcap=15.0, scale=0.8,
                            temperature=tau, mask_frac=0.2)
-        _check_small(spec, inp, dtype, chunks=chunks)
+        _check_small(spec, inp, dtype, chunks=min(chunks, max_chunks(dtype, spec)))
 
 
 @pytest.mark.parametrize("combo", HINTON_COMBOS)
@@ -414,10 +416,13 @@ def test_outlier_logits(dtype, combo, chunks, mode):
 
 # the longest rows each mode supports: 9 chunks x 1024 threads x 20 vectors
 # (student), x 10 vectors (teacher), 8 chunks for from-distribution CE with
-# the Hinton temperature (8 exchanged statistics per chunk)
+# the Hinton temperature (8 exchanged statistics per chunk); fp32 teacher
+# slices of at most 8 vectors (4 Hinton) and the fp32 chunk caps (8 for the
+# KL modes, 5 for Hinton FDCE)
 MAX_V = [("bf16", "ce_z", 1_474_560, (9, 1024, 20)), ("bf16", "ce_z", 1_474_553, (9, 1024, 20)),
          ("f32", "ce_z", 737_280, (9, 1024, 20)), ("bf16", "all_rkl", 737_280, (9, 1024, 10)),
-         ("bf16", "all_fdce_h", 655_360, (8, 1024, 10))]
+         ("bf16", "all_fdce_h", 655_360, (8, 1024, 10)), ("f32", "ce_fkl", 262_144, (8, 1024, 8)),
+         ("f32", "all_fdce_h", 81_920, (5, 1024, 4))]
 
 
 @pytest.mark.parametrize("case", MAX_V, ids=[f"{d}-{c}-{v}" for d, c, v, _ in MAX_V])
@@ -432,7 +437,8 @@ def test_maximum_vocabulary(case):
 # one vector past the longest slices the chunk exchange serves: statistics
 # streamed, then the gradient from the fused kernel in load mode
 LONG_ROWS = [("bf16", "ce_z", 1_474_569, False), ("bf16", "all_rkl", 737_288, True),
-             ("f32", "ce_fkl", 368_644, False), ("bf16", "all_fdce_h", 655_368, False)]
+             ("f32", "ce_fkl", 368_644, False), ("bf16", "all_fdce_h", 655_368, False),
+             ("f32", "all_fdce_h", 81_924, False)]
 
 
 @pytest.mark.parametrize("case", LONG_ROWS, ids=[f"{d}-{c}-{v}" for d, c, v, _ in LONG_ROWS])
@@ -446,7 +452,7 @@ def test_rows_past_every_slice(case):
                        accumulate=acc, bad_labels=1, mask_frac=0.0)
     plan, _, _ = _check_small(spec, inp, dtype)
     d = plan.describe()
-    assert d["block"] == 1024 and d["chunks"] >= 8
+    assert d["block"] == 1024 and d["chunks"] > max_chunks(dtype, spec)
     _check_small(spec, inp, dtype, grad_mode="none")
     # the same rows with a gradient buffer misaligned against the logits: row-wise
     ref_sc, ref_g, _ = run_oracle(spec, inp)
