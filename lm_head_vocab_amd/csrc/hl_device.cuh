@@ -648,6 +648,67 @@ __device__ __forceinline__ CoefsFor<HP> row_coefs(const FusedParams& p, const Re
 }
 
 
+// Pass-2 constants with the probability coefficient folded into the
+// exponent (the 16-bit instances outside the Hinton modes). With A the
+// coefficient that multiplies q (alpha; in reverse KL rho2) and sA its sign,
+// each element's gradient is sA * h, where
+//   h = 2^(aq + log2|A|)                                (no teacher)
+//   h = 2^(aq + log2|A|) - sA sg 2^(up + log2|gam|)     (forward KL, FDCE)
+//   h = 2^(aq') (aq' - up'')                            (reverse KL)
+// with aq' = aq + log2|A| and up'' = up + log2|A| - c0 / rho2, so that
+// aq' - up'' = (aq - up) + c0 / rho2 and rho2 q (aq - up) + c0 q = sA h. The
+// sign is applied to the packed output (one xor per two elements, skipped
+// when sA = +1), so the multiply by the coefficient disappears. A zero
+// coefficient folds to 2^-Inf = 0, a NaN one to NaN. ok = false (reverse KL
+// with rho2 = 0 or not finite) selects the plain element path.
+struct Fold {
+    float sBq;       // student exponent offset + log2|A|
+    float sBp;       // teacher exponent offset (+ log2|gam|, or + log2|A| - c0 / rho2)
+    float m;         // forward KL / FDCE: -sA sg
+    float sA;        // +1 or -1
+    uint32_t flip;   // sign bits of two packed 16-bit values when sA = -1, else 0
+    bool ok;
+};
+
+template <int TMODE>
+__device__ __forceinline__ Fold fold_coefs(const Coefs& k) {
+    Fold f;
+    const float A = TMODE == TM_RKL ? k.rho2 : k.alpha;
+    f.sA = A < 0.f ? -1.f : 1.f;
+    f.flip = A < 0.f ? 0x80008000u : 0u;
+    const float lA = __builtin_amdgcn_logf(fabsf(A));
+    f.sBq = k.sB + lA;
+    f.sBp = 0.f;
+    f.m = 0.f;
+    f.ok = true;
+    if (fkl_like(TMODE)) {
+        f.sBp = k.sBt + __builtin_amdgcn_logf(fabsf(k.gam));
+        f.m = (k.gam < 0.f) == (A < 0.f) ? -1.f : 1.f;
+    } else if (TMODE == TM_RKL) {
+        f.sBp = k.sBt + lA - k.c0 / k.rho2;
+        f.ok = A != 0.f && __builtin_isfinite(A) && __builtin_isfinite(f.sBp);
+    }
+    return f;
+}
+
+// sA times the gradient of one element that is not the label (see Fold).
+template <int TMODE, bool SOFTCAP>
+__device__ __forceinline__ float grad_folded(const FusedParams& p, const Fold& f, float x, float t) {
+    float aq, r = 0.f;
+    if (SOFTCAP) {
+        r = cap_r(x, p.kc2);
+        aq = fmaf(r, -2.0f * p.cl, f.sBq);
+    } else {
+        aq = fmaf(x, p.K1, f.sBq);
+    }
+    const float q = fast_exp2(aq);
+    float h;
+    if (TMODE == TM_NONE) h = q;
+    else if (fkl_like(TMODE)) h = fmaf(f.m, fast_exp2(fmaf(t, p.K2, f.sBp)), q);
+    else h = q * (aq - fmaf(t, p.K2, f.sBp));
+    return SOFTCAP ? (r * fmaf(-4.0f, r, 4.0f)) * h : h;
+}
+
 // Gradient of one element; lab = the label-column coefficient at the label,
 // else 0. The fp32 instances (HP) compute in fp64 and return the unrounded
 // value (the caller adds the existing gradient, if any, and rounds once).
@@ -776,6 +837,7 @@ __device__ __forceinline__ void stat_term(const FusedParams& p, float M, float M
 // fused_kernel
 // ---------------------------------------------------------------------------
 
+
 // Waves per SIMD the register allocation must allow (the second
 // __launch_bounds__ argument): student-only slices of at most 10 vectors per
 // thread (8 with softcap) are held to 64 VGPRs, i.e. 8 waves per SIMD, so that
@@ -788,6 +850,19 @@ constexpr int min_waves_per_simd() {
     return (!std::is_same<T, F32T>::value && TMODE == TM_NONE && NVEC <= (SOFTCAP ? 8 : 10)) ? 8 : 4;
 }
 
+// Slots of the slice held in LDS instead of registers: 16-bit teacher
+// instances at 512 threads with slices of 9 register vectors plus up to 4
+// LDS vectors per tensor (NVEC 11..13; 2 x 4 x 512 x 16 B = 64 KiB of LDS,
+// so two workgroups still share a CU). A larger slice per workgroup means
+// fewer chunks per row and fewer exchanges; on the V = 151936 rows that
+// measured 4.5% faster for the Hinton modes (3 x 512 x 13 against
+// 4 x 512 x 10) and no faster for the others, so only the Hinton modes
+// instantiate them.
+template <typename T, int BLOCK, int NVEC, int TMODE>
+constexpr int lds_slots() {
+    return (!std::is_same<T, F32T>::value && TMODE != TM_NONE && BLOCK == 512 && NVEC > 10) ? NVEC - 9 : 0;
+}
+
 template <typename T, int BLOCK, int NVEC, int TMODE, bool SOFTCAP>
 __global__ __launch_bounds__(BLOCK, (min_waves_per_simd<T, BLOCK, NVEC, TMODE, SOFTCAP>()))
 void fused_kernel(const FusedParams p) {
@@ -796,6 +871,9 @@ void fused_kernel(const FusedParams p) {
     constexpr int NW = BLOCK / 64;
     constexpr bool HP = std::is_same<T, F32T>::value;   // fp32: exact shifts, hi + lo constants
     static_assert(NW <= 16, "at most 16 waves per workgroup");
+    constexpr int NL = lds_slots<T, BLOCK, NVEC, TMODE>();   // slots 0..NR-1 in registers, NR.. in LDS
+    constexpr int NR = NVEC - NL;
+    static_assert(NL <= 4 && NR >= 1, "slice split");
 
     __shared__ float s_rec[16][REC];
     __shared__ float s_fin[REC];
@@ -807,8 +885,10 @@ void fused_kernel(const FusedParams p) {
     // it as well (they share one counter); teacher instances whose slots fit
     // in 72 KiB of LDS stage the whole old slice there with direct-to-LDS
     // loads issued before the first store, one latency per workgroup.
-    constexpr bool STAGE_OLD = TMODE != TM_NONE && (size_t)NVEC * BLOCK * 16 <= 73728;
+    constexpr bool STAGE_OLD = TMODE != TM_NONE && NL == 0 && (size_t)NVEC * BLOCK * 16 <= 73728;
     __shared__ u32x4 s_old[STAGE_OLD ? NVEC : 1][STAGE_OLD ? BLOCK : 1];
+    // the LDS part of the slice: [logits slots..., teacher slots...][thread]
+    __shared__ u32x4 s_ext[NL > 0 ? 2 * NL : 1][NL > 0 ? BLOCK : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -911,11 +991,11 @@ void fused_kernel(const FusedParams p) {
     // arrived: timed on the student rows, the extra requests and the earlier
     // start were each about 1% slower, while on the teacher rows the early
     // start is 5-8% faster.
-    u32x4 xs[NVEC];
-    u32x4 ts[TMODE != TM_NONE ? NVEC : 1];
+    u32x4 xs[NR];
+    u32x4 ts[TMODE != TM_NONE ? NR : 1];
     if (TMODE == TM_NONE) {
 #pragma unroll
-        for (int v = 0; v < NVEC; ++v)
+        for (int v = 0; v < NR; ++v)
             if (tid < nv - v * BLOCK) xs[v] = ld_stream(xv + v * BLOCK + tid);
     } else {
         const bool body = nv > 0;
@@ -923,13 +1003,40 @@ void fused_kernel(const FusedParams p) {
         const u32x4* tb = body ? tv : reinterpret_cast<const u32x4*>(p.row_rec);
         const int lastv = body ? nv - 1 : 0;
 #pragma unroll
-        for (int v = 0; v < NVEC; ++v) {
+        for (int v = 0; v < NR; ++v) {
             int i = v * BLOCK + tid;
             i = i < lastv ? i : lastv;
             xs[v] = ld_stream(xb + i);
             ts[v] = ld_stream(tb + i);
         }
+        // LDS slots: direct-to-LDS loads after the register slots (each
+        // wave fills its own 64 x 16 B of every slot row, in lane order, and
+        // later reads back only its own lanes)
+#pragma unroll
+        for (int v = NR; v < NVEC; ++v) {
+            int i = v * BLOCK + tid;
+            i = i < lastv ? i : lastv;
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(xb + i),
+                                             (__attribute__((address_space(3))) void*)&s_ext[v - NR][wave * 64],
+                                             16, 0, 2);
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(tb + i),
+                                             (__attribute__((address_space(3))) void*)&s_ext[NL + v - NR][wave * 64],
+                                             16, 0, 2);
+        }
     }
+    // slot v of this thread: registers, or (after lds_ready) LDS
+    auto slot_x = [&](int v) -> u32x4 { return v < NR ? xs[v < NR ? v : 0] : s_ext[v >= NR ? v - NR : 0][tid]; };
+    auto slot_t = [&](int v) -> u32x4 {
+        if constexpr (TMODE == TM_NONE) return xs[0];
+        else return v < NR ? ts[v < NR ? v : 0] : s_ext[NL + (v >= NR ? v - NR : 0)][tid];
+    };
+    // the LDS slots have landed once this wave's vector loads are done
+    auto lds_ready = [&]() {
+        if constexpr (NL > 0) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unconstrained
+            asm volatile("" ::: "memory");
+        }
+    };
     if (tid < 3) s_row[tid] = tid == 0 ? T::from_raw(small_b) : __uint_as_float(small_b);
     if (p.load_mode && tid >= 8 && tid < 8 + REC) s_lrec[tid - 8] = __uint_as_float(small_b);
     const float xe = has_e ? T::from_raw(xe_b) : 0.f;
@@ -960,7 +1067,7 @@ void fused_kernel(const FusedParams p) {
         // fp32: the wave's exact maxima (its largest elements then sit at
         // offset ~0, where the fp32 offsets are exact)
 #pragma unroll
-        for (int v = 0; v < NVEC; ++v) {
+        for (int v = 0; v < NR; ++v) {   // (no LDS slots in the fp32 instances)
             if (tid < nv - v * BLOCK) {
                 mx = T::vmax(mx, xs[v]);
                 if (TMODE != TM_NONE) mt = T::vmax(mt, ts[v]);
@@ -1020,19 +1127,20 @@ void fused_kernel(const FusedParams p) {
         float s0 = 0.f, sx0 = 0.f, st0 = 0.f;
 #pragma unroll
         for (int v = 0; v < NVEC; ++v) {
+            if (v == NR) lds_ready();
             if (tid < nv - v * BLOCK) {
+                const u32x4 xw = slot_x(v), tw = slot_t(v);
                 if constexpr (HP) {
                     // fp64 sums: straight into the thread's totals
 #pragma unroll
                     for (int e = 0; e < VEC; ++e)
-                        acc(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z0, s0, zt0, sx0, st0,
-                            zs0);
+                        acc(T::get(xw, e), TMODE != TM_NONE ? T::get(tw, e) : 0.f, z0, s0, zt0, sx0, st0, zs0);
                 } else {
                     Acc z = 0, zt = 0, zs = 0;
                     float s = 0.f, sx = 0.f, st = 0.f;
 #pragma unroll
                     for (int e = 0; e < VEC; ++e)
-                        acc(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, z, s, zt, sx, st, zs);
+                        acc(T::get(xw, e), TMODE != TM_NONE ? T::get(tw, e) : 0.f, z, s, zt, sx, st, zs);
                     z0 += z; s0 += s; zt0 += zt; sx0 += sx; st0 += st; zs0 += zs;
                 }
             }
@@ -1154,6 +1262,11 @@ void fused_kernel(const FusedParams p) {
             // lane l polls word (l % NXW) of chunk (l / NXW)
             const int nwords = p.chunks * NXW;
             const int lw = (lane / NXW) * XS + lane % NXW;
+            // Polls are device-scope loads that travel to memory and take
+            // microseconds under a full memory pipe; a pause of 32 x 64 clocks
+            // between them measured 1.2% faster on the teacher rows than back-
+            // to-back polls (fewer of them compete with the slice traffic),
+            // while several polls in flight measured 9% slower.
             uint64_t w = 0;
             uint32_t spins = 0;
             bool gave_up = false;
@@ -1161,7 +1274,7 @@ void fused_kernel(const FusedParams p) {
                 if (lane < nwords) w = __hip_atomic_load(words + lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const bool ok = (lane >= nwords) || ((w & 0xffffffff00000000ull) == epoch);
                 if (__all(ok)) break;
-                __builtin_amdgcn_s_sleep(1);
+                __builtin_amdgcn_s_sleep(32);
                 if (++spins > spin_limit) {
                     gave_up = true;
                     break;
@@ -1276,18 +1389,60 @@ void fused_kernel(const FusedParams p) {
         ly = (int)((y - head) % VEC);
     }
 
+    // Folded path (see Fold): every 16-bit instance outside the Hinton modes;
+    // the reverse-KL ones fall back to the plain path when rho2 = 0. A
+    // non-finite coefficient (the poisoned load-mode call) folds to NaN.
+    constexpr bool FOLD = !HP && !is_hinton(TMODE);
+    constexpr bool FOLD_ONLY = FOLD && TMODE != TM_RKL;
+    Fold fd{};
+    if constexpr (FOLD) fd = fold_coefs<TMODE>(kf);
+    auto folded_pass = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int v = 0; v < NVEC; ++v) {
+            if (tid < nv - v * BLOCK) {
+                const u32x4 xw = slot_x(v), tw = slot_t(v);
+                float g[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    g[e] = grad_folded<TMODE, SOFTCAP>(p, fd, T::get(xw, e), TMODE != TM_NONE ? T::get(tw, e) : 0.f);
+                if (tid == yv - v * BLOCK) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        if (e == ly)
+                            g[e] = fd.sA * (float)grad_elem(T::get(xw, e), TMODE != TM_NONE ? T::get(tw, e) : 0.f,
+                                                            beta);
+                }
+                u32x4 out;
+                if (p.accumulate) {
+                    const u32x4 old = STAGE_OLD ? s_old[v][tid] : ld_stream(gv + v * BLOCK + tid);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) g[e] = fmaf(fd.sA, g[e], T::get(old, e));
+                    out = T::pack(g);
+                } else {
+                    out = T::pack(g);
+                    if (fd.flip) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) out[c] ^= fd.flip;
+                    }
+                }
+                st_stream(gv + v * BLOCK + tid, out);
+            }
+        }
+    };
+    auto plain_pass = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < NVEC; ++v) {
         if (tid < nv - v * BLOCK) {
+            const u32x4 xw = slot_x(v), tw = slot_t(v);
             CT gd[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
-                gd[e] = grad_elem(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, (CT)0);
+                gd[e] = grad_elem(T::get(xw, e), TMODE != TM_NONE ? T::get(tw, e) : 0.f, (CT)0);
             if (tid == yv - v * BLOCK) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     if (e == ly)
-                        gd[e] = grad_elem(T::get(xs[v], e), TMODE != TM_NONE ? T::get(ts[v], e) : 0.f, beta);
+                        gd[e] = grad_elem(T::get(xw, e), TMODE != TM_NONE ? T::get(tw, e) : 0.f, beta);
             }
             if (p.accumulate) {
                 const u32x4 old = STAGE_OLD ? s_old[v][tid] : ld_stream(gv + v * BLOCK + tid);
@@ -1299,6 +1454,16 @@ void fused_kernel(const FusedParams p) {
             for (int e = 0; e < VEC; ++e) g[e] = (float)gd[e];   // the one rounding
             st_stream(gv + v * BLOCK + tid, T::pack(g));
         }
+    }
+    };
+    lds_ready();   // load mode skips pass 1
+    if constexpr (FOLD_ONLY) {
+        folded_pass();
+    } else if constexpr (FOLD) {
+        if (fd.ok) folded_pass();
+        else plain_pass();
+    } else {
+        plain_pass();
     }
     if (has_e) {
         CT g = grad_elem(xe, te, (int64_t)eidx == y ? beta : (CT)0);

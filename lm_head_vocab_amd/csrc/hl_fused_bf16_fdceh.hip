@@ -16,6 +16,8 @@ FusedLauncher get_fused_bf16_fdceh(int block, int nvec, bool softcap) {
     HL_FUSED_CASE(hl::BF16T, 512, 8, hl::TM_FDCE_H)
     HL_FUSED_CASE(hl::BF16T, 512, 9, hl::TM_FDCE_H)
     HL_FUSED_CASE(hl::BF16T, 512, 10, hl::TM_FDCE_H)
+    HL_FUSED_CASE(hl::BF16T, 512, 12, hl::TM_FDCE_H)
+    HL_FUSED_CASE(hl::BF16T, 512, 13, hl::TM_FDCE_H)
     return nullptr;
 }
 

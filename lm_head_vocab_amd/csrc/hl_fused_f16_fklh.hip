@@ -16,6 +16,8 @@ FusedLauncher get_fused_f16_fklh(int block, int nvec, bool softcap) {
     HL_FUSED_CASE(hl::F16T, 512, 8, hl::TM_FKL_H)
     HL_FUSED_CASE(hl::F16T, 512, 9, hl::TM_FKL_H)
     HL_FUSED_CASE(hl::F16T, 512, 10, hl::TM_FKL_H)
+    HL_FUSED_CASE(hl::F16T, 512, 12, hl::TM_FKL_H)
+    HL_FUSED_CASE(hl::F16T, 512, 13, hl::TM_FKL_H)
     return nullptr;
 }
 

@@ -150,9 +150,10 @@ Geometry geometry_for(int64_t V, hl_dtype dt, int tmode, int C, int block = 0) {
     }
     if (block == kMidBlock) {
         const int* set = tmode == TM_NONE ? kMidNvecStudent : kMidNvecTeacher;
+        const int n_set = tmode == TM_NONE ? 4 : (is_hinton(tmode) && dt != HL_F32 ? 6 : 4);
         const int64_t need = (per + kMidBlock - 1) / kMidBlock;
         if (need > (1 << 20)) return g;
-        const int nv = round_up_to(set, 4, (int)need, cap);
+        const int nv = round_up_to(set, n_set, (int)need, cap);
         return nv < 0 ? g : Geometry{C, kMidBlock, nv};
     }
     if (block != 0 && block != kLargeBlock) return g;

@@ -270,7 +270,9 @@ constexpr int kMidBlock = 512;
 constexpr int kLargeBlock = 1024;
 constexpr int kSmallNvec[] = {1, 2, 4};
 constexpr int kMidNvecStudent[] = {10, 12, 16, 20};
-constexpr int kMidNvecTeacher[] = {6, 8, 9, 10};
+// (12 and 13: 9 register vectors plus 3 or 4 held in LDS; 16-bit Hinton
+// instances only, the one family where the larger slice measured faster)
+constexpr int kMidNvecTeacher[] = {6, 8, 9, 10, 12, 13};
 constexpr int kLargeNvecStudent[] = {2, 4, 6, 8, 10, 12, 14, 16, 18, 20};
 constexpr int kLargeNvecTeacher[] = {2, 4, 6, 8, 10};
 // fp32 slices with a teacher hold at most this many vectors per tensor (the

@@ -217,7 +217,8 @@ def test_hinton_plans_and_the_eight_statistic_chunk_cap():
         assert st == 0
         c, b, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
         assert lib.hl_plan_describe(h, ctypes.byref(c), ctypes.byref(b), ctypes.byref(n)) == 0
-        assert (c.value, b.value) == (4, 512)
+        # the 16-bit Hinton instances hold 9 register + 4 LDS vectors per tensor
+        assert (c.value, b.value, n.value) == (3, 512, 13)
         # the from-distribution mode with Hinton exchanges 8 statistics per
         # chunk: one wave polls at most 64 words, so 8 chunks at most
         expect9 = hl.HL_ERR_UNSUPPORTED if mode == hl.FDCE else hl.HL_OK

@@ -264,6 +264,37 @@ def test_teacher_slice_layouts(combo, variant):
     grad_check(g.cpu(), ref_g, "bf16", labels=to_np(inp["labels"]))
 
 
+@pytest.mark.parametrize("V, nvec", [(95003, 12), (100001, 13)])
+@pytest.mark.parametrize("mode", ["overwrite", "accumulate"])
+@pytest.mark.parametrize("combo", HINTON_COMBOS)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_lds_held_slices(dtype, combo, mode, V, nvec):
+    """Hinton slices of 9 register vectors plus 3 or 4 LDS vectors per tensor
+    (two chunks of 512 threads, ragged rows): the LDS slots take part in both
+    passes, the labels of rows 0 and 1 sit in the LDS part of chunk 0 and of
+    chunk 1, and accumulate mode reads the old gradient beside them."""
+    spec, inp = _small(dtype, combo, 8, V, seed=V % 997 + nvec, softcap=12.0, scale=0.9, temperature=2.0,
+                       accumulate=mode == "accumulate", mask_frac=0.0, ignore_frac=0.0)
+    half = -(-(V // 8) // 2)                       # body vectors per chunk (about)
+    inp["labels"][0] = (9 * 512 + 700) * 8 + 3     # slot 9 of chunk 0
+    inp["labels"][1] = (half + 11 * 512 + 5) * 8   # slot 11 of chunk 1
+    if spec.flags & GRPO:
+        inp["old_logprobs"] = oracle_old_logprobs(spec, inp["logits"], inp["labels"], inp["old_noise"])
+    plan = make_plan(spec, TDT[dtype])
+    plan.set_variant(2, 512)
+    d = plan.describe()
+    say(f"[gpu] LDS-held slice {dtype} {combo} {mode} V={V} -> {d}")
+    assert (d["chunks"], d["block"], d["vec_per_thread"]) == (2, 512, nvec)
+    sc, g = run_hip(plan, _to_dev(inp), mode)
+    ref_sc, ref_g, _ = run_oracle(spec, inp)
+    y = to_np(inp["labels"]).astype(np.int64)
+    valid, _ = oracle.row_validity(8, spec.V, y, to_np(inp["mask"]))
+    vals = oracle.row_values(spec, to_np(inp["logits"]), y, to_np(inp["teacher"]), to_np(inp.get("old_logprobs")),
+                             to_np(inp.get("advantages")))
+    assert_scalars(spec, sc, ref_sc, dtype, vals, valid)
+    grad_check(g.cpu(), ref_g, dtype, labels=y)
+
+
 @pytest.mark.parametrize("chunks", [0, 3])
 @pytest.mark.parametrize("combo", ["all_rkl", "all_fkl", "all_fdce"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
