@@ -319,6 +319,25 @@ def main(argv=None):
                 "kernel_ms_avg": round(kernel_avg, 5),
                 "algorithmic_bytes_per_launch": algo_bytes}
 
+    # The memory system's own rate for this traffic shape: a data-movement-only
+    # kernel with the fused kernel's geometry (same block, loads per thread,
+    # tensors read and written), over full tensors of this workload's size.
+    ceiling = None
+    if not args.no_grad:
+        vpt = min((4, 6, 8, 9, 10) + ((13,) if geo["block"] == 512 else ()),
+                  key=lambda v: (abs(v - geo["vec_per_thread"]), v))
+        out = torch.empty_like(inp["logits"])
+        reads = [inp["logits"]] + ([inp["teacher"]] if inp["teacher"] is not None else [])
+        cms = hl.stream_ceiling(reads[0], reads[1] if len(reads) > 1 else None, out, geo["block"], vpt, reps=5)
+        del out
+        moved = (len(reads) + 1) * inp["logits"].numel() * inp["logits"].element_size()
+        cgbps = moved / (cms * 1e-3) / 1e9
+        ceiling = {"kernel": "hl_stream_ceiling", "reads": len(reads), "writes": 1, "block": geo["block"],
+                   "vec_per_thread": vpt, "ms": round(cms, 5), "GBps": round(cgbps, 1),
+                   "frac_of_peak": round(cgbps / PEAK_HBM_GBPS, 4), "fused_over_ceiling": round(achieved / cgbps, 4)}
+        log(f"stream ceiling {cgbps:.0f} GB/s ({cgbps / PEAK_HBM_GBPS:.1%} of peak); fused/ceiling "
+            f"{achieved / cgbps:.3f}")
+
     if separate is not None:
         separate["fused_speedup"] = round(separate["ms_per_step"] / ms_step, 3)
     tokens_s = w.N / (ms_step * 1e-3)
@@ -343,6 +362,7 @@ def main(argv=None):
         "frac_peak_step": round(algo_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "copy_GBps": round(copy_gbps, 1),
         "roofline": roofline,
+        "ceiling": ceiling,
         "cpu_baseline": cpu,
         "separate_pass": separate,
         "src_hash": src_hash,

@@ -347,6 +347,21 @@ hl_status hl_plan_set_timing_events(hl_plan_t plan, hipEvent_t before, hipEvent_
 hl_status hl_plan_set_exchange_test(hl_plan_t plan, uint32_t spin_limit, int64_t withhold_row,
                                     int withhold_chunk);
 
+/* Measurement aid (Fast-LLM PR #549, section Performance: the fused path
+ * is judged by the memory traffic it moves): the memory system's rate for
+ * the fused kernel's traffic shape, with no arithmetic. Each workgroup of
+ * `block` threads (512 or 1024) reads vec_per_thread (4, 6, 8, 9 or 10; 13
+ * at 512 threads) 16-byte vectors per thread from read0 (and read1, if not NULL) into
+ * registers, issuing every load before any use, then writes their bitwise
+ * xor to `write`; each buffer holds `bytes` bytes (a multiple of 16, 16-byte
+ * aligned device pointers; `write` is overwritten). One warm-up launch, then
+ * `reps` timed launches on `stream` (this call synchronizes it);
+ * *ms_per_launch receives the mean. Errors: HL_ERR_INVALID_ARG (NULL
+ * pointer, size or alignment), HL_ERR_UNSUPPORTED (another block or vector
+ * count), HL_ERR_HIP (see hl_last_error). */
+hl_status hl_stream_ceiling(const void* read0, const void* read1, void* write, int64_t bytes, int block,
+                            int vec_per_thread, int reps, hipStream_t stream, float* ms_per_launch);
+
 /* Text of the last HIP failure seen by this thread (which call, the HIP
  * error string and code), or of the last workspace-size refusal of
  * hl_forward_backward_noalloc, or "" if none. Valid until the next failing

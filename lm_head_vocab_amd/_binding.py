@@ -121,6 +121,9 @@ def load_library(path: str | None = None):
     lib.hl_last_error.restype = ctypes.c_char_p
     lib.hl_status_str.argtypes = [ctypes.c_int]
     lib.hl_status_str.restype = ctypes.c_char_p
+    lib.hl_stream_ceiling.argtypes = [vp, vp, vp, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                      ctypes.POINTER(ctypes.c_float)]
+    lib.hl_stream_ceiling.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -319,6 +322,24 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def stream_ceiling(read0, read1, write, block: int, vec_per_thread: int, reps: int = 5) -> float:
+    """hl_stream_ceiling on the current stream: milliseconds per launch of the
+    data-movement-only kernel over tensors of write's size (read1 may be None)."""
+    torch = _torch()
+    lib = load_library()
+    nbytes = write.numel() * write.element_size()
+    for t in (read0, read1):
+        if t is not None and t.numel() * t.element_size() < nbytes:
+            raise ValueError("every read tensor must hold at least as many bytes as write")
+    ms = ctypes.c_float(0.0)
+    stream = torch.cuda.current_stream(write.device).cuda_stream
+    _check("hl_stream_ceiling", lib.hl_stream_ceiling(
+        ctypes.c_void_p(read0.data_ptr()), ctypes.c_void_p(read1.data_ptr() if read1 is not None else 0),
+        ctypes.c_void_p(write.data_ptr()), nbytes, block, vec_per_thread, reps, ctypes.c_void_p(stream),
+        ctypes.byref(ms)))
+    return float(ms.value)
 
 
 def scalars_dict(scalars) -> dict:

@@ -337,3 +337,16 @@ def test_noalloc_checks_before_any_hip_call():
     msg = lib.hl_last_error().decode()
     assert "HL_STATIC_WORKSPACE_BYTES" in msg and str(n) in msg
     lib.hl_plan_destroy(h)
+
+
+def test_stream_ceiling_host_checks():
+    """The measurement aid refuses bad arguments on the host, before any HIP call."""
+    ms = ctypes.c_float()
+    f = lib.hl_stream_ceiling
+    assert f(None, None, VP(4096), 1 << 20, 1024, 10, 1, None, ctypes.byref(ms)) == hl.HL_ERR_INVALID_ARG
+    assert f(VP(4096), None, VP(8192), 1 << 20, 1024, 10, 0, None, ctypes.byref(ms)) == hl.HL_ERR_INVALID_ARG
+    assert f(VP(4096), None, VP(8192), 1000, 1024, 10, 1, None, ctypes.byref(ms)) == hl.HL_ERR_INVALID_ARG
+    assert f(VP(4096 + 8), None, VP(8192), 1 << 20, 1024, 10, 1, None, ctypes.byref(ms)) == hl.HL_ERR_INVALID_ARG
+    assert f(VP(4096), None, VP(8192), 1 << 20, 256, 10, 1, None, ctypes.byref(ms)) == hl.HL_ERR_UNSUPPORTED
+    assert f(VP(4096), None, VP(8192), 1 << 20, 1024, 13, 1, None, ctypes.byref(ms)) == hl.HL_ERR_UNSUPPORTED
+    assert f(VP(4096), VP(12288), VP(8192), 1 << 20, 512, 7, 1, None, ctypes.byref(ms)) == hl.HL_ERR_UNSUPPORTED

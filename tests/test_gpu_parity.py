@@ -697,3 +697,19 @@ def test_fused_equals_separate_passes(combo):
         first = False
     torch.cuda.synchronize()
     assert (g - g_f).abs().max().item() <= 1e-6
+
+
+@pytest.mark.parametrize("reads, block, vpt", [(1, 1024, 10), (2, 512, 13), (2, 1024, 8), (1, 512, 9), (2, 512, 6)])
+def test_stream_ceiling_moves_every_byte(reads, block, vpt):
+    """The memory-system reference writes the xor of its inputs over the
+    whole buffer (several workgroups and a ragged last one), bit for bit."""
+    n = 3 * block * vpt + 37                      # 16-byte vectors
+    gen = torch.Generator(device="cpu").manual_seed(block + vpt + reads)
+    a = torch.randint(-2**31, 2**31 - 1, (n, 4), dtype=torch.int32, generator=gen).to(DEV)
+    b = torch.randint(-2**31, 2**31 - 1, (n, 4), dtype=torch.int32, generator=gen).to(DEV) if reads == 2 else None
+    out = torch.zeros_like(a)
+    say(f"[gpu] stream ceiling reads={reads} block={block} vec={vpt} n={n}")
+    ms = hl.stream_ceiling(a, b, out, block, vpt, reps=2)
+    ref = a ^ b if b is not None else a
+    assert torch.equal(out, ref)
+    assert ms > 0.0
