@@ -323,7 +323,7 @@ def main(argv=None):
     # kernel with the fused kernel's geometry (same block, loads per thread,
     # tensors read and written), over full tensors of this workload's size.
     ceiling = None
-    if not args.no_grad:
+    if not args.no_grad and geo["block"] in (512, 1024):   # (256-thread variants: rows too short to stream)
         vpt = min((4, 6, 8, 9, 10) + ((13,) if geo["block"] == 512 else ()),
                   key=lambda v: (abs(v - geo["vec_per_thread"]), v))
         out = torch.empty_like(inp["logits"])
