@@ -50,12 +50,15 @@ def row_value_scale(key, ref):
     return sc
 
 
-def degenerate_allowance(spec, x) -> float:
-    """Rows of one element (V = 1), a reading: the exact CE, new log-prob and
-    every KL are 0 there, while the kernel forms them from fp32 statistics of
-    magnitude S = max |s| (with a softcap c, max(max |s|, c)); a slot is
-    accepted within 4 ulps of S times (1 + the weight sum). 0 for V > 1."""
-    if spec.V != 1 or x is None or np.size(x) == 0:
+def degenerate_allowance(spec, x, dtype="bf16") -> float:
+    """Rows of one element (V = 1) in the 16-bit instances, a reading: the
+    exact CE, new log-prob and every KL are 0 there, while those instances
+    form them from fp32 statistics of magnitude S = max |s| (with a softcap
+    c, max(max |s|, c)); a slot is accepted within 4 ulps of S times (1 + the
+    weight sum). 0 for V > 1 and for fp32 inputs, whose instances form the
+    statistics and coefficients in fp64 (measured: gradient errors below
+    5e-10 on those rows), so the plain gates hold."""
+    if spec.V != 1 or dtype == "f32" or x is None or np.size(x) == 0:
         return 0.0
     x = np.asarray(x, dtype=np.float64)
     s = spec.softcap * np.tanh(spec.logit_scale * x / spec.softcap) if spec.softcap > 0 else spec.logit_scale * x
@@ -203,7 +206,7 @@ def assert_scalars(spec, got, ref, dtype, vals=None, valid=None, skip=(), x=None
     (V = 1) also within degenerate_allowance(spec, x) absolute."""
     rel = TOL[dtype]["scalar_rel"]
     errs = scalar_errors(spec, got, ref, vals, valid)
-    allow = degenerate_allowance(spec, x)
+    allow = degenerate_allowance(spec, x, dtype)
     for name in ("N_VALID", "N_BADLABEL"):
         assert got[SLOT[name]] == ref[SLOT[name]], (name, got[SLOT[name]], ref[SLOT[name]])
     bad = {k: v for k, v in errs.items()

@@ -417,15 +417,16 @@ def test_outlier_logits(dtype, combo, chunks, mode):
         inp["teacher"] = t.to(TDT[dtype])
     if spec.has(GRPO):
         inp["old_logprobs"] = oracle_old_logprobs(spec, inp["logits"], inp["labels"], inp["old_noise"])
-    # fp32 gradient: the plain 1e-6 absolute gate (the fp32 instances carry
-    # k log2(e) and the log-partitions as hi + lo pairs and shift by the exact
-    # wave maxima, so an outlier's exponent keeps its low bits).
+    # fp32 gradient: the plain 1e-6 absolute gate (the fp32 instances form
+    # exponents with fp64 constants, sum the normalizers in fp64 and write
+    # each element from fp64 coefficients, so an outlier's exponent keeps its
+    # low bits).
     #
     # Entropy: these rows are nearly one-hot, so the exact entropy is ~1e-7
-    # nats and the fp32 record's Z sits at 1 + O(1e-9); each rounding of Z
-    # moves log Z by up to 2^-24 nats, and a row's record goes through up to
-    # ~20 merges, so the entropy is checked to 2e-6 nats absolute instead of
-    # relative to its near-zero value.
+    # nats, while the entropy sum S and (in the 16-bit instances) Z are fp32
+    # sums whose every rounding moves the result by up to 2^-24 nats through
+    # up to ~20 merges, so the entropy is checked to 2e-6 nats absolute
+    # instead of relative to its near-zero value.
     ref_sc, ref_g, _ = run_oracle(spec, inp)
     gm = None if mode == "gradient" else "none"
     _, sc, met = _check_small(spec, inp, dtype, chunks=chunks, grad_mode=gm, skip_scalars=("ENTROPY",))
