@@ -714,3 +714,39 @@ def test_stream_ceiling_moves_every_byte(reads, block, vpt):
     ref = a ^ b if b is not None else a
     assert torch.equal(out, ref)
     assert ms > 0.0
+
+
+# signs and zeros of the probability, teacher and reverse-KL coefficients
+# (the 16-bit instances fold the coefficient's magnitude into the exponent and
+# apply its sign to the packed output; reverse KL with rho2 = 0 takes the plain
+# element path)
+SIGN_CASES = [
+    ("ce", dict(ce=-0.7)),                                           # alpha < 0, no teacher
+    ("ce_fkl", dict(ce=-0.7, distill=1.0)),                          # alpha < 0 < gam
+    ("ce_fkl", dict(ce=0.5, distill=-0.8)),                          # gam < 0 < alpha
+    ("ce_fkl", dict(ce=-0.5, distill=-0.8)),                         # both negative
+    ("ce_fdce", dict(ce=0.0, distill=-1.1)),                         # alpha = gam < 0
+    ("ce_fkl", dict(ce=0.5, distill=0.0)),                           # gam = 0
+    ("all_rkl", dict(ce=1.0, z=1e-3, distill=0.0, grpo=1.0)),        # rho2 = 0: plain path
+    ("all_rkl", dict(ce=1.0, z=1e-3, distill=-0.5, grpo=1.0)),       # rho2 < 0
+    ("ce_rkl", dict(ce=-0.5, distill=0.7)),                          # c0 < 0 < rho2
+]
+
+
+@pytest.mark.parametrize("mode", ["overwrite", "accumulate"])
+@pytest.mark.parametrize("case", SIGN_CASES, ids=[f"{c}-{'_'.join(f'{k}{v}' for k, v in w.items())}" for c, w in SIGN_CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_coefficient_signs_and_zeros(dtype, case, mode):
+    combo, w = case
+    flags = COMBOS[combo][0] | (ACC if mode == "accumulate" else 0)
+    w = dict(w)
+    if dtype == "f16":
+        w["grad_scale"] = w.get("grad_scale", 1.0) * F16_LOSS_SCALE
+    N, V = 9, 20011
+    spec = spec_from(V, flags, w, temperature=1.5, eps=0.2, logit_scale=0.9, softcap=0.0)
+    inp = workloads.small_inputs(N, V, dtype, "cpu", 500 + len(combo) * 7 + N, teacher=bool(flags & DISTILL),
+                                 grpo=bool(flags & GRPO), accumulate=mode == "accumulate", mask_frac=0.2)
+    if flags & GRPO:
+        inp["old_logprobs"] = oracle_old_logprobs(spec, inp["logits"], inp["labels"], inp["old_noise"])
+    for chunks in (0, 3):
+        _check_small(spec, inp, dtype, chunks=chunks)
