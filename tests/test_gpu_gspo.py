@@ -123,9 +123,11 @@ def _scalar_vals(vals, seam):
     return out
 
 
-def _check(spec, inp, dtype, chunks=0, grad_mode=None):
+def _check(spec, inp, dtype, chunks=0, grad_mode=None, variant=None):
     grad_mode = grad_mode or ("accumulate" if spec.has(ACC) else "overwrite")
     plan = make_plan(spec, TDT[dtype], chunks)
+    if variant is not None:
+        plan.set_variant(*variant)
     N = inp["logits"].shape[0]
     say(f"[gpu] gspo N={N} V={spec.V} S={inp['seq_offsets'].numel() - 1} {dtype} flags={spec.flags:#x} "
         f"{plan.describe()} grad={grad_mode}")
@@ -311,3 +313,16 @@ def test_gspo_empty_batch_and_all_masked():
     assert torch.all(sc.cpu() == 0)
     spec, inp = _case("bf16", "all_gspo_rkl", 10, 777, seed=1, ignore_frac=1.0)
     _check(spec, inp, "bf16")
+
+
+@pytest.mark.parametrize("accumulate", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_gspo_load_mode_with_lds_held_slices(dtype, accumulate):
+    """The reloading backward of a Hinton GSPO call on slices of 9 register
+    vectors plus 4 LDS vectors per tensor (2 chunks x 512 threads at
+    V = 100001): the LDS slots are read in pass 2 without a pass 1."""
+    spec, inp = _case(dtype, "all_gspo_rkl_h", 12, 100001, seed=29 + accumulate, accumulate=accumulate,
+                      mask_frac=0.2)
+    plan, _, _, _, _ = _check(spec, inp, dtype, variant=(2, 512))
+    d = plan.describe()
+    assert (d["chunks"], d["block"], d["vec_per_thread"]) == (2, 512, 13)
