@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -43,15 +44,25 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """The source without // and /* */ comments and without blank space, so
+    that an edit of a comment does not invalidate stored counters. (String
+    literals holding comment markers would be cut too; the kernel sources
+    have none that change code.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash() -> str:
-    """Hash of the kernel sources (tells whether stored counters still apply)."""
+    """Hash of the kernel sources' code (tells whether stored counters still apply)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "lm_head_vocab_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".cuh", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
                 h.update(name.encode())
-                h.update(f.read())
+                h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

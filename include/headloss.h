@@ -49,7 +49,10 @@ typedef enum {
 
 /* Element type of logits, teacher logits and gradient (all three share it).
  * fp16 inputs are among the dtypes the monolithic kernel is validated with
- * (#558 Validation); an fp16 gradient underflows below 6e-8 (use grad_scale). */
+ * (#558 Validation); an fp16 gradient underflows below 6e-8 (use grad_scale).
+ * HL_F32 plans keep the softmax statistics, the per-row coefficients and each
+ * gradient element in fp64 internally and round once on output; bf16 and fp16
+ * plans compute in fp32 (#549 Approach: fp32 accumulation, one cast). */
 typedef enum { HL_F32 = 0, HL_BF16 = 1, HL_F16 = 2 } hl_dtype;
 
 /* Loss and metric flags (#507 Proposed direction: a flag set naming the
@@ -195,8 +198,8 @@ hl_status hl_plan_set_workspace(hl_plan_t plan, void* dev_workspace, size_t byte
  *                   scalars agree with a gradient call's to float rounding,
  *                   not bit for bit). Overwrite
  *                   mode writes every element (masked rows +0.0);
- *                   HL_ACCUMULATE adds in fp32 and rounds once, and leaves
- *                   masked rows untouched.
+ *                   HL_ACCUMULATE adds in fp32 (HL_F32 plans: fp64) and
+ *                   rounds once, and leaves masked rows untouched.
  *   scalars_out     device float[HL_NUM_SCALARS], must not be NULL.
  *   stream          HIP stream for all work of the call.
  * Alignment: rows are split into 16-byte vectors (plus a head and a tail of

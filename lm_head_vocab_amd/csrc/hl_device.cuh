@@ -490,12 +490,13 @@ __device__ __forceinline__ void row_status(const int64_t* labels, const uint8_t*
 // and by up to |B2| 2^-24 through that of the log-partition B2, which moves
 // every softmax entry by as much relatively; the GRPO ratio exp(s_y - lse -
 // old) suffers the same from lse, and the hardware exp2 and every fp32
-// product add about an ulp each. The fp32 instances therefore carry
-// k log2(e), log2(e) / tau and 1 / tau as hi + lo pairs, take each wave's
-// exact maxima as the pass-1 shifts (the largest elements then sit at offset
-// ~0, where an fp32 offset is exact), form the per-row coefficients in fp64
-// and evaluate each gradient element in fp64 from the fp32 inputs (and, with
-// softcap, the same fp32 cap_r value pass 1 summed), rounding it once.
+// product add about an ulp each. The fp32 instances therefore take
+// k log2(e), log2(e) / tau and 1 / tau in fp64 (K1d, K2d, betad), shift each
+// wave by the ceiling of its exact maximum (an integer, so records merge by
+// exact powers of two), sum the normalizers Z, Zt, Zs in fp64 and carry them
+// as hi + lo float pairs, form the per-row coefficients in fp64 and evaluate
+// each gradient element in fp64 from the fp32 inputs (and, with softcap, the
+// same fp32 cap_r value pass 1 summed), rounding it once.
 template <typename R>
 struct CoefsT {
     R alpha;   // probability coefficient, times G k / n
@@ -776,8 +777,8 @@ grad_one(const FusedParams& p, const CoefsFor<HP>& k, float x, float t,
 // when WS: the entropy sum), Zt += 2^u, the distillation cross sum SX (and
 // St = sum 2^u u, Zs = sum 2^(a / tau) in the modes that need them), with
 // a = s log2(e) - M the student's and u = t log2(e) / tau - Mt the teacher's
-// offset. HP (the fp32 instances): the offsets with the low parts of the
-// constants in fp64, the normalizer terms from the fp64 exp2, and Z, Zt, Zs
+// offset. HP (the fp32 instances): the offsets in fp64 with the fp64
+// constants, the normalizer terms from the fp64 exp2, and Z, Zt, Zs
 // accumulated in fp64 (A = double); S, SX, St stay fp32 sums.
 template <int TMODE, bool SOFTCAP, bool WS, bool HP, typename A>
 __device__ __forceinline__ void stat_term(const FusedParams& p, float M, float Mt, float x, float t, A& z,
@@ -869,7 +870,7 @@ void fused_kernel(const FusedParams p) {
     constexpr int VEC = T::VEC;
     constexpr int ES = T::ESIZE;
     constexpr int NW = BLOCK / 64;
-    constexpr bool HP = std::is_same<T, F32T>::value;   // fp32: exact shifts, hi + lo constants
+    constexpr bool HP = std::is_same<T, F32T>::value;   // fp32: fp64 constants, sums and coefficients
     static_assert(NW <= 16, "at most 16 waves per workgroup");
     constexpr int NL = lds_slots<T, BLOCK, NVEC, TMODE>();   // slots 0..NR-1 in registers, NR.. in LDS
     constexpr int NR = NVEC - NL;
